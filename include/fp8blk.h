@@ -1,0 +1,186 @@
+/*
+ * fp8blk.h -- C ABI of the MI355X (gfx950) FP8 blockwise-quantized linear layer.
+ *
+ * The operation is the "Block_FP8" quantized linear layer: FP8 e4m3fn
+ * activations with one scale per token and 128-wide K group (1x128), FP8
+ * e4m3fn weights with one scale per 128x128 block, fp32 accumulation, bf16
+ * output.  Format named on page "Helion: improving vLLM inference with
+ * autotuning", section "Helion Linear Backend" / "Scope".  The activation
+ * quantizer is per_token_group_fp8_quant and the GEMM is scaled_mm_blockwise
+ * (page "Helion-Kernel in vLLM: PyTorch FP8 ohne CUDA", section "Welche
+ * Kernel wurden in vLLM integriert"; page "[RFC]: Using Helion for Selected
+ * vLLM CustomOps", section "Motivation").  The GEMM variants Standard,
+ * Split-K and Swap-AB and their selection per shape follow the sections
+ * "Kernel Implementation", "Hybrid Dispatch" and "Per-shape Config Tuning"
+ * of the autotuning page.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device.
+ *     bf16 is passed as uint16_t bit patterns, fp8 e4m3fn as uint8_t codes.
+ *   - Row-major 2-D layouts with an explicit leading dimension ("ld", in
+ *     elements).  Activations X/Q/A are [M][K], weights W are [N][K] (K
+ *     contiguous), the output Y is [M][N]; Y = A * W^T.
+ *   - Activation scales are [M][K/128] (row pitch ldsa/lds floats), weight
+ *     scales are [N/128][K/128] (row pitch ldsw floats); groups and blocks
+ *     start at k = 0 and n = 0.
+ *   - The caller owns every buffer.  The library never allocates device or
+ *     host memory, never synchronizes, never reads device memory on the host
+ *     and keeps no mutable global state: calls are thread-safe and can be
+ *     captured into a HIP graph.  Work is ordered on the given stream
+ *     (a hipStream_t passed as void*; NULL is the default stream).
+ *   - Outputs are fully overwritten; inputs are never modified.
+ *   - Invalid arguments return a negative status before anything is
+ *     launched.  A launch failure reported by the HIP runtime returns
+ *     FP8BLK_ERR_HIP.  M == 0 (or n == 0) is a no-op returning FP8BLK_OK.
+ *   - Required alignment: every base pointer 16 bytes, every fp8/bf16 row
+ *     pitch a multiple of 16 bytes; scale pointers 4 bytes.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified (but memory-safe)
+ *     results.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BLK_ABI_VERSION 1
+#define FP8BLK_GROUP 128      /* K-group width and weight block edge */
+#define FP8BLK_E4M3_MAX 448.0f
+
+/* status codes */
+#define FP8BLK_OK 0
+#define FP8BLK_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
+#define FP8BLK_ERR_BAD_SHAPE (-2)   /* K%128, N%128, negative sizes, group != 128, too large */
+#define FP8BLK_ERR_MISALIGNED (-3)  /* pointer or row pitch not 16-byte aligned */
+#define FP8BLK_ERR_BAD_STRIDE (-4)  /* leading dimension smaller than the row */
+#define FP8BLK_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required */
+#define FP8BLK_ERR_BAD_CONFIG (-6)  /* unknown variant or unsupported tile/split */
+#define FP8BLK_ERR_HIP (-7)         /* the HIP runtime rejected a launch */
+
+/* flags */
+#define FP8BLK_FLAG_UE8M0 1u /* scales rounded up to a power of two ("UE8M0",
+                                "float32 ceiling E8M0"): page "Helion-Kernel in
+                                vLLM", section "Praktische Einschränkungen";
+                                RFC page, H100 end-to-end settings */
+
+/* GEMM variants (autotuning page, section "Kernel Implementation") */
+#define FP8BLK_STANDARD 0 /* tiles over (M, N), loop over K */
+#define FP8BLK_SWAPAB 1   /* computes (W A^T)^T: weight rows on the matrix-core
+                             row side, tokens on the column side (small M) */
+
+/* A GEMM configuration.  split_k > 1 is the Split-K variant: the K blocks
+ * are divided among split_k groups of workgroups, each writing an fp32
+ * partial product to the workspace, then a second kernel sums the partials
+ * in a fixed order and writes bf16 (deterministic, no atomics).
+ *   STANDARD: tile_m in {64, 128, 256}, tile_n in {128, 256}.
+ *   SWAPAB:   tile_m (tokens per workgroup) in {16, 32, 64} and >= M,
+ *             tile_n (weight rows per workgroup) in {16, 32, 64},
+ *             kwaves (waves sharing one tile, each on its own K range,
+ *             summed in the workgroup) in {1, 2, 4, 8}.
+ *   split_k: 1 .. min(256, K/128). */
+typedef struct fp8blk_gemm_config {
+    int32_t variant;
+    int32_t tile_m;
+    int32_t tile_n;
+    int32_t split_k;
+    int32_t kwaves;
+    int32_t reserved[3]; /* must be 0 */
+} fp8blk_gemm_config;
+
+/* Library ABI version (FP8BLK_ABI_VERSION of the build). */
+int fp8_abi_version(void);
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char *fp8_status_string(int status);
+
+/*
+ * per_token_group_fp8_quant -- dynamic activation quantization.
+ *
+ * For every row m and group g (128 consecutive K elements from k = 128 g):
+ *   amax = max_j |x[m][128g + j]|                 (bf16 -> fp32 exactly)
+ *   s    = max(amax, eps) / 448                   (fp32, correctly rounded)
+ *   if (flags & FP8BLK_FLAG_UE8M0) s = 2^ceil(log2 s)  (power-of-two ceiling)
+ *   q[m][128g + j] = e4m3fn_rne(clamp(x / s, -448, 448))  (fp32 quotient,
+ *                                                  ties to even, sign of zero kept)
+ *   s_out[m][g] = s
+ * Format: autotuning page, "Helion Linear Backend" / "Scope" (Block_FP8, 1x128
+ * activation scaling).  eps guards the all-zero group (pages silent; 1e-10
+ * is the suggested value).
+ *
+ *   x     bf16 [M][ldx], ldx >= K        q  uint8 [M][ldq], ldq >= K
+ *   s     fp32 [M][lds], lds >= K/128    group must be 128
+ *   Requires K % 128 == 0, M >= 0, eps > 0 and finite.
+ */
+int fp8_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                    uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                    int32_t group, float eps, uint32_t flags, void *stream);
+
+/*
+ * 128x128 weight block quantization (offline preparation of W; same rule as
+ * fp8_group_quant over 128x128 blocks of an fp32 matrix):
+ *   s = max(amax_block, eps) / 448 [power-of-two ceiling if UE8M0],
+ *   q = e4m3fn_rne(clamp(w / s, -448, 448)).
+ * Format: autotuning page, "Helion Linear Backend" / "Scope" (128x128
+ * weight scaling).
+ *   w fp32 [N][ldw], ldw >= K;  q uint8 [N][ldq];  s fp32 [N/128][lds], lds >= K/128.
+ *   Requires N % 128 == 0 and K % 128 == 0.
+ */
+int fp8_weight_block_quant(const float *w, int64_t N, int64_t K, int64_t ldw,
+                           uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                           float eps, uint32_t flags, void *stream);
+
+/*
+ * The encoding step on its own: q[i] = e4m3fn_rne(clamp(t[i], -448, 448))
+ * for n contiguous fp32 values (same encoder as the quantizers).
+ *   t fp32 [n], q uint8 [n]; n >= 0; both pointers 16-byte aligned.
+ */
+int fp8_e4m3_encode(const float *t, uint8_t *q, int64_t n, void *stream);
+
+/*
+ * Per-shape dispatch: the configuration fp8_block_gemm uses when cfg is NULL.
+ * A table tuned on MI355X keyed on (N, K) and a bucket of M, with a
+ * heuristic for shapes not in the table (autotuning page, "Hybrid Dispatch"
+ * and "Per-shape Config Tuning").  Deterministic, host-only, O(1).
+ * Returns FP8BLK_OK or FP8BLK_ERR_BAD_SHAPE / FP8BLK_ERR_NULL_PTR.
+ */
+int fp8_block_gemm_select(int64_t M, int64_t N, int64_t K, uint32_t flags,
+                          fp8blk_gemm_config *out);
+
+/*
+ * Workspace bytes fp8_block_gemm needs for this shape and configuration
+ * (cfg NULL: the dispatched one).  Split-K needs split_k * M * N * 4 bytes;
+ * the other variants need 0.  Returns a negative status on a bad argument.
+ */
+int64_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
+                                      const fp8blk_gemm_config *cfg);
+
+/*
+ * scaled_mm_blockwise -- blockwise-scaled FP8 GEMM, bf16 out:
+ *   y[m][n] = bf16_rne( sum_kb  sa[m][kb] * sw[n/128][kb] *
+ *                       sum_{k in block kb} dec(a[m][k]) * dec(w[n][k]) )
+ * with fp32 accumulation (autotuning page, "Kernel Implementation": the
+ * quantized GEMM follows the unified GEMM with scaling added; "Scope":
+ * 1x128 / 128x128 scales).
+ *   a  uint8 e4m3fn [M][lda], lda >= K      sa fp32 [M][ldsa], ldsa >= K/128
+ *   w  uint8 e4m3fn [N][ldw], ldw >= K      sw fp32 [N/128][ldsw], ldsw >= K/128
+ *   y  bf16 [M][ldy], ldy >= N
+ *   cfg NULL selects through fp8_block_gemm_select.
+ *   workspace: device buffer of at least fp8_block_gemm_workspace_size bytes
+ *   (may be NULL when that is 0).  Concurrent calls must not share one.
+ * Requires K % 128 == 0, N % 128 == 0, M >= 0.
+ */
+int fp8_block_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
+                   const uint8_t *w, const float *sw, int64_t ldw, int64_t ldsw,
+                   uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                   const fp8blk_gemm_config *cfg, void *workspace,
+                   int64_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

@@ -1,0 +1,439 @@
+/*
+ * oracle.c -- plain CPU reference of the FP8 blockwise-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file; only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no source with the GPU library
+ * (no headers, no helpers, no tables).
+ *
+ * What it computes, and where that is defined:
+ *   - "Block_FP8": FP8 with 1x128 activation scaling and 128x128 weight
+ *     scaling.  Page "Helion: improving vLLM inference with autotuning",
+ *     section "Helion Linear Backend" / "Scope".
+ *   - The activation quantizer per_token_group_fp8_quant (named among the
+ *     nine kernels of page "Helion-Kernel in vLLM: PyTorch FP8 ohne CUDA",
+ *     section "Welche Kernel wurden in vLLM integriert", and as the first
+ *     rollout kernel of page "[RFC]: Using Helion for Selected vLLM
+ *     CustomOps", section "Motivation").
+ *   - The power-of-two ("UE8M0", "float32 ceiling E8M0") scale option: page
+ *     "Helion-Kernel in vLLM", section "Praktische Einschränkungen", and the
+ *     H100 settings of the RFC page, section "End-to-End Model Performance".
+ *   - The blockwise-scaled GEMM scaled_mm_blockwise: same structure as the
+ *     plain GEMM of the "Kernel Implementation" section of the autotuning
+ *     page, plus the quantization scales.
+ *
+ * The pages do not print the e4m3fn bit layout, the rounding mode, the
+ * saturation rule, the all-zero-group rule or the scale layouts.  The
+ * readings taken here (OCP e4m3fn, round to nearest with ties to even,
+ * clamp to +-448 before encoding, amax clamped below by eps, scales stored
+ * row-major as [M][K/128] and [N/128][K/128], weights as W[N][K]) are the
+ * documented conventions of this project.
+ *
+ * Floating point: fp32 steps use C float arithmetic (SSE on x86-64, IEEE
+ * single, correctly rounded division); build with -ffp-contract=off so that
+ * no multiply-add is fused.  The GEMM reference is accumulated in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_GROUP 128
+#define ORC_E4M3_MAX 448.0f
+
+/* ------------------------------------------------------------------ */
+/* e4m3fn codec                                                        */
+/* ------------------------------------------------------------------ */
+
+/* Value of an e4m3fn code: sign bit, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent field 0 is the subnormal range m * 2^-9; code 0x7F / 0xFF
+ * is NaN; there is no infinity. */
+double orc_e4m3_decode(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xF;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Round |t| <= 448 to the nearest e4m3fn value, ties to the code whose
+ * mantissa is even.  Written as the definition: the non-negative codes
+ * 0x00..0x7E are in increasing order of value, so find the pair that
+ * brackets |t| and compare |t| with their midpoint exactly (2|t| and the
+ * sum of two e4m3 values are exact in double).  The sign of t (also of -0)
+ * is kept in bit 7.  Values beyond 448 are the caller's to clamp. */
+uint8_t orc_e4m3_encode(float t)
+{
+    int neg = signbit(t) ? 1 : 0;
+    double a = fabs((double)t);
+    int lo = 0, hi = 126, code;
+    if (a >= 448.0) {
+        code = 126;
+    } else {
+        /* largest code c with value(c) <= a */
+        while (lo < hi) {
+            int mid = (lo + hi + 1) / 2;
+            if (orc_e4m3_decode((uint8_t)mid) <= a)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        {
+            double vlo = orc_e4m3_decode((uint8_t)lo);
+            double vhi = orc_e4m3_decode((uint8_t)(lo + 1));
+            double twice = 2.0 * a;
+            double mids = vlo + vhi;
+            if (twice < mids)
+                code = lo;
+            else if (twice > mids)
+                code = lo + 1;
+            else
+                code = (lo & 1) ? lo + 1 : lo; /* mantissa LSB is the code LSB */
+        }
+    }
+    return (uint8_t)((neg << 7) | code);
+}
+
+void orc_e4m3_encode_array(const float *t, uint8_t *q, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = orc_e4m3_encode(t[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* scales                                                              */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32. */
+static float bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Power-of-two ceiling of a positive normal float: s = f * 2^e with
+ * f in [0.5, 1); s is already a power of two iff f == 0.5. */
+float orc_pow2_ceil(float s)
+{
+    int e;
+    float f = frexpf(s, &e);
+    if (f == 0.5f)
+        return s;
+    return ldexpf(1.0f, e);
+}
+
+/* scale = max(amax, eps) / 448, then optionally its power-of-two ceiling. */
+float orc_scale_from_amax(float amax, float eps, int ue8m0)
+{
+    float a = amax > eps ? amax : eps;
+    float s = a / ORC_E4M3_MAX;
+    if (ue8m0)
+        s = orc_pow2_ceil(s);
+    return s;
+}
+
+/* Encode one value with a given scale: t = v / s in fp32, clamped to
+ * [-448, 448] (a value inside the range, -0 included, passes unchanged). */
+static uint8_t quantize_one(float v, float s)
+{
+    float t = v / s;
+    if (t > ORC_E4M3_MAX)
+        t = ORC_E4M3_MAX;
+    else if (t < -ORC_E4M3_MAX)
+        t = -ORC_E4M3_MAX;
+    return orc_e4m3_encode(t);
+}
+
+/* ------------------------------------------------------------------ */
+/* per-token 1x128 group quantizer                                     */
+/* ------------------------------------------------------------------ */
+
+/* x: bf16 bits [M][ldx]; q: [M][ldq]; s: [M][lds], one scale per group of
+ * 128 consecutive K elements starting at k = 0.  K % 128 == 0. */
+void orc_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                     uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                     float eps, int ue8m0)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t g = 0; g < K / ORC_GROUP; ++g) {
+            const uint16_t *xg = x + m * ldx + g * ORC_GROUP;
+            float v[ORC_GROUP];
+            float amax = 0.0f;
+            for (int j = 0; j < ORC_GROUP; ++j) {
+                v[j] = bf16_value(xg[j]);
+                if (fabsf(v[j]) > amax)
+                    amax = fabsf(v[j]);
+            }
+            float sc = orc_scale_from_amax(amax, eps, ue8m0);
+            s[m * lds + g] = sc;
+            for (int j = 0; j < ORC_GROUP; ++j)
+                q[m * ldq + g * ORC_GROUP + j] = quantize_one(v[j], sc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* 128x128 weight block quantizer                                      */
+/* ------------------------------------------------------------------ */
+
+/* w: fp32 [N][K]; q: [N][K]; s: [N/128][K/128].  N, K multiples of 128. */
+void orc_weight_block_quant(const float *w, int64_t N, int64_t K,
+                            uint8_t *q, float *s, float eps, int ue8m0)
+{
+    int64_t kb_n = K / ORC_GROUP;
+    for (int64_t nb = 0; nb < N / ORC_GROUP; ++nb) {
+        for (int64_t kb = 0; kb < kb_n; ++kb) {
+            float amax = 0.0f;
+            for (int64_t i = 0; i < ORC_GROUP; ++i)
+                for (int64_t j = 0; j < ORC_GROUP; ++j) {
+                    float a = fabsf(w[(nb * ORC_GROUP + i) * K + kb * ORC_GROUP + j]);
+                    if (a > amax)
+                        amax = a;
+                }
+            float sc = orc_scale_from_amax(amax, eps, ue8m0);
+            s[nb * kb_n + kb] = sc;
+            for (int64_t i = 0; i < ORC_GROUP; ++i)
+                for (int64_t j = 0; j < ORC_GROUP; ++j) {
+                    int64_t idx = (nb * ORC_GROUP + i) * K + kb * ORC_GROUP + j;
+                    q[idx] = quantize_one(w[idx], sc);
+                }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* blockwise-scaled GEMM, fp64                                         */
+/* ------------------------------------------------------------------ */
+
+/* y[r][n] = sum_k (dec(qa[m][k]) * sa[m][k/128]) * (dec(qw[n][k]) * sw[n/128][k/128])
+ * for m = rows[r] (or m = r when rows is NULL), summed in increasing k.
+ * qa: [M][K], sa: [M][K/128], qw: [N][K], sw: [N/128][K/128], y: [nrows][N].
+ * Every output is an independent fixed-order sum, so the row split over
+ * threads does not change any result. */
+typedef struct {
+    const uint8_t *qa;
+    const float *sa;
+    const uint8_t *qw;
+    const float *sw;
+    int64_t N, K;
+    const int64_t *rows;
+    int64_t r0, r1;
+    double *y;
+} gemm_job;
+
+static void *gemm_worker(void *arg)
+{
+    gemm_job *j = (gemm_job *)arg;
+    double dec[256];
+    int64_t kb_n = j->K / ORC_GROUP;
+    for (int c = 0; c < 256; ++c)
+        dec[c] = orc_e4m3_decode((uint8_t)c);
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        int64_t m = j->rows ? j->rows[r] : r;
+        const uint8_t *arow = j->qa + m * j->K;
+        const float *srow = j->sa + m * kb_n;
+        for (int64_t n = 0; n < j->N; ++n) {
+            const uint8_t *wrow = j->qw + n * j->K;
+            const float *swrow = j->sw + (n / ORC_GROUP) * kb_n;
+            double acc = 0.0;
+            for (int64_t k = 0; k < j->K; ++k) {
+                double a = dec[arow[k]] * (double)srow[k / ORC_GROUP];
+                double b = dec[wrow[k]] * (double)swrow[k / ORC_GROUP];
+                acc += a * b;
+            }
+            j->y[r * j->N + n] = acc;
+        }
+    }
+    return NULL;
+}
+
+int orc_block_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                   const float *sw, int64_t M, int64_t N, int64_t K,
+                   const int64_t *rows, int64_t nrows, double *y, int nthreads)
+{
+    int64_t total = rows ? nrows : M;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (total < nthreads)
+        nthreads = total > 0 ? (int)total : 1;
+    pthread_t tid[256];
+    gemm_job jobs[256];
+    int64_t per = (total + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        gemm_job *j = &jobs[t];
+        j->qa = qa; j->sa = sa; j->qw = qw; j->sw = sw;
+        j->N = N; j->K = K; j->rows = rows; j->y = y;
+        j->r0 = t * per;
+        j->r1 = (t + 1) * per < total ? (t + 1) * per : total;
+        tid[t] = 0;
+        if (j->r0 >= j->r1)
+            continue;
+        if (pthread_create(&tid[t], NULL, gemm_worker, j) != 0) {
+            gemm_worker(j);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+    return nthreads;
+}
+
+/* Row-parallel group quantizer over threads (each row independent). */
+typedef struct {
+    const uint16_t *x;
+    int64_t K, ldx, ldq, lds, m0, m1;
+    uint8_t *q;
+    float *s;
+    float eps;
+    int ue8m0;
+} quant_job;
+
+static void *quant_worker(void *arg)
+{
+    quant_job *j = (quant_job *)arg;
+    orc_group_quant(j->x + j->m0 * j->ldx, j->m1 - j->m0, j->K, j->ldx,
+                    j->q + j->m0 * j->ldq, j->ldq, j->s + j->m0 * j->lds,
+                    j->lds, j->eps, j->ue8m0);
+    return NULL;
+}
+
+int orc_group_quant_mt(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                       float eps, int ue8m0, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (M < nthreads)
+        nthreads = M > 0 ? (int)M : 1;
+    pthread_t tid[256];
+    quant_job jobs[256];
+    int64_t per = (M + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        quant_job *j = &jobs[t];
+        j->x = x; j->K = K; j->ldx = ldx; j->ldq = ldq; j->lds = lds;
+        j->q = q; j->s = s; j->eps = eps; j->ue8m0 = ue8m0;
+        j->m0 = t * per;
+        j->m1 = (t + 1) * per < M ? (t + 1) * per : M;
+        tid[t] = 0;
+        if (j->m0 >= j->m1)
+            continue;
+        if (pthread_create(&tid[t], NULL, quant_worker, j) != 0) {
+            quant_worker(j);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+    return nthreads;
+}
+
+/* 128-row bands of W are independent: threads over bands. */
+typedef struct {
+    const float *w;
+    int64_t N, K, nb0, nb1;
+    uint8_t *q;
+    float *s;
+    float eps;
+    int ue8m0;
+} wq_job;
+
+static void *wq_worker(void *arg)
+{
+    wq_job *j = (wq_job *)arg;
+    int64_t off = j->nb0 * ORC_GROUP;
+    orc_weight_block_quant(j->w + off * j->K, (j->nb1 - j->nb0) * ORC_GROUP, j->K,
+                           j->q + off * j->K, j->s + j->nb0 * (j->K / ORC_GROUP),
+                           j->eps, j->ue8m0);
+    return NULL;
+}
+
+int orc_weight_block_quant_mt(const float *w, int64_t N, int64_t K, uint8_t *q,
+                              float *s, float eps, int ue8m0, int nthreads)
+{
+    int64_t nbands = N / ORC_GROUP;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nbands < nthreads)
+        nthreads = nbands > 0 ? (int)nbands : 1;
+    pthread_t tid[256];
+    wq_job jobs[256];
+    int64_t per = (nbands + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        wq_job *j = &jobs[t];
+        j->w = w; j->N = N; j->K = K; j->q = q; j->s = s;
+        j->eps = eps; j->ue8m0 = ue8m0;
+        j->nb0 = t * per;
+        j->nb1 = (t + 1) * per < nbands ? (t + 1) * per : nbands;
+        tid[t] = 0;
+        if (j->nb0 >= j->nb1)
+            continue;
+        if (pthread_create(&tid[t], NULL, wq_worker, j) != 0) {
+            wq_worker(j);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+    return nthreads;
+}
+
+/* Threaded codec over a flat array (used by the exhaustive codec pin). */
+typedef struct {
+    const float *t;
+    uint8_t *q;
+    int64_t i0, i1;
+} enc_job;
+
+static void *enc_worker(void *arg)
+{
+    enc_job *j = (enc_job *)arg;
+    orc_e4m3_encode_array(j->t + j->i0, j->q + j->i0, j->i1 - j->i0);
+    return NULL;
+}
+
+int orc_e4m3_encode_array_mt(const float *t, uint8_t *q, int64_t n, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t tid[256];
+    enc_job jobs[256];
+    int64_t per = (n + nthreads - 1) / nthreads;
+    for (int i = 0; i < nthreads; ++i) {
+        enc_job *j = &jobs[i];
+        j->t = t; j->q = q;
+        j->i0 = i * per;
+        j->i1 = (i + 1) * per < n ? (i + 1) * per : n;
+        tid[i] = 0;
+        if (j->i0 >= j->i1)
+            continue;
+        if (pthread_create(&tid[i], NULL, enc_worker, j) != 0) {
+            enc_worker(j);
+            tid[i] = 0;
+        }
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (tid[i])
+            pthread_join(tid[i], NULL);
+    return nthreads;
+}
