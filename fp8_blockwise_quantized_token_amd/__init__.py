@@ -1,0 +1,224 @@
+"""MI355X (gfx950) FP8 blockwise-quantized linear layer.
+
+Python binding of ``libfp8blk.so`` (C ABI in ``include/fp8blk.h``).  This
+module only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and streams.  If the
+library has not been built, every call raises ``RuntimeError``; there is no
+fallback implementation.
+
+Entry points (same names as the C ABI):
+  fp8_group_quant        per-token 1x128 group quantization (bf16 -> e4m3fn + fp32 scales)
+  fp8_weight_block_quant 128x128 weight block quantization (fp32 -> e4m3fn + fp32 scales)
+  fp8_e4m3_encode        the saturating round-to-nearest-even encoder alone
+  fp8_block_gemm_select  per-shape dispatch (host only)
+  fp8_block_gemm_workspace_size
+  fp8_block_gemm         blockwise-scaled FP8 GEMM, bf16 out
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
+
+GROUP = 128
+FLAG_UE8M0 = 1
+STANDARD = 0
+SWAPAB = 1
+DEFAULT_EPS = 1e-10
+
+_STATUS = {0: "ok", -1: "null pointer", -2: "unsupported shape", -3: "misaligned",
+           -4: "leading dimension too small", -5: "workspace too small",
+           -6: "unsupported configuration", -7: "HIP launch failure"}
+
+
+class GemmConfig(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("kwaves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+    def as_dict(self) -> dict:
+        return {"variant": "swapab" if self.variant == SWAPAB else "standard",
+                "tile_m": self.tile_m, "tile_n": self.tile_n,
+                "split_k": self.split_k, "kwaves": self.kwaves}
+
+    def __repr__(self) -> str:
+        return f"GemmConfig({self.as_dict()})"
+
+
+def make_config(variant: int, tile_m: int, tile_n: int, split_k: int = 1, kwaves: int = 1) -> GemmConfig:
+    c = GemmConfig()
+    c.variant, c.tile_m, c.tile_n, c.split_k, c.kwaves = variant, tile_m, tile_n, split_k, kwaves
+    return c
+
+
+class Fp8BlkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: status {status} ({_STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (ctypes handle with argument types set)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, U32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+    L.fp8_abi_version.restype = ctypes.c_int
+    L.fp8_abi_version.argtypes = []
+    L.fp8_status_string.restype = ctypes.c_char_p
+    L.fp8_status_string.argtypes = [ctypes.c_int]
+    L.fp8_group_quant.restype = ctypes.c_int
+    L.fp8_group_quant.argtypes = [P, I64, I64, I64, P, I64, P, I64, I32, F, U32, P]
+    L.fp8_weight_block_quant.restype = ctypes.c_int
+    L.fp8_weight_block_quant.argtypes = [P, I64, I64, I64, P, I64, P, I64, F, U32, P]
+    L.fp8_e4m3_encode.restype = ctypes.c_int
+    L.fp8_e4m3_encode.argtypes = [P, P, I64, P]
+    L.fp8_block_gemm_select.restype = ctypes.c_int
+    L.fp8_block_gemm_select.argtypes = [I64, I64, I64, U32, ctypes.POINTER(GemmConfig)]
+    L.fp8_block_gemm_workspace_size.restype = I64
+    L.fp8_block_gemm_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(GemmConfig)]
+    L.fp8_block_gemm.restype = ctypes.c_int
+    L.fp8_block_gemm.argtypes = [P, P, I64, I64, P, P, I64, I64, P, I64, I64, I64, I64,
+                                 ctypes.POINTER(GemmConfig), P, I64, P]
+    _lib = L
+    return L
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ld(t, what: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{what}: expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _check(st: int, what: str) -> None:
+    if st != 0:
+        raise Fp8BlkError(st, what)
+
+
+def fp8_abi_version() -> int:
+    return lib().fp8_abi_version()
+
+
+def fp8_status_string(status: int) -> str:
+    return lib().fp8_status_string(status).decode()
+
+
+def fp8_group_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
+    """x: bf16 [M, K] (cuda), q: 1-byte [M, K], s: float32 [M, K/128]; outputs overwritten."""
+    M, K = x.shape
+    if q.shape != (M, K) or s.shape[0] != M or x.element_size() != 2 or q.element_size() != 1:
+        raise ValueError("fp8_group_quant: shape/dtype mismatch")
+    st = lib().fp8_group_quant(x.data_ptr(), M, K, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
+                               s.data_ptr(), _ld(s, "s"), GROUP, eps,
+                               FLAG_UE8M0 if ue8m0 else 0, _stream(stream))
+    _check(st, "fp8_group_quant")
+
+
+def fp8_weight_block_quant(w, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
+    """w: float32 [N, K], q: 1-byte [N, K], s: float32 [N/128, K/128]."""
+    N, K = w.shape
+    if q.shape != (N, K) or w.element_size() != 4 or q.element_size() != 1:
+        raise ValueError("fp8_weight_block_quant: shape/dtype mismatch")
+    st = lib().fp8_weight_block_quant(w.data_ptr(), N, K, _ld(w, "w"), q.data_ptr(), _ld(q, "q"),
+                                      s.data_ptr(), _ld(s, "s"), eps,
+                                      FLAG_UE8M0 if ue8m0 else 0, _stream(stream))
+    _check(st, "fp8_weight_block_quant")
+
+
+def fp8_e4m3_encode(t, q, stream=None) -> None:
+    """t: contiguous float32 (any shape), q: contiguous 1-byte, same number of elements."""
+    if not (t.is_contiguous() and q.is_contiguous()) or t.numel() != q.numel():
+        raise ValueError("fp8_e4m3_encode: need contiguous tensors of equal size")
+    _check(lib().fp8_e4m3_encode(t.data_ptr(), q.data_ptr(), t.numel(), _stream(stream)),
+           "fp8_e4m3_encode")
+
+
+def fp8_block_gemm_select(M: int, N: int, K: int, flags: int = 0) -> GemmConfig:
+    c = GemmConfig()
+    _check(lib().fp8_block_gemm_select(M, N, K, flags, ctypes.byref(c)), "fp8_block_gemm_select")
+    return c
+
+
+def fp8_block_gemm_workspace_size(M: int, N: int, K: int, cfg: GemmConfig | None = None) -> int:
+    n = lib().fp8_block_gemm_workspace_size(M, N, K, ctypes.byref(cfg) if cfg is not None else None)
+    if n < 0:
+        raise Fp8BlkError(int(n), "fp8_block_gemm_workspace_size")
+    return int(n)
+
+
+def fp8_block_gemm(a, sa, w, sw, y, cfg: GemmConfig | None = None, workspace=None,
+                   stream=None) -> None:
+    """y[M, N] (bf16) = blockwise-scaled a[M, K] (e4m3fn) x w[N, K]^T."""
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or y.shape != (M, N):
+        raise ValueError("fp8_block_gemm: shape mismatch")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_block_gemm(a.data_ptr(), sa.data_ptr(), _ld(a, "a"), _ld(sa, "sa"),
+                              w.data_ptr(), sw.data_ptr(), _ld(w, "w"), _ld(sw, "sw"),
+                              y.data_ptr(), _ld(y, "y"), M, N, K,
+                              ctypes.byref(cfg) if cfg is not None else None,
+                              ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "fp8_block_gemm")
+
+
+# -- conveniences that allocate their outputs with torch (plumbing only) ----
+
+def quantize_activations(x, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
+    import torch
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // GROUP), dtype=torch.float32, device=x.device)
+    fp8_group_quant(x, q, s, eps, ue8m0, stream)
+    return q, s
+
+
+def quantize_weight(w, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
+    import torch
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // GROUP, K // GROUP), dtype=torch.float32, device=w.device)
+    fp8_weight_block_quant(w, q, s, eps, ue8m0, stream)
+    return q, s
+
+
+def workspace_for(M: int, N: int, K: int, cfg: GemmConfig | None, device):
+    import torch
+    n = fp8_block_gemm_workspace_size(M, N, K, cfg)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device) if n else None
+
+
+def block_gemm(a, sa, w, sw, cfg: GemmConfig | None = None, stream=None):
+    import torch
+    M, K = a.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = workspace_for(M, N, K, cfg, a.device)
+    fp8_block_gemm(a, sa, w, sw, y, cfg, ws, stream)
+    return y
+
+
+def linear(x, qw, sw, eps: float = DEFAULT_EPS, ue8m0: bool = False, cfg: GemmConfig | None = None,
+           stream=None):
+    """The whole FP8 linear layer: quantize x per 1x128 group, then the blockwise GEMM."""
+    qa, sa = quantize_activations(x, eps, ue8m0, stream)
+    return block_gemm(qa, sa, qw, sw, cfg, stream)

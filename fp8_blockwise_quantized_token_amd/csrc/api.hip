@@ -1,0 +1,186 @@
+// api.hip -- the C ABI of libfp8blk (declared in include/fp8blk.h).
+//
+// Every entry point validates its arguments completely before touching the
+// HIP runtime, so that a bad call returns an error code with nothing
+// launched.  No entry point allocates, synchronizes or reads device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fp8blk.h"
+#include "dispatch.hpp"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kG = FP8BLK_GROUP;
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // every extent fits int32 index math
+constexpr int64_t kMaxK = int64_t(1) << 22;    // the strided quantizer's row division
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HIP; }
+
+int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
+  const int64_t kb = K / kG;
+  for (int i = 0; i < 3; ++i)
+    if (c.reserved[i] != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.split_k < 1 || c.split_k > 256 || c.split_k > kb) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.variant == FP8BLK_STANDARD) {
+    if (!fp8blk::standard_tile_supported(c.tile_m, c.tile_n)) return FP8BLK_ERR_BAD_CONFIG;
+    if (N % c.tile_n != 0) return FP8BLK_ERR_BAD_CONFIG;
+    // one workgroup per (tile, split): the grid must fit a 32-bit count
+    const int64_t blocks = ((M + c.tile_m - 1) / c.tile_m) * (N / c.tile_n) * c.split_k;
+    if (blocks > 2147483647) return FP8BLK_ERR_BAD_SHAPE;
+    return FP8BLK_OK;
+  }
+  if (c.variant == FP8BLK_SWAPAB) {
+    if (!fp8blk::swapab_tile_supported(c.tile_m, c.tile_n, c.kwaves)) return FP8BLK_ERR_BAD_CONFIG;
+    if (M > c.tile_m) return FP8BLK_ERR_BAD_CONFIG;
+    return FP8BLK_OK;
+  }
+  return FP8BLK_ERR_BAD_CONFIG;
+}
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0) return FP8BLK_ERR_BAD_SHAPE;
+  if (K % kG != 0 || N % kG != 0) return FP8BLK_ERR_BAD_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  return FP8BLK_OK;
+}
+
+int64_t workspace_for(const fp8blk_gemm_config& c, int64_t M, int64_t N) {
+  return c.split_k > 1 ? (int64_t)c.split_k * M * N * 4 : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8BLK_ABI_VERSION; }
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8BLK_OK: return "ok";
+    case FP8BLK_ERR_NULL_PTR: return "null pointer";
+    case FP8BLK_ERR_BAD_SHAPE: return "unsupported shape";
+    case FP8BLK_ERR_MISALIGNED: return "misaligned pointer or row pitch";
+    case FP8BLK_ERR_BAD_STRIDE: return "leading dimension too small";
+    case FP8BLK_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8BLK_ERR_BAD_CONFIG: return "unsupported GEMM configuration";
+    case FP8BLK_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int fp8_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                    float* s, int64_t lds, int32_t group, float eps, uint32_t flags, void* stream) {
+  if (group != kG) return FP8BLK_ERR_BAD_SHAPE;
+  if (M < 0 || K <= 0 || K % kG != 0 || K > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (ldx < K || ldq < K || lds < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(s) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_group_quant(x, M, K, ldx, q, ldq, s, lds, eps,
+                                              (flags & FP8BLK_FLAG_UE8M0) != 0,
+                                              (hipStream_t)stream));
+}
+
+int fp8_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                           int64_t ldq, float* s, int64_t lds, float eps, uint32_t flags,
+                           void* stream) {
+  if (N < 0 || K < 0 || N % kG != 0 || K % kG != 0 || N >= kMaxDim || K >= kMaxDim)
+    return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (ldw < K || ldq < K || lds < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (N == 0 || K == 0) return FP8BLK_OK;
+  if (!w || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(w) || !aligned16(q) || !aligned4(s) || (ldw * 4) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  if (K / kG > 2147483647 || N / kG > 2147483647) return FP8BLK_ERR_BAD_SHAPE;
+  return to_status(fp8blk::launch_weight_block_quant(w, N, K, ldw, q, ldq, s, lds, eps,
+                                                     (flags & FP8BLK_FLAG_UE8M0) != 0,
+                                                     (hipStream_t)stream));
+}
+
+int fp8_e4m3_encode(const float* t, uint8_t* q, int64_t n, void* stream) {
+  if (n < 0) return FP8BLK_ERR_BAD_SHAPE;
+  if (n == 0) return FP8BLK_OK;
+  if (!t || !q) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(t) || !aligned16(q)) return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_e4m3_encode(t, q, n, (hipStream_t)stream));
+}
+
+int fp8_block_gemm_select(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8blk_gemm_config* out) {
+  if (!out) return FP8BLK_ERR_NULL_PTR;
+  const int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  fp8blk::select_config(M, N, K, flags, out);
+  return FP8BLK_OK;
+}
+
+int64_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, const fp8blk_gemm_config* cfg) {
+  const int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+    const int cs = check_config(c, M, N, K);
+    if (cs != FP8BLK_OK) return cs;
+  } else {
+    fp8blk::select_config(M, N, K, 0, &c);
+  }
+  return workspace_for(c, M, N);
+}
+
+int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa, const uint8_t* w,
+                   const float* sw, int64_t ldw, int64_t ldsw, uint16_t* y, int64_t ldy, int64_t M,
+                   int64_t N, int64_t K, const fp8blk_gemm_config* cfg, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    fp8blk::select_config(M, N, K, 0, &c);
+  }
+  st = check_config(c, M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (lda < K || ldw < K || ldy < N || ldsa < K / kG || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!a || !sa || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned4(sa) || !aligned4(sw) ||
+      lda % 16 != 0 || ldw % 16 != 0 || (ldy * 2) % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  const int64_t need = workspace_for(c, M, N);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8BLK_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
+  }
+  fp8blk::GemmArgs g;
+  g.a = a;
+  g.sa = sa;
+  g.lda = lda;
+  g.ldsa = ldsa;
+  g.w = w;
+  g.sw = sw;
+  g.ldw = ldw;
+  g.ldsw = ldsw;
+  g.y = y;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ws = need > 0 ? (float*)workspace : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if (c.variant == FP8BLK_STANDARD)
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, s));
+  return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// device_common.hpp -- gfx950 device helpers shared by the library's kernels.
+//
+// Quantization rule (Block_FP8, 1x128 activation / 128x128 weight scaling:
+// page "Helion: improving vLLM inference with autotuning", section "Helion
+// Linear Backend" / "Scope"): scale = max(amax, eps) / 448, optionally
+// rounded up to a power of two (UE8M0: page "Helion-Kernel in vLLM: PyTorch
+// FP8 ohne CUDA", section "Praktische Einschränkungen"), then every value is
+// divided by the scale in fp32, clamped to +-448 and rounded to the nearest
+// e4m3fn code (ties to even).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+constexpr int kGroup = 128;
+constexpr float kE4M3Max = 448.0f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// bf16 halves of a packed dword, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15): two quad
+// permutations, then the half-row and row mirrors.  Every lane of the row
+// ends with the row maximum.  Operates on non-negative fp32 bit patterns,
+// which order like unsigned integers.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // row_mirror
+  return v;
+}
+
+// scale = max(amax, eps) / 448 (correctly rounded fp32 division), with the
+// optional power-of-two ceiling done on the exponent field.
+__device__ __forceinline__ float scale_from_amax(float amax, float eps, bool ue8m0) {
+  float a = amax > eps ? amax : eps;
+  float s = a / kE4M3Max;
+  if (ue8m0) {
+    uint32_t b = __float_as_uint(s);
+    if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+    s = __uint_as_float(b);
+  }
+  return s;
+}
+
+// x / s, correctly rounded, from y = RN(1/s): q0 = RN(x y) is within one ulp
+// of x/s, the residual x - q0 s is exact under an FMA, and one correction
+// step RN(q0 + r y) rounds to RN(x/s) (Markstein's division theorem).  The
+// sign is copied from x so that x = -0 (and results that underflow) keep
+// the sign IEEE division gives them.  The test-suite checks this against
+// IEEE division for every pair of bf16 value and bf16-derived scale
+// significands.
+__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
+  float q0 = x * y;
+  float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+}
+
+// Four already-scaled values -> four e4m3fn codes (byte i = value i), clamp
+// to +-448 first.  gfx950's v_cvt_pk_fp8_f32 rounds to nearest even into the
+// OCP e4m3fn format.
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+  d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// 16x16x128 fp8 x fp8 -> fp32 matrix-core product (no block scaling).
+// Operand layout: lane l supplies row (l & 15) of its matrix and the 32
+// consecutive K bytes starting at 32 * (l >> 4).  Result: lane l holds
+// column (l & 15), rows 4 * (l >> 4) + 0..3.
+__device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: data used once, keep it out of the
+// caches' way).
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ __forceinline__ v8i make_v8i(u32x4 lo, u32x4 hi) {
+  v8i r;
+  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,83 @@
+// dispatch.cpp -- per-shape choice among the GEMM variants (host only).
+//
+// The pages tune one GEMM per shape and pick the best variant and tile
+// configuration for each (page "Helion: improving vLLM inference with
+// autotuning", sections "Kernel Implementation", "Hybrid Dispatch" and
+// "Per-shape Config Tuning").  Here the choice is a compiled-in table keyed
+// on (N, K) and a bucket of M, measured on MI355X, with a heuristic for
+// shapes the table does not hold (the pages fall back to a default config
+// rather than failing when no tuned config exists).  Lookup is O(1) and
+// deterministic; nothing is tuned at run time.
+#include <stdint.h>
+
+#include "../../include/fp8blk.h"
+#include "dispatch.hpp"
+
+namespace fp8blk {
+namespace {
+
+struct Entry {
+  int32_t n, k;       // weight shape
+  int32_t m_lo, m_hi; // inclusive bucket of M
+  fp8blk_gemm_config cfg;
+};
+
+#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, {0, 0, 0}}
+
+// Measured table (MI355X).  Entries are checked in order; the first bucket
+// containing M wins.
+#include "dispatch_table.inc"
+
+constexpr int kCUs = 256;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void heuristic(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* c) {
+  const int64_t kb = K / 128;
+  *c = fp8blk_gemm_config{};
+  if (M <= 64) {
+    // Swap-AB: tokens on the 16-wide column side of the matrix core.
+    c->variant = FP8BLK_SWAPAB;
+    c->tile_m = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    c->tile_n = 16;
+    c->kwaves = kb >= 8 ? 8 : (kb >= 4 ? 4 : (kb >= 2 ? 2 : 1));
+    int64_t split = 1;
+    const int64_t blocks = N / c->tile_n;
+    while (blocks * split < 2 * kCUs && split * 2 * c->kwaves <= kb && split < 256) split *= 2;
+    c->split_k = (int32_t)split;
+    return;
+  }
+  c->variant = FP8BLK_STANDARD;
+  const int64_t t256 = cdiv(M, 256) * (N / 128);
+  const int64_t t128 = cdiv(M, 128) * (N / 128);
+  if (t256 >= kCUs) {
+    c->tile_m = 256;
+    c->tile_n = 128;
+  } else if (t128 >= kCUs) {
+    c->tile_m = 128;
+    c->tile_n = 128;
+  } else {
+    c->tile_m = M <= 64 ? 64 : 128;
+    c->tile_n = 128;
+  }
+  const int64_t tiles = cdiv(M, c->tile_m) * (N / c->tile_n);
+  int64_t split = 1;
+  while (tiles * split < kCUs && split * 2 * 4 <= kb && split < 256) split *= 2;
+  c->split_k = (int32_t)split;
+  c->kwaves = 1;
+}
+
+}  // namespace
+
+void select_config(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8blk_gemm_config* out) {
+  (void)flags;
+  for (const Entry& e : kTable) {
+    if (e.n == N && e.k == K && M >= e.m_lo && M <= e.m_hi) {
+      *out = e.cfg;
+      return;
+    }
+  }
+  heuristic(M, N, K, out);
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,47 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                              float eps, bool ue8m0, hipStream_t stream);
+
+hipError_t launch_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw,
+                                     uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                     float eps, bool ue8m0, hipStream_t stream);
+
+hipError_t launch_e4m3_encode(const float* t, uint8_t* q, int64_t n, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t* a;
+  const float* sa;
+  int64_t lda, ldsa;
+  const uint8_t* w;
+  const float* sw;
+  int64_t ldw, ldsw;
+  uint16_t* y;
+  int64_t ldy;
+  int64_t M, N, K;
+  float* ws;  // split-K partials [split][M][N], or nullptr
+};
+
+// Standard variant: (tile_m, tile_n) among the compiled tiles.
+bool standard_tile_supported(int tile_m, int tile_n);
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k,
+                                hipStream_t stream);
+
+// Swap-AB variant.
+bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);
+hipError_t launch_gemm_swapab(const GemmArgs& g, int tile_m, int tile_n, int kwaves,
+                              int split_k, hipStream_t stream);
+
+// Fixed-order sum of split_k fp32 partials -> bf16.
+hipError_t launch_splitk_reduce(const float* ws, int split_k, int64_t M, int64_t N,
+                                uint16_t* y, int64_t ldy, hipStream_t stream);
+
+}  // namespace fp8blk

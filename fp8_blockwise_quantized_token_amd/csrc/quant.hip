@@ -1,0 +1,229 @@
+// quant.hip -- per-token 1x128 group quantizer, 128x128 weight block
+// quantizer and the bare e4m3fn encoder for gfx950.
+//
+// per_token_group_fp8_quant (page "[RFC]: Using Helion for Selected vLLM
+// CustomOps", section "Motivation"; Block_FP8 1x128 activation scaling on
+// page "Helion: improving vLLM inference with autotuning", section "Helion
+// Linear Backend" / "Scope").
+//
+// Group quantizer design (HBM-bound: 2 bytes in, 1 byte + 4/128 out per
+// element):
+//   - 16 lanes (one DPP row) own one 128-element group; each lane loads 16
+//     contiguous bytes (8 bf16) with one global_load_dwordx4, so a wave reads
+//     four whole groups = 1 KiB of contiguous HBM per load instruction.
+//   - U = 4 groups per lane are loaded before any is used, keeping 4 KiB per
+//     wave in flight.
+//   - amax: packed u16 max of |bf16| bit patterns in registers, then a 4-step
+//     DPP reduction inside the row (no LDS, no barriers).
+//   - scale = max(amax, eps)/448 once per group (IEEE division), 1/scale once
+//     per group, and every element divided by the scale with a 3-instruction
+//     correctly rounded division (Markstein) instead of a full IEEE divide.
+//   - clamp with v_med3 and encode two values per v_cvt_pk_fp8_f32; 8 bytes
+//     stored per lane.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+#pragma clang fp contract(off)
+
+namespace fp8blk {
+namespace {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t amax8_bits(u32x4 v) {
+  // |bf16| bit patterns order like their magnitudes.
+  us2 a = __builtin_bit_cast(us2, v.x & 0x7FFF7FFFu);
+  us2 b = __builtin_bit_cast(us2, v.y & 0x7FFF7FFFu);
+  us2 c = __builtin_bit_cast(us2, v.z & 0x7FFF7FFFu);
+  us2 d = __builtin_bit_cast(us2, v.w & 0x7FFF7FFFu);
+  us2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  uint32_t mm = m.x > m.y ? m.x : m.y;
+  return mm << 16;
+}
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantUnroll = 4;
+constexpr uint32_t kGroupsPerIter = (kQuantThreads / 16) * kQuantUnroll;
+
+template <bool UE8M0, bool CONTIG>
+__global__ __launch_bounds__(kQuantThreads) void k_group_quant(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s,
+    uint32_t total_groups, uint32_t gpr, uint64_t magic, int64_t ldx, int64_t ldq,
+    int64_t lds, float eps) {
+  const uint32_t sub = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;
+  const uint32_t step = gridDim.x * kGroupsPerIter;
+  for (uint32_t base = blockIdx.x * kGroupsPerIter; base < total_groups; base += step) {
+    u32x4 v[kQuantUnroll];
+    int64_t qo[kQuantUnroll], so[kQuantUnroll];
+    bool valid[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const uint32_t g = base + u * 16u + slot;
+      valid[u] = g < total_groups;
+      int64_t xo;
+      if (CONTIG) {
+        xo = (int64_t)g * kGroup + sub * 8;
+        qo[u] = xo;
+        so[u] = g;
+      } else {
+        const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
+        const uint32_t col = g - row * gpr;
+        xo = (int64_t)row * ldx + (int64_t)col * kGroup + sub * 8;
+        qo[u] = (int64_t)row * ldq + (int64_t)col * kGroup + sub * 8;
+        so[u] = (int64_t)row * lds + col;
+      }
+      v[u] = valid[u] ? load_nt16(x + xo) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const float amax = __uint_as_float(row16_max_u32(amax8_bits(v[u])));
+      const float sc = scale_from_amax(amax, eps, UE8M0);
+      const float rc = 1.0f / sc;
+      const u32x4 w = v[u];
+      const uint32_t lo = encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+                                  div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
+      const uint32_t hi = encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+                                  div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
+      if (valid[u]) {
+        *(uint2*)(q + qo[u]) = make_uint2(lo, hi);
+        if (sub == 0) s[so[u]] = sc;
+      }
+    }
+  }
+}
+
+// One workgroup per 128x128 block: thread t owns half a row (64 floats).
+template <bool UE8M0>
+__global__ __launch_bounds__(256) void k_weight_block_quant(
+    const float* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s, int64_t lds, float eps) {
+  __shared__ float red[4];
+  const int kb = blockIdx.x;
+  const int64_t nb = blockIdx.y;
+  const int t = threadIdx.x;
+  const int row = t >> 1, half = t & 1;
+  const float4* src = (const float4*)(w + (nb * kGroup + row) * ldw + (int64_t)kb * kGroup + half * 64);
+  float4 v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = src[i];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = scale_from_amax(amax, eps, UE8M0);
+  uint4* dst = (uint4*)(q + (nb * kGroup + row) * ldq + (int64_t)kb * kGroup + half * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 o;
+    o.x = encode4(v[4 * i].x / sc, v[4 * i].y / sc, v[4 * i].z / sc, v[4 * i].w / sc);
+    o.y = encode4(v[4 * i + 1].x / sc, v[4 * i + 1].y / sc, v[4 * i + 1].z / sc, v[4 * i + 1].w / sc);
+    o.z = encode4(v[4 * i + 2].x / sc, v[4 * i + 2].y / sc, v[4 * i + 2].z / sc, v[4 * i + 2].w / sc);
+    o.w = encode4(v[4 * i + 3].x / sc, v[4 * i + 3].y / sc, v[4 * i + 3].z / sc, v[4 * i + 3].w / sc);
+    dst[i] = o;
+  }
+  if (t == 0) s[nb * lds + kb] = sc;
+}
+
+__global__ __launch_bounds__(256) void k_e4m3_encode(const float* __restrict__ t,
+                                                     uint8_t* __restrict__ q, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      const float4 v = *(const float4*)(t + i);
+      *(uint32_t*)(q + i) = encode4(v.x, v.y, v.z, v.w);
+    } else {
+      for (int64_t j = i; j < n; ++j) q[j] = (uint8_t)(encode4(t[j], 0.f, 0.f, 0.f) & 0xFFu);
+    }
+  }
+}
+
+int device_cu_count() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  return cus;
+}
+
+}  // namespace
+
+hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* s, int64_t lds, float eps, bool ue8m0,
+                              hipStream_t stream) {
+  const int64_t gpr = K / kGroup;
+  const bool contig = (ldx == K) && (ldq == K) && (lds == gpr);
+  const int max_blocks = device_cu_count() * 8;
+  // Contiguous: one flat launch per 2^31 groups.  Strided: row chunks with
+  // fewer than 2^24 groups, so that row = (g * ceil(2^40/gpr)) >> 40 is exact.
+  const int64_t chunk_groups = contig ? (int64_t(1) << 31) : (int64_t(1) << 24);
+  int64_t rows_per_chunk = chunk_groups / gpr;
+  if (rows_per_chunk < 1) rows_per_chunk = 1;
+  const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)gpr - 1) / (uint64_t)gpr;
+  for (int64_t r0 = 0; r0 < M; r0 += rows_per_chunk) {
+    const int64_t rows = (M - r0) < rows_per_chunk ? (M - r0) : rows_per_chunk;
+    const uint32_t total = (uint32_t)(rows * gpr);
+    int64_t blocks = (total + kGroupsPerIter - 1) / kGroupsPerIter;
+    if (blocks > max_blocks) blocks = max_blocks;
+    const uint16_t* xr = x + r0 * ldx;
+    uint8_t* qr = q + r0 * ldq;
+    float* sr = s + r0 * lds;
+    dim3 grid((unsigned)blocks), block(kQuantThreads);
+    if (contig) {
+      if (ue8m0)
+        hipLaunchKernelGGL((k_group_quant<true, true>), grid, block, 0, stream, xr, qr, sr, total,
+                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+      else
+        hipLaunchKernelGGL((k_group_quant<false, true>), grid, block, 0, stream, xr, qr, sr, total,
+                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+    } else {
+      if (ue8m0)
+        hipLaunchKernelGGL((k_group_quant<true, false>), grid, block, 0, stream, xr, qr, sr, total,
+                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+      else
+        hipLaunchKernelGGL((k_group_quant<false, false>), grid, block, 0, stream, xr, qr, sr, total,
+                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                     int64_t ldq, float* s, int64_t lds, float eps, bool ue8m0,
+                                     hipStream_t stream) {
+  // grid.y is limited to 65535 row bands per launch
+  const int64_t nbands = N / kGroup;
+  for (int64_t b0 = 0; b0 < nbands; b0 += 65535) {
+    const int64_t nb = (nbands - b0) < 65535 ? (nbands - b0) : 65535;
+    dim3 grid((unsigned)(K / kGroup), (unsigned)nb), block(256);
+    const float* wb = w + b0 * kGroup * ldw;
+    uint8_t* qb = q + b0 * kGroup * ldq;
+    float* sb = s + b0 * lds;
+    if (ue8m0)
+      hipLaunchKernelGGL(k_weight_block_quant<true>, grid, block, 0, stream, wb, ldw, qb, ldq, sb, lds, eps);
+    else
+      hipLaunchKernelGGL(k_weight_block_quant<false>, grid, block, 0, stream, wb, ldw, qb, ldq, sb, lds, eps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_e4m3_encode(const float* t, uint8_t* q, int64_t n, hipStream_t stream) {
+  int64_t blocks = (n + 1023) / 1024;
+  const int64_t max_blocks = (int64_t)device_cu_count() * 16;
+  if (blocks > max_blocks) blocks = max_blocks;
+  hipLaunchKernelGGL(k_e4m3_encode, dim3((unsigned)blocks), dim3(256), 0, stream, t, q, n);
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

@@ -22,6 +22,8 @@ synthetic tensors of the same shapes stand in for them.
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -102,15 +104,47 @@ def outlier_channels(K: int, config_idx: int, shape_idx: int) -> np.ndarray:
     return np.sort(_rng(config_idx, shape_idx, 2).choice(K, size=n, replace=False))
 
 
+ROWS_PER_CHUNK = 256
+
+
+def _chunked(rows: int, cols: int, key: tuple, fill) -> np.ndarray:
+    """[rows, cols] fp32 drawn in fixed 256-row chunks, each from its own
+    generator keyed by (key, chunk index): the result does not depend on how
+    many threads draw it."""
+    out = np.empty((rows, cols), dtype=np.float32)
+    chunks = [(r0, min(rows, r0 + ROWS_PER_CHUNK)) for r0 in range(0, rows, ROWS_PER_CHUNK)]
+
+    def work(ci_r):
+        ci, (r0, r1) = ci_r
+        fill(_rng(*key, ci), out[r0:r1])
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    if len(chunks) == 1 or workers == 1:
+        for item in enumerate(chunks):
+            work(item)
+    else:
+        with _cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(work, enumerate(chunks)))
+    return out
+
+
+def _fill_normal(rng, dst):
+    rng.standard_normal(size=dst.shape, dtype=np.float32, out=dst)
+
+
+def _fill_student_t3(rng, dst):
+    dst[...] = rng.standard_t(3.0, size=dst.shape)
+
+
 def activations_f32(case: Case) -> np.ndarray:
     """X [M, K] in fp32 before the bf16 rounding; one draw per (config, shape, M)."""
     M = case.M
     ci = CONFIG_INDEX[case.config]
-    rng = _rng(ci, case.shape_idx, 0, M)
+    key = (ci, case.shape_idx, 0, M)
     if case.x_dist == "student_t3":
-        x = rng.standard_t(3.0, size=(M, case.K)).astype(np.float32)
+        x = _chunked(M, case.K, key, _fill_student_t3)
     else:
-        x = rng.standard_normal(size=(M, case.K), dtype=np.float32)
+        x = _chunked(M, case.K, key, _fill_normal)
         if case.x_dist == "normal_outlier":
             x[:, outlier_channels(case.K, ci, case.shape_idx)] *= np.float32(20.0)
     return x
@@ -121,11 +155,14 @@ def activations_bf16(case: Case) -> np.ndarray:
     return to_bf16_bits(activations_f32(case))
 
 
-def weights_f32(case: Case) -> np.ndarray:
-    """W [N, K] ~ N(0, 0.02) in fp32; one draw per (config, shape), independent of M."""
-    ci = CONFIG_INDEX[case.config]
-    rng = _rng(ci, case.shape_idx, 1)
-    w = rng.standard_normal(size=(case.N, case.K), dtype=np.float32)
+def weights_f32(case_or_n, K: int | None = None) -> np.ndarray:
+    """W [N, K] ~ N(0, 0.02) in fp32; one draw per (N, K): every workload that
+    uses a layer shape sees the same weight, whatever its M."""
+    if K is None:
+        N, K = case_or_n.N, case_or_n.K
+    else:
+        N = case_or_n
+    w = _chunked(N, K, (7, N, K, 1), _fill_normal)
     w *= np.float32(0.02)
     return w
 

@@ -1,0 +1,168 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/fp8blk.h declares, and rejects every invalid argument with its status
+code before any HIP call (the fake device addresses used here are never
+dereferenced).  Also the per-shape dispatcher, which is host-only.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_blockwise_quantized_token_amd as fb
+from fp8_blockwise_quantized_token_amd import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp8blk.h")
+
+OK, NULL, SHAPE, MISAL, STRIDE, WS, CFG = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000  # fake 16-byte aligned device addresses
+B = 0x20000
+C = 0x30000
+D = 0x40000
+E = 0x50000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"fp8_group_quant", "fp8_block_gemm", "fp8_block_gemm_select"} <= set(names)
+    L = fb.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert fb.fp8_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert fb.fp8_status_string(st) != "unknown status"
+    assert fb.fp8_status_string(-99) == "unknown status"
+
+
+def _gq(x=A, M=4, K=256, ldx=256, q=B, ldq=256, s=C, lds=2, group=128, eps=1e-10, flags=0):
+    return fb.lib().fp8_group_quant(x, M, K, ldx, q, ldq, s, lds, group, eps, flags, None)
+
+
+def test_group_quant_argument_errors():
+    assert _gq(x=None) == NULL
+    assert _gq(q=None) == NULL
+    assert _gq(s=None) == NULL
+    assert _gq(K=200, ldx=200, ldq=200) == SHAPE
+    assert _gq(M=-1) == SHAPE
+    assert _gq(group=64) == SHAPE
+    assert _gq(eps=0.0) == SHAPE
+    assert _gq(eps=float("inf")) == SHAPE
+    assert _gq(flags=2) == CFG
+    assert _gq(ldx=128) == STRIDE
+    assert _gq(ldq=128) == STRIDE
+    assert _gq(lds=1) == STRIDE
+    assert _gq(x=A + 2) == MISAL
+    assert _gq(q=B + 8) == MISAL
+    assert _gq(s=C + 2) == MISAL
+    assert _gq(ldx=260, ldq=256) == MISAL
+    assert _gq(ldq=264) == MISAL
+    # M == 0 is a no-op, no pointer is needed
+    assert _gq(M=0, x=None, q=None, s=None) == OK
+
+
+def _wq(w=A, N=256, K=256, ldw=256, q=B, ldq=256, s=C, lds=2, eps=1e-10, flags=0):
+    return fb.lib().fp8_weight_block_quant(w, N, K, ldw, q, ldq, s, lds, eps, flags, None)
+
+
+def test_weight_quant_argument_errors():
+    assert _wq(w=None) == NULL
+    assert _wq(N=200) == SHAPE
+    assert _wq(K=200, ldw=200, ldq=200) == SHAPE
+    assert _wq(ldw=128) == STRIDE
+    assert _wq(w=A + 4) == MISAL
+    assert _wq(ldw=257) == MISAL
+    assert _wq(flags=4) == CFG
+    assert _wq(N=0, w=None, q=None, s=None) == OK
+
+
+def test_encode_argument_errors():
+    L = fb.lib()
+    assert L.fp8_e4m3_encode(None, B, 16, None) == NULL
+    assert L.fp8_e4m3_encode(A, None, 16, None) == NULL
+    assert L.fp8_e4m3_encode(A + 4, B, 16, None) == MISAL
+    assert L.fp8_e4m3_encode(A, B, -1, None) == SHAPE
+    assert L.fp8_e4m3_encode(None, None, 0, None) == OK
+
+
+def _gemm(a=A, sa=B, lda=256, ldsa=2, w=C, sw=D, ldw=256, ldsw=2, y=E, ldy=256, M=8, N=256, K=256,
+          cfg=None, ws=None, ws_bytes=0):
+    return fb.lib().fp8_block_gemm(a, sa, lda, ldsa, w, sw, ldw, ldsw, y, ldy, M, N, K,
+                                   ctypes.byref(cfg) if cfg is not None else None, ws, ws_bytes, None)
+
+
+def test_gemm_argument_errors():
+    std = fb.make_config(fb.STANDARD, 128, 128)
+    assert _gemm(a=None, cfg=std) == NULL
+    assert _gemm(sa=None, cfg=std) == NULL
+    assert _gemm(w=None, cfg=std) == NULL
+    assert _gemm(sw=None, cfg=std) == NULL
+    assert _gemm(y=None, cfg=std) == NULL
+    assert _gemm(K=200, lda=256, ldw=256, cfg=std) == SHAPE
+    assert _gemm(N=200, ldy=256, cfg=std) == SHAPE
+    assert _gemm(M=-1, cfg=std) == SHAPE
+    assert _gemm(lda=128, cfg=std) == STRIDE
+    assert _gemm(ldw=128, cfg=std) == STRIDE
+    assert _gemm(ldy=128, cfg=std) == STRIDE
+    assert _gemm(ldsa=1, cfg=std) == STRIDE
+    assert _gemm(ldsw=1, cfg=std) == STRIDE
+    assert _gemm(a=A + 1, cfg=std) == MISAL
+    assert _gemm(w=C + 8, cfg=std) == MISAL
+    assert _gemm(y=E + 2, cfg=std) == MISAL
+    assert _gemm(lda=264, cfg=std) == MISAL
+    assert _gemm(ldy=260, cfg=std) == MISAL
+    assert _gemm(sa=B + 1, cfg=std) == MISAL
+    # configurations
+    assert _gemm(cfg=fb.make_config(7, 128, 128)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 96, 128)) == CFG
+    assert _gemm(N=384, ldy=384, cfg=fb.make_config(fb.STANDARD, 128, 256)) == CFG  # N % tile_n
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=0)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=4)) == CFG  # K/128 = 2 blocks
+    assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 3)) == CFG         # kwaves
+    assert _gemm(M=40, cfg=fb.make_config(fb.SWAPAB, 32, 16, 1, 4)) == CFG   # M > tile_m
+    bad = fb.make_config(fb.STANDARD, 128, 128)
+    bad.reserved[1] = 5
+    assert _gemm(cfg=bad) == CFG
+    # split-K needs a workspace of split * M * N * 4 bytes
+    sk = fb.make_config(fb.STANDARD, 128, 128, split_k=2)
+    assert fb.fp8_block_gemm_workspace_size(8, 256, 256, sk) == 2 * 8 * 256 * 4
+    assert _gemm(cfg=sk) == WS
+    assert _gemm(cfg=sk, ws=0x60000, ws_bytes=2 * 8 * 256 * 4 - 1) == WS
+    assert _gemm(cfg=sk, ws=0x60004, ws_bytes=2 * 8 * 256 * 4) == MISAL
+    # M == 0 is a no-op
+    assert _gemm(M=0, a=None, sa=None, w=None, sw=None, y=None, cfg=std) == OK
+
+
+def test_select_and_workspace_queries():
+    L = fb.lib()
+    assert L.fp8_block_gemm_select(1, 4096, 4096, 0, None) == NULL
+    assert L.fp8_block_gemm_workspace_size(1, 100, 4096, None) == SHAPE
+    for config in ("single", "decode_8b", "prefill_8b", "ue8m0_32b", "sweep"):
+        for case in synth.cases(config):
+            c = fb.fp8_block_gemm_select(case.M, case.N, case.K)
+            # every dispatched configuration is one the library accepts
+            n = fb.fp8_block_gemm_workspace_size(case.M, case.N, case.K, c)
+            assert n == (c.split_k * case.M * case.N * 4 if c.split_k > 1 else 0)
+            assert n == fb.fp8_block_gemm_workspace_size(case.M, case.N, case.K, None)
+            if c.variant == fb.SWAPAB:
+                assert case.M <= c.tile_m
+            assert 1 <= c.split_k <= case.K // 128
+
+
+def test_select_is_deterministic_and_swaps_small_m():
+    a = fb.fp8_block_gemm_select(8, 24576, 4096).as_dict()
+    b = fb.fp8_block_gemm_select(8, 24576, 4096).as_dict()
+    assert a == b
+    assert fb.fp8_block_gemm_select(1, 4096, 4096).variant == fb.SWAPAB
+    assert fb.fp8_block_gemm_select(8192, 4096, 4096).variant == fb.STANDARD
+    # a shape no table holds still gets a valid configuration
+    c = fb.fp8_block_gemm_select(777, 384, 1152)
+    assert fb.fp8_block_gemm_workspace_size(777, 384, 1152, c) >= 0

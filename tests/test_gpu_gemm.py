@@ -1,0 +1,202 @@
+"""GPU parity of the blockwise-scaled FP8 GEMM against the fp64 CPU oracle.
+
+Bar: |y - y_ref| <= 1e-2 |y_ref| + 1e-3 max|y_ref| for every compared output
+(max over the compared outputs of the call), for every variant; Standard,
+Split-K and Swap-AB agree bit for bit on integer-exact inputs.  GEMM inputs
+are oracle-quantized bytes, so quantization error is not part of the check.
+"""
+import numpy as np
+import pytest
+
+import fp8_blockwise_quantized_token_amd as fb
+import oracle
+from fp8_blockwise_quantized_token_amd import synth
+
+from gpu_common import assert_close, dev, host, oracle_weight, sample_rows, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _configs(M, N, K):
+    """Every compiled configuration valid for this shape."""
+    kb = K // 128
+    out = []
+    for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256)):
+        if N % tn:
+            continue
+        for sk in (1, 2, 3):
+            if sk <= kb:
+                out.append(fb.make_config(fb.STANDARD, tm, tn, sk))
+    for tm in (16, 32, 64):
+        if M > tm:
+            continue
+        for tn in (16, 32, 64):
+            if tn == 64 and tm == 64:
+                continue
+            for kw in (1, 2, 8):
+                for sk in (1, 2):
+                    if sk <= kb:
+                        out.append(fb.make_config(fb.SWAPAB, tm, tn, sk, kw))
+    return out
+
+
+def _run(qa, sa, qw, sw, cfg):
+    say("gemm", qa.shape, qw.shape, cfg.as_dict() if cfg is not None else "dispatch")
+    y = fb.block_gemm(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), cfg)
+    return host(y).astype(np.float64)
+
+
+def _random_operands(M, N, K, key):
+    rng = synth.generator(700, M, N, K, key)
+    qa = rng.choice(FINITE, size=(M, K)).astype(np.uint8)
+    qw = rng.choice(FINITE, size=(N, K)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-8, 4, size=(M, K // 128)) * rng.uniform(1, 2, (M, K // 128))).astype(np.float32)
+    sw = (2.0 ** rng.integers(-8, 4, size=(N // 128, K // 128)) * rng.uniform(1, 2, (N // 128, K // 128))).astype(np.float32)
+    return qa, sa, qw, sw
+
+
+SMALL = [(1, 256, 512), (5, 384, 1152), (16, 640, 384), (17, 256, 256), (33, 512, 640),
+         (64, 384, 1024), (100, 256, 512), (257, 512, 384), (300, 768, 896)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL, ids=lambda v: str(v))
+def test_every_config_against_oracle(M, N, K):
+    qa, sa, qw, sw = _random_operands(M, N, K, 1)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    for cfg in _configs(M, N, K) + [None]:
+        y = _run(qa, sa, qw, sw, cfg)
+        assert_close(y, ref, str(cfg))
+
+
+def test_identity_weight_pins_orientation():
+    M, K = 48, 512
+    rng = synth.generator(701)
+    qa = rng.choice(FINITE, size=(M, K)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-4, 4, size=(M, K // 128))).astype(np.float32)
+    qw = np.zeros((K, K), dtype=np.uint8)
+    qw[np.arange(K), np.arange(K)] = 0x38
+    sw = np.ones((K // 128, K // 128), dtype=np.float32)
+    exp = oracle.e4m3_decode(qa) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    for cfg in _configs(M, K, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        assert np.array_equal(y, exp), str(cfg)
+
+
+def test_closed_form_geometric_scales():
+    M, N, K = 20, 256, 512
+    qa = np.full((M, K), 0x38, np.uint8)
+    qw = np.full((N, K), 0x38, np.uint8)
+    sa = np.tile((2.0 ** np.arange(K // 128)).astype(np.float32), (M, 1))
+    sw = np.ones((N // 128, K // 128), np.float32)
+    for cfg in _configs(M, N, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        assert np.all(y == 1920.0), str(cfg)
+
+
+def test_integer_exact_variants_bitwise_equal():
+    ints = {0x38: 1, 0x40: 2, 0x44: 3, 0x48: 4, 0xB8: -1, 0xC0: -2, 0x00: 0, 0x50: 8}
+    codes = np.array(list(ints), dtype=np.uint8)
+    rng = synth.generator(702)
+    M, N, K = 64, 512, 1024
+    qa = rng.choice(codes, size=(M, K)).astype(np.uint8)
+    qw = rng.choice(codes, size=(N, K)).astype(np.uint8)
+    ia = np.vectorize(ints.get)(qa).astype(np.int64)
+    iw = np.vectorize(ints.get)(qw).astype(np.int64)
+    exact = (ia @ iw.T).astype(np.float64)
+    sa = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    # bf16 of an integer below 2^24 is the same for every variant
+    first = None
+    for cfg in _configs(M, N, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        assert_close(y, exact, str(cfg))
+        if first is None:
+            first = y
+        assert np.array_equal(y, first), str(cfg)
+
+
+def test_scaling_activations_by_two_doubles_output():
+    qa, sa, qw, sw = _random_operands(40, 256, 384, 3)
+    for cfg in [None, fb.make_config(fb.STANDARD, 64, 128, 2), fb.make_config(fb.SWAPAB, 64, 32, 1, 2)]:
+        y1 = _run(qa, sa, qw, sw, cfg)
+        y2 = _run(qa, sa * np.float32(2), qw, sw, cfg)
+        assert np.array_equal(y2, 2 * y1)
+
+
+def _full_cases():
+    out = list(synth.cases("single")) + list(synth.cases("decode_8b")) + \
+        list(synth.cases("prefill_8b")) + list(synth.cases("ue8m0_32b"))
+    for c in synth.cases("sweep"):
+        if c.M in (1, 64, 2048) or (c.M == 16384 and c.K == 25600) or (c.M == 16384 and c.N == 12288):
+            out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("case", _full_cases(), ids=lambda c: c.cid)
+def test_full_size_linear(case):
+    """The whole layer at full size in the dispatched configuration: GPU
+    activation quantization must equal the oracle's bytes; the GEMM is
+    compared with the oracle on sampled rows (every N tile and K block)."""
+    import torch
+    x = synth.activations_bf16(case)
+    qa_ref, sa_ref = oracle.group_quant(x, ue8m0=case.ue8m0)
+    qw, sw = oracle_weight(case.N, case.K, case.ue8m0)
+    say("full", case.cid, fb.fp8_block_gemm_select(case.M, case.N, case.K).as_dict())
+    xd = to_dev_bf16(x)
+    qa, sa = fb.quantize_activations(xd, ue8m0=case.ue8m0)
+    y = fb.block_gemm(qa, sa, to_dev(qw), to_dev(sw))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sa), sa_ref) and np.array_equal(host(qa), qa_ref), "activation quant differs"
+    rows = sample_rows(case.M, 8 if case.N * case.K > 1e8 else 16)
+    ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw, rows=rows)
+    yh = host(y)[rows].astype(np.float64)
+    assert_close(yh, ref, case.cid)
+
+
+@pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 12288)])
+def test_decode_variants_agree(N, K):
+    case = synth.Case("decode_8b", "x", 64, N, K, "normal_outlier", False, 0)
+    x = synth.activations_bf16(case)
+    qa, sa = oracle.group_quant(x)
+    qw, sw = oracle_weight(N, K, False)
+    cfgs = [fb.make_config(fb.STANDARD, 64, 128, 1), fb.make_config(fb.STANDARD, 64, 128, 8),
+            fb.make_config(fb.SWAPAB, 64, 16, 1, 8), fb.make_config(fb.SWAPAB, 64, 32, 4, 4),
+            fb.make_config(fb.SWAPAB, 64, 16, 16, 1)]
+    ys = [_run(qa, sa, qw, sw, c) for c in cfgs]
+    for c, y in zip(cfgs[1:], ys[1:]):
+        assert_close(y, ys[0], f"{c} vs standard")
+    ref = oracle.block_gemm(qa, sa, qw, sw, rows=np.array([0, 31, 63]))
+    assert_close(ys[0][[0, 31, 63]], ref, "standard vs oracle")
+
+
+def test_hip_graph_replay_matches_eager():
+    import torch
+    case = synth.Case("decode_8b", "x", 32, 4096, 4096, "normal_outlier", False, 0)
+    x = to_dev_bf16(synth.activations_bf16(case))
+    qw, sw = oracle_weight(4096, 4096, False)
+    qw, sw = to_dev(qw), to_dev(sw)
+    cfg = fb.make_config(fb.SWAPAB, 32, 16, 4, 4)  # split-K: two kernels and a workspace
+    qa = torch.empty((32, 4096), dtype=torch.uint8, device=dev())
+    sa = torch.empty((32, 32), dtype=torch.float32, device=dev())
+    y = torch.empty((32, 4096), dtype=torch.bfloat16, device=dev())
+    ws = fb.workspace_for(32, 4096, 4096, cfg, dev())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fb.fp8_group_quant(x, qa, sa, stream=s)
+        fb.fp8_block_gemm(qa, sa, qw, sw, y, cfg, ws, stream=s)
+    s.synchronize()
+    eager = host(y).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fb.fp8_group_quant(x, qa, sa, stream=s)
+        fb.fp8_block_gemm(qa, sa, qw, sw, y, cfg, ws, stream=s)
+    for i in range(4):
+        y.zero_()
+        qa.zero_()
+        torch.cuda.synchronize()
+        say("graph replay", i)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), eager), f"replay {i}"
