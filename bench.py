@@ -1,0 +1,333 @@
+"""Benchmark of the FP8 blockwise-quantized linear layer on one MI355X.
+
+A step is one pass of the whole hot path over every case of the workload:
+for each (M, N, K) case, per-token 1x128 activation quantization of X
+(bf16 -> e4m3fn + fp32 scales) followed by the blockwise-scaled FP8 GEMM in
+the dispatched variant (Standard / Split-K / Swap-AB), bf16 out.  Weights are
+quantized once on the GPU before timing.  Inputs are seeded synthetic tensors
+resident in HBM before the timed region starts.
+
+Default workload "qwen3_8b": the Qwen3-8B-shaped layers (qkv, o_proj,
+gate_up, down) at M in {1, 8, 32, 64} (decode) and M = 8192 (prefill), the
+M = 1..8192 range the metric is quoted on.  The step is captured once into a
+HIP graph and replayed (the pages run these kernels under graph replay), and
+the weights rotate over three copies so that no case re-reads a weight from
+the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = GEMM TFLOP/s of the whole step (all GEMM
+flops / step time, quantization time included).  Also reported: per-case
+times, quant GB/s, the dominant kernel's roofline, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+WEIGHT_COPIES = 3
+
+
+def workload_cases(name: str):
+    from fp8_blockwise_quantized_token_amd import synth
+    if name == "qwen3_8b":
+        dec = synth.cases("decode_8b")
+        pre = synth.cases("prefill_8b")
+        out = []
+        for M in (1, 8, 32, 64):
+            out += [c for c in dec if c.M == M]
+        return out + pre
+    if name in ("single", "decode_8b", "prefill_8b", "ue8m0_32b", "sweep"):
+        return synth.cases(name)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def gemm_bytes(c) -> int:
+    M, N, K = c.M, c.N, c.K
+    return M * K + 4 * M * K // 128 + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N
+
+
+def quant_bytes(c) -> int:
+    return 2 * c.M * c.K + c.M * c.K + 4 * c.M * c.K // 128
+
+
+def kernel_symbol(cfg) -> str:
+    """Name fragment of the GEMM kernel a configuration launches."""
+    if cfg.variant == 0:
+        wm = {64: 32, 128: 64, 256: 64}[cfg.tile_m]
+        return f"k_gemm_std<{cfg.tile_m},{cfg.tile_n},{wm},64,{'true' if cfg.split_k > 1 else 'false'}>"
+    return (f"k_gemm_swapab<{cfg.tile_m // 16},{cfg.tile_n // 16},"
+            f"{'true' if cfg.split_k > 1 else 'false'}>")
+
+
+def source_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp8_blockwise_quantized_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(symbol: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on this exact kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != src_hash:
+        return None
+    ent = data.get("kernels", {}).get(symbol)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cases, budget_s: float):
+    """The oracle (untuned) on a bounded sample: every case's GEMM on its first
+    rows, doubling the rows until about budget_s of work has been timed."""
+    import numpy as np
+    import oracle
+    from fp8_blockwise_quantized_token_amd import synth
+
+    threads = oracle.default_threads()
+    prepared = []
+    wcache = {}
+    for c in cases:
+        x = synth.activations_bf16(c)
+        rows = min(c.M, 64)
+        xs = np.ascontiguousarray(x[:rows])
+        key = (c.N, c.K, c.ue8m0)
+        if key not in wcache:
+            wcache[key] = oracle.weight_block_quant(synth.weights_f32(c.N, c.K), ue8m0=c.ue8m0,
+                                                    nthreads=threads)
+        qw, sw = wcache[key]
+        prepared.append((c, xs, qw, sw))
+    flops = 0.0
+    t_total = 0.0
+    rows_used = 0
+    nrows = 1
+    while True:
+        t0 = time.perf_counter()
+        f = 0.0
+        r_used = 0
+        for c, xs, qw, sw in prepared:
+            r = min(nrows, xs.shape[0])
+            qa, sa = oracle.group_quant(xs[:r], ue8m0=c.ue8m0, nthreads=threads)
+            oracle.block_gemm(qa, sa, qw, sw, nthreads=threads)
+            f += 2.0 * r * c.N * c.K
+            r_used += r
+        dt = time.perf_counter() - t0
+        flops, t_total, rows_used = f, dt, r_used
+        if dt > budget_s / 3 or nrows >= 64:
+            break
+        nrows *= 2
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nrows} row(s) of each of the {len(cases)} cases ({rows_used} rows, "
+                      f"{flops / 1e9:.1f} GFLOP incl. their activation quantization), "
+                      f"{t_total:.1f} s on {threads} host threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU path is "
+              "design-only in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import numpy as np
+    import fp8_blockwise_quantized_token_amd as fb
+    from fp8_blockwise_quantized_token_amd import synth
+
+    fb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    cases = workload_cases(args.workload)
+    print(f"[bench] workload {args.workload}: {len(cases)} cases", file=sys.stderr, flush=True)
+
+    # weights: quantized on the GPU, WEIGHT_COPIES buffers per shape
+    wq = {}
+    with torch.cuda.stream(stream):
+        for c in cases:
+            key = (c.N, c.K, c.ue8m0)
+            if key in wq:
+                continue
+            w = torch.from_numpy(synth.weights_f32(c.N, c.K)).to(dev)
+            copies = []
+            for _ in range(WEIGHT_COPIES):
+                q = torch.empty((c.N, c.K), dtype=torch.uint8, device=dev)
+                s = torch.empty((c.N // 128, c.K // 128), dtype=torch.float32, device=dev)
+                fb.fp8_weight_block_quant(w, q, s, ue8m0=c.ue8m0, stream=stream)
+                copies.append((q, s))
+            wq[key] = copies
+            del w
+    stream.synchronize()
+
+    # per-case buffers
+    bufs = []
+    for i, c in enumerate(cases):
+        x = torch.from_numpy(synth.activations_bf16(c).view(np.int16)).to(dev).view(torch.bfloat16)
+        qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K)
+        ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
+        qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
+        bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, qw=qw, sw=sw))
+    torch.cuda.synchronize()
+
+    def step():
+        for b in bufs:
+            c = b["case"]
+            fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream)
+            fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    stream.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        graph.replay()
+        stream.synchronize()
+
+    # ---- timed region: K steps ----
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    total_flops = sum(b["case"].flops() for b in bufs)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-kernel durations (HIP events on the launch stream) ----
+    reps = args.kernel_reps
+    per_case = []
+    sym_time = {}
+    sym_work = {}
+    for b in bufs:
+        c = b["case"]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        with torch.cuda.stream(stream):
+            e[0].record(stream)
+            for _ in range(reps):
+                fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream)
+            e[1].record(stream)
+            e[2].record(stream)
+            for _ in range(reps):
+                fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+            e[3].record(stream)
+        stream.synchronize()
+        tq = e[0].elapsed_time(e[1]) / reps * 1e-3
+        tg = e[2].elapsed_time(e[3]) / reps * 1e-3
+        fl = c.flops()
+        gb = gemm_bytes(c)
+        frac = max(fl / (PEAK_FP8_TFLOPS * 1e12), gb / (PEAK_HBM_GBPS * 1e9)) / tg
+        sym = kernel_symbol(b["cfg"])
+        sym_time[sym] = sym_time.get(sym, 0.0) + tg
+        sym_work.setdefault(sym, [0.0, 0.0, 0])
+        sym_work[sym][0] += fl
+        sym_work[sym][1] += gb
+        sym_work[sym][2] += 1
+        per_case.append({
+            "case": c.cid, "cfg": b["cfg"].as_dict(), "kernel": sym,
+            "gemm_us": round(tg * 1e6, 2), "quant_us": round(tq * 1e6, 2),
+            "gemm_tflops": round(fl / tg / 1e12, 2), "gemm_gbps": round(gb / tg / 1e9, 1),
+            "gemm_roofline_frac": round(frac, 4),
+            "quant_gbps": round(quant_bytes(c) / tq / 1e9, 1),
+        })
+
+    dom = max(sym_time, key=sym_time.get)
+    dflops, dbytes, dlaunches = sym_work[dom]
+    avg_t = sym_time[dom] / dlaunches
+    flop_per_launch = dflops / dlaunches
+    byte_per_launch = dbytes / dlaunches
+    mfma_bound = flop_per_launch / (PEAK_FP8_TFLOPS * 1e12) >= byte_per_launch / (PEAK_HBM_GBPS * 1e9)
+    src_hash = source_hash("gemm.hip", "device_common.hpp")
+    traffic = traffic_from_profiles(dom, src_hash)
+    if mfma_bound:
+        ach = flop_per_launch / avg_t / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+    else:
+        ach = byte_per_launch / avg_t / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic}
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(avg_t * 1e6, 2)
+    roof["launches_measured"] = dlaunches * reps
+
+    qb = sum(quant_bytes(b["case"]) for b in bufs)
+    qt = sum(p["quant_us"] for p in per_case) * 1e-6
+    decode = [p for p, b in zip(per_case, bufs) if b["case"].M <= 64]
+    dec_bytes = sum(gemm_bytes(b["case"]) for b in bufs if b["case"].M <= 64)
+    dec_t = sum(p["gemm_us"] for p in decode) * 1e-6
+
+    out = {
+        "metric": "FP8 block GEMM TFLOP/s + quant GB/s at M=1..8192, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-in/fp32-acc/bf16-out",
+        "data": "synthetic (seeded; Qwen3-shaped layers, random weights N(0,0.02))",
+        "config": {"workload": args.workload, "cases": len(cases),
+                   "m_values": sorted({b["case"].M for b in bufs}),
+                   "nk": sorted({(b["case"].N, b["case"].K) for b in bufs}),
+                   "graph_replay": graph is not None, "weight_copies": WEIGHT_COPIES},
+        "quant_gbps": round(qb / qt / 1e9, 1) if qt > 0 else None,
+        "decode_gemm_gbps": round(dec_bytes / dec_t / 1e9, 1) if dec_t > 0 else None,
+        "roofline": roof,
+        "cases": per_case,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

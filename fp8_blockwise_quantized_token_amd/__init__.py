@@ -103,8 +103,12 @@ def _stream(stream) -> int | None:
 
 
 def _ld(t, what: str) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    """Row pitch in elements.  A single-row tensor may carry any stride for
+    its row dimension (0 included); its pitch is then its row length."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError(f"{what}: expected a 2-D tensor with unit column stride")
+    if t.shape[0] <= 1:
+        return max(t.stride(0), t.shape[1])
     return t.stride(0)
 
 
