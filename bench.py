@@ -62,8 +62,8 @@ def quant_bytes(c) -> int:
 def kernel_symbol(cfg) -> str:
     """Name fragment of the GEMM kernel a configuration launches."""
     if cfg.variant == 0:
-        wm = {64: 32, 128: 64, 256: 64}[cfg.tile_m]
-        return f"k_gemm_std<{cfg.tile_m},{cfg.tile_n},{wm},64,{'true' if cfg.split_k > 1 else 'false'}>"
+        wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
+        return f"k_gemm_lds<{cfg.tile_m},{cfg.tile_n},{wm},64,{'true' if cfg.split_k > 1 else 'false'}>"
     return (f"k_gemm_swapab<{cfg.tile_m // 16},{cfg.tile_n // 16},"
             f"{'true' if cfg.split_k > 1 else 'false'}>")
 

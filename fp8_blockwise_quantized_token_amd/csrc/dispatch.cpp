@@ -48,9 +48,13 @@ void heuristic(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* c) {
     return;
   }
   c->variant = FP8BLK_STANDARD;
+  const int64_t t256x256 = (N % 256 == 0) ? cdiv(M, 256) * (N / 256) : 0;
   const int64_t t256 = cdiv(M, 256) * (N / 128);
   const int64_t t128 = cdiv(M, 128) * (N / 128);
-  if (t256 >= kCUs) {
+  if (t256x256 >= kCUs) {
+    c->tile_m = 256;
+    c->tile_n = 256;
+  } else if (t256 >= kCUs) {
     c->tile_m = 256;
     c->tile_n = 128;
   } else if (t128 >= kCUs) {

@@ -1,4 +1,6 @@
-// gemm.hip -- blockwise-scaled FP8 GEMM for gfx950 (scaled_mm_blockwise).
+// gemm.hip -- Swap-AB variant and the Split-K reduction of the
+// blockwise-scaled FP8 GEMM for gfx950 (scaled_mm_blockwise); the Standard
+// variant is in gemm_standard.hip.
 //
 //   y[m][n] = bf16( sum_kb sa[m][kb] * sw[n/128][kb] * P_kb[m][n] ),
 //   P_kb = sum over the 128 K of block kb of a[m][k] * w[n][k]   (fp8 x fp8 -> fp32)
@@ -22,178 +24,6 @@
 
 namespace fp8blk {
 namespace {
-
-// ---------------------------------------------------------------------------
-// Standard variant
-// ---------------------------------------------------------------------------
-// A workgroup computes a BM x BN tile of y over its range of K blocks.  Per
-// K block it stages a[BM][128] and w[BN][128] (fp8) plus sa[BM][kb] in LDS,
-// double-buffered: the global loads of block kb+1 are in flight while the
-// matrix cores work on block kb.  LDS rows are 128 bytes; 16-byte chunk c of
-// row r lives at chunk c ^ (r & 7) so that the ds_read_b128 of a fragment
-// (16 rows, same chunk) touch distinct banks.  Waves tile the block as
-// (BM/WM) x (BN/WN); a wave's WM x WN tile is (WM/16) x (WN/16) 16x16
-// matrix-core tiles.
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
-
-__device__ __forceinline__ u32x4 lds_load16(const uint8_t* p) { return *(const u32x4*)p; }
-
-template <int N>
-__device__ __forceinline__ void gload_rows(u32x4 (&r)[N], const uint8_t* const (&src)[N], int kb) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) r[i] = *(const u32x4*)(src[i] + (int64_t)kb * 128);
-}
-
-template <int N>
-__device__ __forceinline__ void lstore_rows(uint8_t* lds, const u32x4 (&r)[N], const int (&dst)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) *(u32x4*)(lds + dst[i]) = r[i];
-}
-
-struct StdParams {
-  GemmArgs g;
-  int tiles_m, tiles_n;
-  int kb_total, kb_per_split;
-};
-
-template <int BM, int BN, int WM, int WN>
-struct StdShape {
-  static constexpr int WAVES_M = BM / WM;
-  static constexpr int WAVES_N = BN / WN;
-  static constexpr int NT = WAVES_M * WAVES_N * 64;
-  static constexpr int TM = WM / 16;
-  static constexpr int TN = WN / 16;
-  static constexpr int A_CHUNKS = BM * 8 / NT;
-  static constexpr int B_CHUNKS = BN * 8 / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile not divisible by threads");
-  static_assert(128 % WN == 0, "a wave's N range must sit inside one 128-row weight block");
-  static_assert(BM <= NT, "one thread per row loads the activation scales");
-};
-
-template <int BM, int BN, int WM, int WN, bool SPLIT>
-__global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_std(StdParams p) {
-  using S = StdShape<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * 128];
-  __shared__ float lds_sa[2][BM];
-
-  const GemmArgs& g = p.g;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wave_m = wave % S::WAVES_M;
-  const int wave_n = wave / S::WAVES_M;
-
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int split = blockIdx.x / tiles;
-  const int t = blockIdx.x - split * tiles;
-  const int tm = t % p.tiles_m;
-  const int tn = t / p.tiles_m;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
-  const int kb0 = split * p.kb_per_split;
-  const int kb1 = min(kb0 + p.kb_per_split, p.kb_total);
-  const int64_t mlast = g.M - 1;
-
-  // global -> LDS assignment (rows past M re-read row M-1; never stored)
-  const uint8_t* a_src[S::A_CHUNKS];
-  int a_dst[S::A_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < S::A_CHUNKS; ++i) {
-    const int c = tid + i * S::NT;
-    const int row = c >> 3, ch = c & 7;
-    const int64_t m = min(m0 + row, mlast);
-    a_src[i] = g.a + m * g.lda + ch * 16;
-    a_dst[i] = swz(row, ch);
-  }
-  const uint8_t* b_src[S::B_CHUNKS];
-  int b_dst[S::B_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < S::B_CHUNKS; ++i) {
-    const int c = tid + i * S::NT;
-    const int row = c >> 3, ch = c & 7;
-    b_src[i] = g.w + (n0 + row) * g.ldw + ch * 16;
-    b_dst[i] = swz(row, ch);
-  }
-  const float* sa_src = g.sa + min(m0 + (tid < BM ? tid : 0), mlast) * g.ldsa;
-  const float* sw_src = g.sw + ((n0 + wave_n * WN) >> 7) * g.ldsw;
-
-  u32x4 ra[S::A_CHUNKS], rb[S::B_CHUNKS];
-  float rsa = 0.f;
-  v4f acc[S::TM][S::TN];
-#pragma unroll
-  for (int i = 0; i < S::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int frow = lane & 15;
-  const int fch = (lane >> 4) * 2;
-  const int orow = (lane >> 4) * 4;
-
-  if (kb0 < kb1) {
-    gload_rows(ra, a_src, kb0);
-    gload_rows(rb, b_src, kb0);
-    if (tid < BM) rsa = sa_src[kb0];
-    lstore_rows(&lds_a[0][0], ra, a_dst);
-    lstore_rows(&lds_b[0][0], rb, b_dst);
-    if (tid < BM) lds_sa[0][tid] = rsa;
-  }
-  __syncthreads();
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int buf = (kb - kb0) & 1;
-    if (kb + 1 < kb1) {
-      gload_rows(ra, a_src, kb + 1);
-      gload_rows(rb, b_src, kb + 1);
-      if (tid < BM) rsa = sa_src[kb + 1];
-    }
-    const float swv = sw_src[kb];
-    v8i bf[S::TN];
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const int r = wave_n * WN + j * 16 + frow;
-      bf[j] = make_v8i(lds_load16(&lds_b[buf][swz(r, fch)]), lds_load16(&lds_b[buf][swz(r, fch + 1)]));
-    }
-#pragma unroll
-    for (int i = 0; i < S::TM; ++i) {
-      const int r = wave_m * WM + i * 16 + frow;
-      const v8i af = make_v8i(lds_load16(&lds_a[buf][swz(r, fch)]), lds_load16(&lds_a[buf][swz(r, fch + 1)]));
-      float gsc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) gsc[q] = lds_sa[buf][wave_m * WM + i * 16 + orow + q] * swv;
-#pragma unroll
-      for (int j = 0; j < S::TN; ++j) {
-        const v4f P = mfma16x16x128(af, bf[j]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(P[q], gsc[q], acc[i][j][q]);
-      }
-    }
-    if (kb + 1 < kb1) {
-      lstore_rows(&lds_a[buf ^ 1][0], ra, a_dst);
-      lstore_rows(&lds_b[buf ^ 1][0], rb, b_dst);
-      if (tid < BM) lds_sa[buf ^ 1][tid] = rsa;
-    }
-    __syncthreads();
-  }
-
-  // epilogue: lane holds rows orow..orow+3, column frow of every 16x16 tile
-#pragma unroll
-  for (int i = 0; i < S::TM; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t m = m0 + wave_m * WM + i * 16 + orow + q;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < S::TN; ++j) {
-        const int64_t n = n0 + wave_n * WN + j * 16 + frow;
-        if (SPLIT)
-          g.ws[((int64_t)split * g.M + m) * g.N + n] = acc[i][j][q];
-        else
-          g.y[m * g.ldy + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Swap-AB variant (small M)
@@ -361,23 +191,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t run_std(const GemmArgs& g, int split_k, hipStream_t stream) {
-  using S = StdShape<BM, BN, WM, WN>;
-  StdParams p;
-  p.g = g;
-  p.tiles_m = (int)((g.M + BM - 1) / BM);
-  p.tiles_n = (int)(g.N / BN);
-  p.kb_total = (int)(g.K / 128);
-  p.kb_per_split = (p.kb_total + split_k - 1) / split_k;
-  const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * split_k;
-  if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_std<BM, BN, WM, WN, true>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_gemm_std<BM, BN, WM, WN, false>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
-  return hipGetLastError();
-}
-
 template <int TOKT, int RN>
 hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stream) {
   SwapParams p;
@@ -393,26 +206,6 @@ hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stre
 }
 
 }  // namespace
-
-bool standard_tile_supported(int tile_m, int tile_n) {
-  return (tile_m == 64 && tile_n == 128) || (tile_m == 128 && tile_n == 128) ||
-         (tile_m == 256 && tile_n == 128) || (tile_m == 128 && tile_n == 256);
-}
-
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k,
-                                hipStream_t stream) {
-  hipError_t e = hipErrorInvalidValue;
-  if (tile_m == 64 && tile_n == 128)
-    e = run_std<64, 128, 32, 64>(g, split_k, stream);
-  else if (tile_m == 128 && tile_n == 128)
-    e = run_std<128, 128, 64, 64>(g, split_k, stream);
-  else if (tile_m == 256 && tile_n == 128)
-    e = run_std<256, 128, 64, 64>(g, split_k, stream);
-  else if (tile_m == 128 && tile_n == 256)
-    e = run_std<128, 256, 64, 64>(g, split_k, stream);
-  if (e != hipSuccess || split_k == 1) return e;
-  return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
-}
 
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves) {
   const bool tm = tile_m == 16 || tile_m == 32 || tile_m == 64;

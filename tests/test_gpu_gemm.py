@@ -23,7 +23,7 @@ def _configs(M, N, K):
     """Every compiled configuration valid for this shape."""
     kb = K // 128
     out = []
-    for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256)):
+    for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
         if N % tn:
             continue
         for sk in (1, 2, 3):
