@@ -13,12 +13,13 @@
 //     data never passes through VGPRs).  Two LDS stages: the loads of block
 //     kb+1 are in flight while the matrix cores work on block kb.
 //   * LDS rows are 128 bytes = eight 16-byte chunks; chunk c of row r is
-//     stored at c ^ g(r), g(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), so the
-//     ds_read_b128 of a fragment (16 consecutive rows, one chunk) hit 16
-//     distinct 16-byte bank groups of a 256-byte window (and 8 distinct ones
-//     of any 128-byte window).  One direct-to-LDS instruction fills 8 rows
-//     (1 KiB, lane L at offset 16 L); lane L therefore fetches chunk
-//     (L & 7) ^ g(row) of its row.
+//     stored at c ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read
+//     (ds_read_b128; lane l: row l & 15, chunk 2 (l >> 4) [+1]) then puts
+//     lanes 0-31 and lanes 32-63 each on 32 distinct 16-byte slots modulo
+//     512 bytes, which is what gfx950's LDS needs to serve the read without
+//     bank conflicts (measured: 231 B/clk vs 126 B/clk for an XOR with
+//     r & 7 alone).  One direct-to-LDS instruction fills 8 rows (1 KiB, lane
+//     L at offset 16 L); lane L therefore fetches chunk (L & 7) ^ g(row).
 //   * One v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile and K block gives the
 //     complete block partial P_kb; it is folded into the fp32 accumulator
 //     with one FMA by sa[m][kb] * sw[nb][kb] (a wave's N range lies inside one
@@ -38,7 +39,7 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz_g(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+__device__ __forceinline__ int swz_g(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz_off(int row, int chunk) { return row * 128 + ((chunk ^ swz_g(row)) << 4); }
 
 struct StdParams {
@@ -105,41 +106,50 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const int kb1 = min(kb0 + p.kb_per_split, p.kb_total);
   const int64_t mlast = g.M - 1;
 
-  // ---- direct-to-LDS source addresses (per lane) ----
+  // ---- direct-to-LDS sources: wave-uniform tile bases + 32-bit lane offsets
+  // (row pitches are below 2^24, so every offset inside a tile fits) ----
   // instruction i of this wave fills rows 8 * (wave + i * WAVES) .. +7
   const int lrow = lane >> 3;
   const int lch = lane & 7;
-  const uint8_t* a_src[S::A_INSTR];
+  const int rows_valid = (int)min((int64_t)BM, g.M - m0);  // rows past M re-read the last row
+  const uint8_t* a_base = g.a + m0 * g.lda;
+  const uint8_t* b_base = g.w + n0 * g.ldw;
+  uint32_t a_off[S::A_INSTR];
 #pragma unroll
   for (int i = 0; i < S::A_INSTR; ++i) {
     const int row = 8 * (wave + i * S::WAVES) + lrow;
-    const int64_t m = min(m0 + row, mlast);
-    a_src[i] = g.a + m * g.lda + ((lch ^ swz_g(row)) << 4);
+    a_off[i] = (uint32_t)min(row, rows_valid - 1) * (uint32_t)g.lda + ((lch ^ swz_g(row)) << 4);
   }
-  const uint8_t* b_src[S::B_INSTR];
+  uint32_t b_off[S::B_INSTR];
 #pragma unroll
   for (int i = 0; i < S::B_INSTR; ++i) {
     const int row = 8 * (wave + i * S::WAVES) + lrow;
-    b_src[i] = g.w + (n0 + row) * g.ldw + ((lch ^ swz_g(row)) << 4);
+    b_off[i] = (uint32_t)row * (uint32_t)g.ldw + ((lch ^ swz_g(row)) << 4);
   }
-  const float* sa_src = g.sa + min(m0 + (wave * 64 + lane) % BM, mlast) * g.ldsa;
-  const float* sw_src = g.sw + ((n0 >> 7) + min(lane, BN / 128 - 1)) * g.ldsw;
+  const float* sa_base = g.sa + m0 * g.ldsa;
+  const uint32_t sa_off = (uint32_t)min((wave * 64 + lane) % BM, rows_valid - 1) * (uint32_t)g.ldsa;
+  const float* sw_base = g.sw + (n0 >> 7) * g.ldsw;
+  const uint32_t sw_off = (uint32_t)min(lane, BN / 128 - 1) * (uint32_t)g.ldsw;
   const int sw_slot = BM + ((wave_n * WN) >> 7);  // this wave's weight scale in the stage buffer
+  const bool sa_wave = wave < S::SA_INSTR;
+  const float* sc_base = sa_wave ? sa_base : sw_base;
+  const uint32_t sc_off = sa_wave ? sa_off : sw_off;
+  const int sc_dst = sa_wave ? wave * 64 : BM;
 
   auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) {
-    const int64_t ko = (int64_t)kb * 128;
+    const uint8_t* ab = a_base + (int64_t)kb * 128;
+    const uint8_t* bb = b_base + (int64_t)kb * 128;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ko),
+      __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[i]),
                                        (lds_void*)(la + (wave + i * S::WAVES) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + ko),
+      __builtin_amdgcn_global_load_lds((const void*)(bb + b_off[i]),
                                        (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16, 0, 0);
-    if (wave < S::SA_INSTR)
-      __builtin_amdgcn_global_load_lds((const void*)(sa_src + kb), (lds_void*)(ls + wave * 64), 4, 0, 0);
-    else if (wave == S::SW_WAVE)
-      __builtin_amdgcn_global_load_lds((const void*)(sw_src + kb), (lds_void*)(ls + BM), 4, 0, 0);
+    // one 4-byte scale load per wave: waves < SA_INSTR load activation
+    // scales, the others the weight scales (the same values, harmless)
+    __builtin_amdgcn_global_load_lds((const void*)(sc_base + kb + sc_off), (lds_void*)(ls + sc_dst), 4, 0, 0);
   };
 
   v4f acc[S::TM][S::TN];
@@ -152,6 +162,13 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const int fch = (lane >> 4) * 2;
   const int orow = (lane >> 4) * 4;
 
+  // One K block, software-pipelined over the wave's 16-row tile rows i:
+  // while the matrix cores compute the TN products of row i, the VALU folds
+  // the products of row i-1 into their accumulators (one FMA per element,
+  // factor sa[m][kb] * sw[nb][kb]) and the A fragment and activation scales
+  // of row i+1 are read from LDS.  The products of two rows are live at a
+  // time; the order (the next row's LDS reads, then 1 MFMA : 4 FMA) is
+  // requested from the scheduler per step.
   auto compute = [&](const uint8_t* la, const uint8_t* lb, const float* ls) {
     const float swv = ls[sw_slot];
     v8i bf[S::TN];
@@ -160,36 +177,68 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       const int r = wave_n * WN + j * 16 + frow;
       bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
     }
+    const int arow = wave_m * WM + frow;
+    const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
+    const float* srow = ls + wave_m * WM + orow;                         // + 16 per tile row
+    v8i af[2];
+    v4f scl;     // scales of the row read last
+    v4f gq[2];   // factors sa * sw of rows i and i-1
+    af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
+    scl = *(const v4f*)srow;
+    v4f P[2][S::TN];
 #pragma unroll
-    for (int i = 0; i < S::TM; ++i) {
-      const int r = wave_m * WM + i * 16 + frow;
-      const v8i af = make_v8i(*(const u32x4*)(la + swz_off(r, fch)), *(const u32x4*)(la + swz_off(r, fch + 1)));
-      const v4f sa4 = *(const v4f*)(ls + wave_m * WM + i * 16 + orow);
-      const float g0 = sa4[0] * swv, g1 = sa4[1] * swv, g2 = sa4[2] * swv, g3 = sa4[3] * swv;
+    for (int i = 0; i <= S::TM; ++i) {
+      const int cur = i & 1, prv = cur ^ 1;
+      if (i < S::TM) gq[cur] = scl * swv;  // row i's scales were read one step ago
+      __builtin_amdgcn_sched_barrier(0);    // ...and are consumed before row i+1's are read
+      if (i + 1 < S::TM) {
+        af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
+                           *(const u32x4*)(la + a_hi + (i + 1) * 2048));
+        scl = *(const v4f*)(srow + (i + 1) * 16);
+      }
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
-        const v4f P = mfma16x16x128(af, bf[j]);
-        acc[i][j][0] = __builtin_fmaf(P[0], g0, acc[i][j][0]);
-        acc[i][j][1] = __builtin_fmaf(P[1], g1, acc[i][j][1]);
-        acc[i][j][2] = __builtin_fmaf(P[2], g2, acc[i][j][2]);
-        acc[i][j][3] = __builtin_fmaf(P[3], g3, acc[i][j][3]);
+        if (i < S::TM) P[cur][j] = mfma16x16x128(af[cur], bf[j]);
+        if (i > 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i - 1][j][q] = __builtin_fmaf(P[prv][j][q], gq[prv][q], acc[i - 1][j][q]);
+        }
       }
+      if (i > 0 && i < S::TM) {
+        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next row's LDS reads first
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // Main loop, two K blocks per trip so that every LDS buffer is a static
+  // object (the compiler then knows the stage being read and the stage being
+  // filled never alias and inserts no early wait).  Inside a trip there is no
+  // branch: the next stage is always issued, with the
+  // block index clamped to the last one (re-loading it into the idle buffer
+  // is harmless).  An odd block count leaves one block for after the loop.
   if (kb0 < kb1) issue(lds_a0, lds_b0, lds_s0, kb0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed
   __syncthreads();
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const bool odd = ((kb - kb0) & 1) != 0;
-    uint8_t* ca = odd ? lds_a1 : lds_a0;
-    uint8_t* cb = odd ? lds_b1 : lds_b0;
-    float* cs = odd ? lds_s1 : lds_s0;
-    if (kb + 1 < kb1) issue(odd ? lds_a0 : lds_a1, odd ? lds_b0 : lds_b1, odd ? lds_s0 : lds_s1, kb + 1);
-    compute(ca, cb, cs);
+  int kb = kb0;
+  for (; kb + 1 < kb1; kb += 2) {
+    issue(lds_a1, lds_b1, lds_s1, kb + 1);
+    compute(lds_a0, lds_b0, lds_s0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's next stage has landed
+    __syncthreads();
+    issue(lds_a0, lds_b0, lds_s0, min(kb + 2, kb1 - 1));
+    compute(lds_a1, lds_b1, lds_s1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+  if (kb < kb1) compute(lds_a0, lds_b0, lds_s0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: lane holds rows orow..orow+3 and column frow of each tile ----
 #pragma unroll
