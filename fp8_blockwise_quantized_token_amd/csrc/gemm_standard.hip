@@ -162,50 +162,64 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const int fch = (lane >> 4) * 2;
   const int orow = (lane >> 4) * 4;
 
-  // One K block, software-pipelined over the wave's 16-row tile rows i:
+  // Per K block, software-pipelined over the wave's 16-row tile rows i:
   // while the matrix cores compute the TN products of row i, the VALU folds
   // the products of row i-1 into their accumulators (one FMA per element,
   // factor sa[m][kb] * sw[nb][kb]) and the A fragment and activation scales
   // of row i+1 are read from LDS.  The products of two rows are live at a
   // time; the order (the next row's LDS reads, then 1 MFMA : 4 FMA) is
-  // requested from the scheduler per step.
-  auto compute = [&](const uint8_t* la, const uint8_t* lb, const float* ls) {
-    const float swv = ls[sw_slot];
-    v8i bf[S::TN];
+  // requested from the scheduler per step.  The pipeline also runs across K
+  // blocks: once the last row's products are issued, the wave passes the
+  // stage barrier, refills the stage it has finished with (block kb+2),
+  // reads the next block's B fragments, first A fragment and scales, and
+  // folds the last row's products while those reads are in flight.
+  static_assert(S::TM % 2 == 0, "row pipeline assumes an even number of tile rows");
+  const int arow = wave_m * WM + frow;
+  const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
+  const int srow = wave_m * WM + orow;                                 // + 16 per tile row
+  v8i bf[S::TN];
+  v8i af[2];
+  v4f scl;      // scales of the row read last
+  v4f gq[2];    // factors sa * sw of the rows in flight
+  v4f P[2][S::TN];
+  float swv;
+
+  auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) {
+    swv = ls[sw_slot];
 #pragma unroll
     for (int j = 0; j < S::TN; ++j) {
       const int r = wave_n * WN + j * 16 + frow;
       bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
     }
-    const int arow = wave_m * WM + frow;
-    const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
-    const float* srow = ls + wave_m * WM + orow;                         // + 16 per tile row
-    v8i af[2];
-    v4f scl;     // scales of the row read last
-    v4f gq[2];   // factors sa * sw of rows i and i-1
     af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
-    scl = *(const v4f*)srow;
-    v4f P[2][S::TN];
+    scl = *(const v4f*)(ls + srow);
+  };
+
+  // One K block from the stage (la, ls) whose first fragments are already in
+  // registers; afterwards refill that stage (ra, rb, rs) with block kb_refill
+  // and read the first fragments of the next stage (na, nb, ns).
+  auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
+                    int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns) {
 #pragma unroll
-    for (int i = 0; i <= S::TM; ++i) {
+    for (int i = 0; i < S::TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
-      if (i < S::TM) gq[cur] = scl * swv;  // row i's scales were read one step ago
-      __builtin_amdgcn_sched_barrier(0);    // ...and are consumed before row i+1's are read
+      gq[cur] = scl * swv;                 // row i's scales were read one step ago
+      __builtin_amdgcn_sched_barrier(0);  // ...and are consumed before row i+1's are read
       if (i + 1 < S::TM) {
         af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                            *(const u32x4*)(la + a_hi + (i + 1) * 2048));
-        scl = *(const v4f*)(srow + (i + 1) * 16);
+        scl = *(const v4f*)(ls + srow + (i + 1) * 16);
       }
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
-        if (i < S::TM) P[cur][j] = mfma16x16x128(af[cur], bf[j]);
+        P[cur][j] = mfma16x16x128(af[cur], bf[j]);
         if (i > 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             acc[i - 1][j][q] = __builtin_fmaf(P[prv][j][q], gq[prv][q], acc[i - 1][j][q]);
         }
       }
-      if (i > 0 && i < S::TM) {
+      if (i > 0) {
         if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next row's LDS reads first
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
@@ -215,29 +229,40 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // this wave's loads into the next stage have landed; after the barrier
+    // every wave's have, and nobody reads the stage just consumed any more
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    issue(ra, rb, rs, kb_refill);
+    read_first(na, nb, ns);
+    constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[last][j][q] = __builtin_fmaf(P[lc][j][q], gq[lc][q], acc[last][j][q]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Main loop, two K blocks per trip so that every LDS buffer is a static
-  // object (the compiler then knows the stage being read and the stage being
-  // filled never alias and inserts no early wait).  Inside a trip there is no
-  // branch: the next stage is always issued, with the
-  // block index clamped to the last one (re-loading it into the idle buffer
-  // is harmless).  An odd block count leaves one block for after the loop.
-  if (kb0 < kb1) issue(lds_a0, lds_b0, lds_s0, kb0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed
+  // Stage 0 <- block kb0 (waited), stage 1 <- kb0+1 (in flight).  Two K
+  // blocks per trip so that every LDS buffer is a static object (the
+  // compiler then knows the stage being read and the stage being filled
+  // never alias and inserts no early wait); no branch inside a trip: block
+  // indices are clamped to the last block (re-loading it into an idle stage
+  // is harmless).  An empty K range (a trailing split) loads the last block
+  // and computes nothing.
+  const int kblast = kb1 - 1;
+  issue(lds_a0, lds_b0, lds_s0, min(kb0, kblast));
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+  issue(lds_a1, lds_b1, lds_s1, min(kb0 + 1, kblast));
+  read_first(lds_a0, lds_b0, lds_s0);
   int kb = kb0;
   for (; kb + 1 < kb1; kb += 2) {
-    issue(lds_a1, lds_b1, lds_s1, kb + 1);
-    compute(lds_a0, lds_b0, lds_s0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's next stage has landed
-    __syncthreads();
-    issue(lds_a0, lds_b0, lds_s0, min(kb + 2, kb1 - 1));
-    compute(lds_a1, lds_b1, lds_s1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    kblock(lds_a0, lds_s0, lds_a0, lds_b0, lds_s0, min(kb + 2, kblast), lds_a1, lds_b1, lds_s1);
+    kblock(lds_a1, lds_s1, lds_a1, lds_b1, lds_s1, min(kb + 3, kblast), lds_a0, lds_b0, lds_s0);
   }
-  if (kb < kb1) compute(lds_a0, lds_b0, lds_s0);
+  if (kb < kb1) kblock(lds_a0, lds_s0, lds_a0, lds_b0, lds_s0, kblast, lds_a1, lds_b1, lds_s1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: lane holds rows orow..orow+3 and column frow of each tile ----
