@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   fp8_block_gemm_select  per-shape dispatch (host only)
   fp8_block_gemm_workspace_size
   fp8_block_gemm         blockwise-scaled FP8 GEMM, bf16 out
+  fp8_linear_workspace_size
+  fp8_linear             the whole layer (quantize x, then the GEMM; fused for Swap-AB)
 """
 from __future__ import annotations
 
@@ -89,6 +91,11 @@ def lib() -> ctypes.CDLL:
     L.fp8_block_gemm.restype = ctypes.c_int
     L.fp8_block_gemm.argtypes = [P, P, I64, I64, P, P, I64, I64, P, I64, I64, I64, I64,
                                  ctypes.POINTER(GemmConfig), P, I64, P]
+    L.fp8_linear_workspace_size.restype = I64
+    L.fp8_linear_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(GemmConfig)]
+    L.fp8_linear.restype = ctypes.c_int
+    L.fp8_linear.argtypes = [P, I64, P, P, I64, I64, P, I64, I64, I64, I64, F, U32,
+                             ctypes.POINTER(GemmConfig), P, I64, P]
     _lib = L
     return L
 
@@ -185,6 +192,30 @@ def fp8_block_gemm(a, sa, w, sw, y, cfg: GemmConfig | None = None, workspace=Non
     _check(st, "fp8_block_gemm")
 
 
+def fp8_linear_workspace_size(M: int, N: int, K: int, cfg: GemmConfig | None = None) -> int:
+    n = lib().fp8_linear_workspace_size(M, N, K, ctypes.byref(cfg) if cfg is not None else None)
+    if n < 0:
+        raise Fp8BlkError(int(n), "fp8_linear_workspace_size")
+    return int(n)
+
+
+def fp8_linear(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
+               cfg: GemmConfig | None = None, workspace=None, stream=None) -> None:
+    """y[M, N] (bf16) = blockwise GEMM of group-quantized x[M, K] (bf16) and w[N, K]^T."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or y.shape != (M, N) or x.element_size() != 2:
+        raise ValueError("fp8_linear: shape/dtype mismatch")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_linear(x.data_ptr(), _ld(x, "x"), w.data_ptr(), sw.data_ptr(), _ld(w, "w"),
+                          _ld(sw, "sw"), y.data_ptr(), _ld(y, "y"), M, N, K, eps,
+                          FLAG_UE8M0 if ue8m0 else 0,
+                          ctypes.byref(cfg) if cfg is not None else None,
+                          ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "fp8_linear")
+
+
 # -- conveniences that allocate their outputs with torch (plumbing only) ----
 
 def quantize_activations(x, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
@@ -221,8 +252,19 @@ def block_gemm(a, sa, w, sw, cfg: GemmConfig | None = None, stream=None):
     return y
 
 
+def linear_workspace(M: int, N: int, K: int, cfg: GemmConfig | None, device):
+    import torch
+    n = fp8_linear_workspace_size(M, N, K, cfg)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device) if n else None
+
+
 def linear(x, qw, sw, eps: float = DEFAULT_EPS, ue8m0: bool = False, cfg: GemmConfig | None = None,
            stream=None):
-    """The whole FP8 linear layer: quantize x per 1x128 group, then the blockwise GEMM."""
-    qa, sa = quantize_activations(x, eps, ue8m0, stream)
-    return block_gemm(qa, sa, qw, sw, cfg, stream)
+    """The whole FP8 linear layer (fp8_linear): quantize x per 1x128 group, then the blockwise GEMM."""
+    import torch
+    M, K = x.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = linear_workspace(M, N, K, cfg, x.device)
+    fp8_linear(x, qw, sw, y, eps, ue8m0, cfg, ws, stream)
+    return y

@@ -53,6 +53,38 @@ int64_t workspace_for(const fp8blk_gemm_config& c, int64_t M, int64_t N) {
   return c.split_k > 1 ? (int64_t)c.split_k * M * N * 4 : 0;
 }
 
+int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// fp8_linear's workspace: Swap-AB quantizes in the GEMM and needs only the
+// split-K partials; the other variants first quantize into the workspace:
+// [q: M x K bytes][s: M x K/128 floats][split-K partials], each 256-aligned.
+struct LinearLayout {
+  bool fused;
+  int64_t q_off, s_off, ws_off, total;
+};
+
+LinearLayout linear_layout(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
+  LinearLayout L;
+  L.fused = c.variant == FP8BLK_SWAPAB;
+  const int64_t split = workspace_for(c, M, N);
+  if (L.fused) {
+    L.q_off = L.s_off = L.ws_off = 0;
+    L.total = split;
+    return L;
+  }
+  L.q_off = 0;
+  L.s_off = round256(M * K);
+  L.ws_off = L.s_off + round256(M * (K / kG) * 4);
+  L.total = L.ws_off + split;
+  return L;
+}
+
+int check_quant_args(float eps, uint32_t flags) {
+  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
+  return FP8BLK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,7 +194,7 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
     if (!workspace || workspace_bytes < need) return FP8BLK_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
   }
-  fp8blk::GemmArgs g;
+  fp8blk::GemmArgs g{};
   g.a = a;
   g.sa = sa;
   g.lda = lda;
@@ -181,6 +213,81 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   if (c.variant == FP8BLK_STANDARD)
     return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
+}
+
+int64_t fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, const fp8blk_gemm_config* cfg) {
+  const int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (K > kMaxK) return FP8BLK_ERR_BAD_SHAPE;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+    const int cs = check_config(c, M, N, K);
+    if (cs != FP8BLK_OK) return cs;
+  } else {
+    fp8blk::select_config(M, N, K, 0, &c);
+  }
+  return linear_layout(c, M, N, K).total;
+}
+
+int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw, int64_t ldw,
+               int64_t ldsw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, float eps,
+               uint32_t flags, const fp8blk_gemm_config* cfg, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (K > kMaxK) return FP8BLK_ERR_BAD_SHAPE;
+  st = check_quant_args(eps, flags);
+  if (st != FP8BLK_OK) return st;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    fp8blk::select_config(M, N, K, 0, &c);
+  }
+  st = check_config(c, M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned4(sw) || (ldx * 2) % 16 != 0 ||
+      ldw % 16 != 0 || (ldy * 2) % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  const LinearLayout L = linear_layout(c, M, N, K);
+  if (L.total > 0) {
+    if (!workspace || workspace_bytes < L.total) return FP8BLK_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
+  }
+  const bool ue8m0 = (flags & FP8BLK_FLAG_UE8M0) != 0;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)workspace;
+  fp8blk::GemmArgs g{};
+  g.w = w;
+  g.sw = sw;
+  g.ldw = ldw;
+  g.ldsw = ldsw;
+  g.y = y;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ws = c.split_k > 1 ? (float*)(base + L.ws_off) : nullptr;
+  if (L.fused) {
+    g.x = x;
+    g.ldx = ldx;
+    g.eps = eps;
+    g.ue8m0 = ue8m0 ? 1 : 0;
+    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
+  }
+  uint8_t* q = (uint8_t*)(base + L.q_off);
+  float* sc = (float*)(base + L.s_off);
+  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, s);
+  if (e != hipSuccess) return FP8BLK_ERR_HIP;
+  g.a = q;
+  g.sa = sc;
+  g.lda = K;
+  g.ldsa = K / kG;
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, s));
 }
 
 }  // extern "C"

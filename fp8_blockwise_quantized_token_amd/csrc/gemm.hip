@@ -22,6 +22,10 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+// The fused quantizer must round exactly like fp8_group_quant: no FMA
+// contraction of separate multiplies and adds.
+#pragma clang fp contract(off)
+
 namespace fp8blk {
 namespace {
 
@@ -45,9 +49,15 @@ struct SwapParams {
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const u32x4*)p; }
 
-template <int TOKT, int RN, bool SPLIT>
+// Fused variant (FUSED): the activation operand is quantized here from bf16
+// x with exactly the group rule of fp8_group_quant (same amax, scale,
+// division and encoder), so the GEMM sees the bytes and scales the separate
+// quantizer would have produced.  Lane l holds 32 of the 128 values of group
+// (token, kb); the group amax is reduced over the four lanes l, l^16, l^32,
+// l^48 that hold the same token.
+template <int TOKT, int RN, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
-  constexpr int UNR = 2;
+  constexpr int UNR = (RN + TOKT <= 3) ? 2 : 1;  // K blocks per register batch
   __shared__ float red[8 * RN * TOKT * 4 * 64];
   const GemmArgs& g = p.g;
   const int lane = threadIdx.x & 63;
@@ -61,12 +71,18 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
   const int kb0 = kbs0 + wave * per;
   const int kb1 = min(kb0 + per, kbs1);
 
+  // Matrix-core operands: lane l holds row l & 15 and 32 bytes of the K
+  // block.  Only the pairing of A and B bytes matters, so both operands use
+  // the same K order: lane group g = l >> 4 takes bytes [16g, 16g+16) and
+  // [64+16g, 64+16g+16).  Each 16-byte load instruction then reads 64
+  // contiguous bytes of each of its 16 rows.
   const int row = lane & 15;
-  const int kq = (lane >> 4) * 32;
+  const int kq = (lane >> 4) * 16;
   const uint8_t* wsrc[RN];
 #pragma unroll
   for (int r = 0; r < RN; ++r) wsrc[r] = g.w + (n0 + r * 16 + row) * g.ldw + kq;
   const uint8_t* xsrc[TOKT];
+  const uint16_t* xbsrc[TOKT];  // fused: bf16 activations, element 16g of the block
   const float* sasrc[TOKT];
   bool tvalid[TOKT];
 #pragma unroll
@@ -74,8 +90,12 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
     const int64_t m = t * 16 + row;
     tvalid[t] = m < g.M;
     const int64_t mc = tvalid[t] ? m : 0;
-    xsrc[t] = g.a + mc * g.lda + kq;
-    sasrc[t] = g.sa + mc * g.ldsa;
+    if (FUSED) {
+      xbsrc[t] = g.x + mc * g.ldx + kq;
+    } else {
+      xsrc[t] = g.a + mc * g.lda + kq;
+      sasrc[t] = g.sa + mc * g.ldsa;
+    }
   }
   const float* swsrc = g.sw + (n0 >> 7) * g.ldsw;
 
@@ -85,40 +105,114 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
 #pragma unroll
     for (int t = 0; t < TOKT; ++t) acc[r][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = kb0; kb < kb1; kb += UNR) {
-    v8i wf[UNR][RN], xf[UNR][TOKT];
+  // Two register batches of UNR K blocks each: the loads of the next batch
+  // are issued before the matrix-core work of the current one, so every
+  // wave keeps 2 * UNR K blocks of weight in flight.  Inside a batch, K
+  // blocks past the wave's range re-read its last block (in-bounds, an L2
+  // hit) and get a zero factor.
+  struct Batch {
+    v8i wf[UNR][RN];
+    v8i xf[UNR][TOKT];       // quantized operands (separate-quant path)
     float gsc[UNR][TOKT];
+    u32x4 xr[UNR][TOKT][4];  // fused: 32 raw bf16 values per lane and token tile
+    float swv[UNR];
+  };
+  const int kblast = kb1 - 1;
+  auto load = [&](Batch& b, int kb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int k = kb + u;
-      const bool kval = k < kb1;
-      const int64_t ko = (int64_t)(kval ? k : kb) * 128;
+      const int kc = max(min(k, kblast), 0);
+      const int64_t ko = (int64_t)kc * 128;
 #pragma unroll
       for (int r = 0; r < RN; ++r)
-        wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 16));
-      const float swv = kval ? swsrc[kval ? k : kb] : 0.f;
+        b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
+      const float swv = k <= kblast ? swsrc[kc] : 0.f;
+      if (FUSED) b.swv[u] = swv;
 #pragma unroll
       for (int t = 0; t < TOKT; ++t) {
-        if (tvalid[t]) {
-          xf[u][t] = make_v8i(gload16(xsrc[t] + ko), gload16(xsrc[t] + ko + 16));
-          gsc[u][t] = sasrc[t][kval ? k : kb] * swv;
+        if (FUSED) {
+          if (tvalid[t]) {
+            const uint16_t* src = xbsrc[t] + ko;
+            b.xr[u][t][0] = *(const u32x4*)(src);
+            b.xr[u][t][1] = *(const u32x4*)(src + 8);
+            b.xr[u][t][2] = *(const u32x4*)(src + 64);
+            b.xr[u][t][3] = *(const u32x4*)(src + 72);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b.xr[u][t][c] = u32x4{0u, 0u, 0u, 0u};
+          }
+        } else if (tvalid[t]) {
+          b.xf[u][t] = make_v8i(gload16(xsrc[t] + ko), gload16(xsrc[t] + ko + 64));
+          b.gsc[u][t] = sasrc[t][kc] * swv;
         } else {
-          xf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          gsc[u][t] = 0.f;
+          b.xf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          b.gsc[u][t] = 0.f;
         }
       }
     }
+  };
+  // fused: quantize one lane's 32 values of group (token, kb) -> operand, scale
+  auto quant_operand = [&](const u32x4 (&xr)[4], v8i& op, float& sc) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = xr[c];
+      am = max(am, max(max(w.x & 0x7FFFu, w.x >> 16 & 0x7FFFu), max(w.y & 0x7FFFu, w.y >> 16 & 0x7FFFu)));
+      am = max(am, max(max(w.z & 0x7FFFu, w.z >> 16 & 0x7FFFu), max(w.w & 0x7FFFu, w.w >> 16 & 0x7FFFu)));
+    }
+    am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    sc = scale_from_amax(__uint_as_float(am << 16), g.eps, g.ue8m0 != 0);
+    const float rc = 1.0f / sc;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = xr[c];
+      op[2 * c] = (int)encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+                               div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
+      op[2 * c + 1] = (int)encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+                                   div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
+    }
+  };
+  auto comp = [&](const Batch& b) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
+      v8i xo[TOKT];
+      float gs[TOKT];
+#pragma unroll
+      for (int t = 0; t < TOKT; ++t) {
+        if (FUSED) {
+          float sc;
+          quant_operand(b.xr[u][t], xo[t], sc);
+          gs[t] = sc * b.swv[u];
+        } else {
+          xo[t] = b.xf[u][t];
+          gs[t] = b.gsc[u][t];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RN; ++r)
 #pragma unroll
         for (int t = 0; t < TOKT; ++t) {
-          const v4f P = mfma16x16x128(wf[u][r], xf[u][t]);
+          const v4f P = mfma16x16x128(b.wf[u][r], xo[t]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[r][t][q] = __builtin_fmaf(P[q], gsc[u][t], acc[r][t][q]);
+          for (int q = 0; q < 4; ++q) acc[r][t][q] = __builtin_fmaf(P[q], gs[t], acc[r][t][q]);
         }
     }
+  };
+  Batch b0, b1;
+  load(b0, kb0);
+  for (int kb = kb0; kb < kb1; kb += 2 * UNR) {
+    const bool more1 = kb + UNR < kb1;  // wave-uniform
+    if (more1) load(b1, kb + UNR);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more1) break;
+    if (kb + 2 * UNR < kb1) load(b0, kb + 2 * UNR);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(b1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // lane holds weight rows n0 + 16r + 4*(lane>>4) + q (q = 0..3) for token
@@ -191,6 +285,15 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
+template <int TOKT, int RN, bool FUSED>
+hipError_t run_swap3(const SwapParams& p, dim3 grid, int kwaves, bool split, hipStream_t stream) {
+  if (split)
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true, FUSED>), grid, dim3(64 * kwaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false, FUSED>), grid, dim3(64 * kwaves), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int TOKT, int RN>
 hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stream) {
   SwapParams p;
@@ -198,11 +301,8 @@ hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stre
   p.kb_total = (int)(g.K / 128);
   p.kb_per_split = (p.kb_total + split_k - 1) / split_k;
   dim3 grid((unsigned)(g.N / (16 * RN)), (unsigned)split_k);
-  if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true>), grid, dim3(64 * kwaves), 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false>), grid, dim3(64 * kwaves), 0, stream, p);
-  return hipGetLastError();
+  if (g.x != nullptr) return run_swap3<TOKT, RN, true>(p, grid, kwaves, split_k > 1, stream);
+  return run_swap3<TOKT, RN, false>(p, grid, kwaves, split_k > 1, stream);
 }
 
 }  // namespace

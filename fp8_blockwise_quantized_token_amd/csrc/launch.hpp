@@ -28,6 +28,13 @@ struct GemmArgs {
   int64_t ldy;
   int64_t M, N, K;
   float* ws;  // split-K partials [split][M][N], or nullptr
+  // Fused activation quantization (Swap-AB only): when x is set, the
+  // activation operand is quantized from bf16 x in the GEMM itself and a/sa
+  // are unused.
+  const uint16_t* x;
+  int64_t ldx;
+  float eps;
+  int ue8m0;
 };
 
 // Standard variant: (tile_m, tile_n) among the compiled tiles.
@@ -38,7 +45,7 @@ hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int s
 // Swap-AB variant.
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);
 hipError_t launch_gemm_swapab(const GemmArgs& g, int tile_m, int tile_n, int kwaves,
-                              int split_k, hipStream_t stream);
+                              int split_k, hipStream_t stream);  // fused when g.x != nullptr
 
 // Fixed-order sum of split_k fp32 partials -> bf16.
 hipError_t launch_splitk_reduce(const float* ws, int split_k, int64_t M, int64_t N,

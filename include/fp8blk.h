@@ -179,6 +179,40 @@ int fp8_block_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
                    const fp8blk_gemm_config *cfg, void *workspace,
                    int64_t workspace_bytes, void *stream);
 
+/*
+ * The whole FP8 linear layer in one call: y = scaled_mm_blockwise(
+ * per_token_group_fp8_quant(x), w), i.e. exactly fp8_group_quant(x) (group
+ * 128, this eps and flags) followed by fp8_block_gemm on its output.
+ * Fusing the quantizer into the GEMM removes a launch: at a few tokens the
+ * quantizer is launch-bound (RFC page "[RFC]: Using Helion for Selected vLLM
+ * CustomOps", the SM120 benchmark comment), and the pages count kernel
+ * launches per forward pass as the cost fusion cuts (page "Helion-Kernel in
+ * vLLM", section "Welche Kernel wurden in vLLM integriert").
+ *   SWAPAB configurations (the small-M choice of the dispatcher) quantize
+ *   each 1x128 group of x inside the GEMM's operand load: one kernel (plus
+ *   the split-K sum), and no fp8 copy of x is written.  Codes and scales are
+ *   the ones fp8_group_quant would produce, bit for bit.
+ *   STANDARD configurations run fp8_group_quant into the workspace, then the
+ *   GEMM.
+ *   x  bf16 [M][ldx], ldx >= K            w, sw, y, ldw, ldsw, ldy as in
+ *                                           fp8_block_gemm
+ *   eps, flags as in fp8_group_quant (flags: FP8BLK_FLAG_UE8M0 or 0).
+ *   cfg NULL selects through fp8_block_gemm_select.
+ *   workspace: device buffer of at least fp8_linear_workspace_size bytes,
+ *   16-byte aligned (may be NULL when that is 0); concurrent calls must not
+ *   share one.  Layout (STANDARD): fp8 x [M][K], then its scales
+ *   [M][K/128], then the split-K partials, each at a 256-byte boundary.
+ * Requires K % 128 == 0, K <= 2^22, N % 128 == 0, M >= 0.
+ */
+int64_t fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K,
+                                  const fp8blk_gemm_config *cfg);
+
+int fp8_linear(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw,
+               int64_t ldw, int64_t ldsw, uint16_t *y, int64_t ldy, int64_t M,
+               int64_t N, int64_t K, float eps, uint32_t flags,
+               const fp8blk_gemm_config *cfg, void *workspace,
+               int64_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

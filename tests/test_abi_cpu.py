@@ -166,3 +166,53 @@ def test_select_is_deterministic_and_swaps_small_m():
     # a shape no table holds still gets a valid configuration
     c = fb.fp8_block_gemm_select(777, 384, 1152)
     assert fb.fp8_block_gemm_workspace_size(777, 384, 1152, c) >= 0
+
+
+def _lin(x=A, ldx=256, w=C, sw=D, ldw=256, ldsw=2, y=E, ldy=256, M=8, N=256, K=256, eps=1e-10,
+         flags=0, cfg=None, ws=None, ws_bytes=0):
+    return fb.lib().fp8_linear(x, ldx, w, sw, ldw, ldsw, y, ldy, M, N, K, eps, flags,
+                               ctypes.byref(cfg) if cfg is not None else None, ws, ws_bytes, None)
+
+
+def test_linear_argument_errors():
+    sw1 = fb.make_config(fb.SWAPAB, 16, 16, 1, 2)
+    std = fb.make_config(fb.STANDARD, 128, 128)
+    assert _lin(x=None, cfg=sw1) == NULL
+    assert _lin(w=None, cfg=sw1) == NULL
+    assert _lin(sw=None, cfg=sw1) == NULL
+    assert _lin(y=None, cfg=sw1) == NULL
+    assert _lin(K=200, cfg=sw1) == SHAPE
+    assert _lin(N=200, cfg=sw1) == SHAPE
+    assert _lin(M=-1, cfg=sw1) == SHAPE
+    assert _lin(K=(1 << 22) + 128, ldx=(1 << 22) + 128, ldw=(1 << 22) + 128, ldsw=1 << 16,
+                cfg=sw1) == SHAPE
+    assert _lin(eps=0.0, cfg=sw1) == SHAPE
+    assert _lin(eps=float("nan"), cfg=sw1) == SHAPE
+    assert _lin(flags=2, cfg=sw1) == CFG
+    assert _lin(ldx=128, cfg=sw1) == STRIDE
+    assert _lin(ldw=128, cfg=sw1) == STRIDE
+    assert _lin(ldy=128, cfg=sw1) == STRIDE
+    assert _lin(ldsw=1, cfg=sw1) == STRIDE
+    assert _lin(x=A + 2, cfg=sw1) == MISAL
+    assert _lin(ldx=260, cfg=sw1) == MISAL
+    assert _lin(M=40, cfg=sw1) == CFG  # Swap-AB tile_m < M
+    # Swap-AB quantizes in the GEMM: workspace only for split-K partials
+    assert fb.fp8_linear_workspace_size(8, 256, 256, sw1) == 0
+    sk = fb.make_config(fb.SWAPAB, 16, 16, 2, 1)
+    assert fb.fp8_linear_workspace_size(8, 256, 256, sk) == 2 * 8 * 256 * 4
+    assert _lin(cfg=sk) == WS
+    # Standard: q [M][K] bytes and s [M][K/128] floats first, each padded to 256 bytes
+    n = fb.fp8_linear_workspace_size(8, 256, 256, std)
+    assert n == 8 * 256 + 256
+    assert _lin(cfg=std) == WS
+    assert _lin(cfg=std, ws=0x60000, ws_bytes=n - 1) == WS
+    assert _lin(cfg=std, ws=0x60008, ws_bytes=n) == MISAL
+    stdk = fb.make_config(fb.STANDARD, 64, 128, 2)
+    assert fb.fp8_linear_workspace_size(300, 256, 256, stdk) == 300 * 256 + 2560 + 2 * 300 * 256 * 4
+    assert _lin(M=0, x=None, w=None, sw=None, y=None, cfg=std) == OK
+    # the dispatched configuration is the GEMM's
+    for config in ("decode_8b", "prefill_8b"):
+        for case in synth.cases(config):
+            assert fb.fp8_linear_workspace_size(case.M, case.N, case.K) == \
+                fb.fp8_linear_workspace_size(case.M, case.N, case.K,
+                                             fb.fp8_block_gemm_select(case.M, case.N, case.K))
