@@ -1,11 +1,12 @@
 """Benchmark of the FP8 blockwise-quantized linear layer on one MI355X.
 
 A step is one pass of the whole hot path over every case of the workload:
-for each (M, N, K) case, per-token 1x128 activation quantization of X
-(bf16 -> e4m3fn + fp32 scales) followed by the blockwise-scaled FP8 GEMM in
-the dispatched variant (Standard / Split-K / Swap-AB), bf16 out.  Weights are
-quantized once on the GPU before timing.  Inputs are seeded synthetic tensors
-resident in HBM before the timed region starts.
+for each (M, N, K) case one fp8_linear call -- per-token 1x128 activation
+quantization of X (bf16 -> e4m3fn + fp32 scales) and the blockwise-scaled
+FP8 GEMM in the dispatched variant (Standard / Split-K / Swap-AB; for Swap-AB
+the quantizer runs inside the GEMM), bf16 out.  Weights are quantized once on
+the GPU before timing.  Inputs are seeded synthetic tensors resident in HBM
+before the timed region starts.
 
 Default workload "qwen3_8b": the Qwen3-8B-shaped layers (qkv, o_proj,
 gate_up, down) at M in {1, 8, 32, 64} (decode) and M = 8192 (prefill), the
@@ -59,13 +60,20 @@ def quant_bytes(c) -> int:
     return 2 * c.M * c.K + c.M * c.K + 4 * c.M * c.K // 128
 
 
-def kernel_symbol(cfg) -> str:
-    """Name fragment of the GEMM kernel a configuration launches."""
+def kernel_symbol(cfg, fused: bool = False) -> str:
+    """Name of the GEMM kernel a configuration launches, as rocprofv3 prints it."""
+    b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
-        return f"k_gemm_lds<{cfg.tile_m},{cfg.tile_n},{wm},64,{'true' if cfg.split_k > 1 else 'false'}>"
-    return (f"k_gemm_swapab<{cfg.tile_m // 16},{cfg.tile_n // 16},"
-            f"{'true' if cfg.split_k > 1 else 'false'}>")
+        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}>"
+    return (f"k_gemm_swapab<{cfg.tile_m // 16}, {cfg.tile_n // 16}, "
+            f"{b(cfg.split_k > 1)}, {b(fused)}>")
+
+
+def kernel_sources(symbol: str):
+    if symbol.startswith("k_gemm_lds"):
+        return ("gemm_standard.hip", "device_common.hpp")
+    return ("gemm.hip", "device_common.hpp")
 
 
 def source_hash(*names: str) -> str:
@@ -76,9 +84,10 @@ def source_hash(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(symbol: str, src_hash: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on this exact kernel source; else None."""
+def traffic_from_profiles(symbol: str):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), if it was taken on the
+    current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -86,55 +95,49 @@ def traffic_from_profiles(symbol: str, src_hash: str):
         data = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if data.get("source_hash") != src_hash:
-        return None
     ent = data.get("kernels", {}).get(symbol)
-    return None if ent is None else ent.get("bytes_per_launch")
+    if ent is None or ent.get("source_hash") != source_hash(*kernel_sources(symbol)):
+        return None
+    return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(cases, budget_s: float):
-    """The oracle (untuned) on a bounded sample: every case's GEMM on its first
-    rows, doubling the rows until about budget_s of work has been timed."""
+def cpu_baseline(cases, xs, budget_s: float):
+    """The oracle (untuned) on a bounded sample: every case's quantization and
+    fp64 GEMM on its first rows, doubling the rows until one pass takes
+    about half the budget (or every row of every case is covered)."""
     import numpy as np
     import oracle
     from fp8_blockwise_quantized_token_amd import synth
 
     threads = oracle.default_threads()
-    prepared = []
     wcache = {}
     for c in cases:
-        x = synth.activations_bf16(c)
-        rows = min(c.M, 64)
-        xs = np.ascontiguousarray(x[:rows])
         key = (c.N, c.K, c.ue8m0)
         if key not in wcache:
             wcache[key] = oracle.weight_block_quant(synth.weights_f32(c.N, c.K), ue8m0=c.ue8m0,
                                                     nthreads=threads)
-        qw, sw = wcache[key]
-        prepared.append((c, xs, qw, sw))
-    flops = 0.0
-    t_total = 0.0
-    rows_used = 0
     nrows = 1
     while True:
-        t0 = time.perf_counter()
         f = 0.0
         r_used = 0
-        for c, xs, qw, sw in prepared:
-            r = min(nrows, xs.shape[0])
-            qa, sa = oracle.group_quant(xs[:r], ue8m0=c.ue8m0, nthreads=threads)
+        t_total = 0.0
+        for c, x in zip(cases, xs):
+            r = min(nrows, c.M)
+            qw, sw = wcache[(c.N, c.K, c.ue8m0)]
+            rows = np.ascontiguousarray(x[:r])
+            t0 = time.perf_counter()
+            qa, sa = oracle.group_quant(rows, ue8m0=c.ue8m0, nthreads=threads)
             oracle.block_gemm(qa, sa, qw, sw, nthreads=threads)
+            t_total += time.perf_counter() - t0
             f += 2.0 * r * c.N * c.K
             r_used += r
-        dt = time.perf_counter() - t0
-        flops, t_total, rows_used = f, dt, r_used
-        if dt > budget_s / 3 or nrows >= 64:
+        if t_total > budget_s / 2 or all(nrows >= c.M for c in cases):
             break
         nrows *= 2
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {nrows} row(s) of each of the {len(cases)} cases ({rows_used} rows, "
-                      f"{flops / 1e9:.1f} GFLOP incl. their activation quantization), "
-                      f"{t_total:.1f} s on {threads} host threads"}
+    return {"value": round(f / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first min(M, {nrows}) rows of each of the {len(cases)} cases ({r_used} rows, "
+                      f"{f / 1e9:.1f} GFLOP; oracle quantizer + fp64 GEMM), {t_total:.1f} s on "
+                      f"{threads} host threads"}
 
 
 def main() -> int:
@@ -145,7 +148,7 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--kernel-reps", type=int, default=10)
     args = ap.parse_args()
 
@@ -186,22 +189,29 @@ def main() -> int:
 
     # per-case buffers
     bufs = []
+    xs = []
     for i, c in enumerate(cases):
-        x = torch.from_numpy(synth.activations_bf16(c).view(np.int16)).to(dev).view(torch.bfloat16)
+        xh = synth.activations_bf16(c)
+        xs.append(xh)
+        x = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
         qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
         sa = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
         cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K)
         ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
+        lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
-        bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, qw=qw, sw=sw))
+        bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, lws=lws, qw=qw, sw=sw,
+                         fused=cfg.variant == fb.SWAPAB))
     torch.cuda.synchronize()
+
+    def linear(b):
+        fb.fp8_linear(b["x"], b["qw"], b["sw"], b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
+                      workspace=b["lws"], stream=stream)
 
     def step():
         for b in bufs:
-            c = b["case"]
-            fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream)
-            fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+            linear(b)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -236,51 +246,64 @@ def main() -> int:
     total_flops = sum(b["case"].flops() for b in bufs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-kernel durations (HIP events on the launch stream) ----
+    # ---- per-case and per-kernel durations (HIP events on the launch stream) ----
+    # quant: fp8_group_quant alone; gemm: the GEMM kernel of the step's call
+    # (fused Swap-AB: fp8_linear itself; Standard: fp8_block_gemm on the
+    # quantized input; a split-K call includes its reduce kernel); linear:
+    # the step's fp8_linear call.
     reps = args.kernel_reps
+
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            fn()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
     per_case = []
     sym_time = {}
     sym_work = {}
     for b in bufs:
         c = b["case"]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        with torch.cuda.stream(stream):
-            e[0].record(stream)
-            for _ in range(reps):
-                fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream)
-            e[1].record(stream)
-            e[2].record(stream)
-            for _ in range(reps):
-                fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
-            e[3].record(stream)
-        stream.synchronize()
-        tq = e[0].elapsed_time(e[1]) / reps * 1e-3
-        tg = e[2].elapsed_time(e[3]) / reps * 1e-3
+        tq = timed(lambda: fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream))
+        tl = timed(lambda: linear(b))
+        if b["fused"]:
+            tg = tl
+        else:
+            tg = timed(lambda: fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"],
+                                                 b["ws"], stream=stream))
         fl = c.flops()
-        gb = gemm_bytes(c)
-        frac = max(fl / (PEAK_FP8_TFLOPS * 1e12), gb / (PEAK_HBM_GBPS * 1e9)) / tg
-        sym = kernel_symbol(b["cfg"])
+        gb = gemm_bytes(c) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
+        lb = gemm_bytes(c) + quant_bytes(c) if not b["fused"] else gb
+        sym = kernel_symbol(b["cfg"], b["fused"])
         sym_time[sym] = sym_time.get(sym, 0.0) + tg
-        sym_work.setdefault(sym, [0.0, 0.0, 0])
-        sym_work[sym][0] += fl
-        sym_work[sym][1] += gb
-        sym_work[sym][2] += 1
+        w = sym_work.setdefault(sym, [0.0, 0.0, 0, 0])
+        w[0] += fl
+        w[1] += gb
+        w[2] += 1
+        w[3] += 1 if b["cfg"].split_k > 1 else 0
+        roof_t = max(fl / (PEAK_FP8_TFLOPS * 1e12), gb / (PEAK_HBM_GBPS * 1e9))
         per_case.append({
             "case": c.cid, "cfg": b["cfg"].as_dict(), "kernel": sym,
-            "gemm_us": round(tg * 1e6, 2), "quant_us": round(tq * 1e6, 2),
+            "linear_us": round(tl * 1e6, 2), "gemm_us": round(tg * 1e6, 2), "quant_us": round(tq * 1e6, 2),
             "gemm_tflops": round(fl / tg / 1e12, 2), "gemm_gbps": round(gb / tg / 1e9, 1),
-            "gemm_roofline_frac": round(frac, 4),
+            "gemm_roofline_frac": round(roof_t / tg, 4),
+            "linear_tflops": round(fl / tl / 1e12, 2), "linear_gbps": round(lb / tl / 1e9, 1),
             "quant_gbps": round(quant_bytes(c) / tq / 1e9, 1),
         })
 
     dom = max(sym_time, key=sym_time.get)
-    dflops, dbytes, dlaunches = sym_work[dom]
+    dflops, dbytes, dlaunches, dsplit = sym_work[dom]
     avg_t = sym_time[dom] / dlaunches
     flop_per_launch = dflops / dlaunches
     byte_per_launch = dbytes / dlaunches
     mfma_bound = flop_per_launch / (PEAK_FP8_TFLOPS * 1e12) >= byte_per_launch / (PEAK_HBM_GBPS * 1e9)
-    src_hash = source_hash("gemm.hip", "device_common.hpp")
-    traffic = traffic_from_profiles(dom, src_hash)
+    traffic = traffic_from_profiles(dom)
     if mfma_bound:
         ach = flop_per_launch / avg_t / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
@@ -292,12 +315,18 @@ def main() -> int:
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
     roof["launches_measured"] = dlaunches * reps
+    roof["algorithmic_per_launch"] = {"flop": flop_per_launch, "bytes": byte_per_launch}
+    if dsplit:
+        roof["note"] = "split-K calls: duration includes the reduce kernel"
 
     qb = sum(quant_bytes(b["case"]) for b in bufs)
     qt = sum(p["quant_us"] for p in per_case) * 1e-6
-    decode = [p for p, b in zip(per_case, bufs) if b["case"].M <= 64]
-    dec_bytes = sum(gemm_bytes(b["case"]) for b in bufs if b["case"].M <= 64)
-    dec_t = sum(p["gemm_us"] for p in decode) * 1e-6
+    dec = [(p, b) for p, b in zip(per_case, bufs) if b["case"].M <= 64]
+    dec_bytes = sum(gemm_bytes(b["case"]) for _, b in dec)
+    dec_t = sum(p["linear_us"] for p, _ in dec) * 1e-6
+    pre = [(p, b) for p, b in zip(per_case, bufs) if b["case"].M >= 4096]
+    pre_fl = sum(b["case"].flops() for _, b in pre)
+    pre_t = sum(p["linear_us"] for p, _ in pre) * 1e-6
 
     out = {
         "metric": "FP8 block GEMM TFLOP/s + quant GB/s at M=1..8192, % of MI355X roofline",
@@ -315,16 +344,18 @@ def main() -> int:
         "config": {"workload": args.workload, "cases": len(cases),
                    "m_values": sorted({b["case"].M for b in bufs}),
                    "nk": sorted({(b["case"].N, b["case"].K) for b in bufs}),
-                   "graph_replay": graph is not None, "weight_copies": WEIGHT_COPIES},
+                   "call": "fp8_linear", "graph_replay": graph is not None,
+                   "weight_copies": WEIGHT_COPIES},
         "quant_gbps": round(qb / qt / 1e9, 1) if qt > 0 else None,
-        "decode_gemm_gbps": round(dec_bytes / dec_t / 1e9, 1) if dec_t > 0 else None,
+        "decode_linear_gbps": round(dec_bytes / dec_t / 1e9, 1) if dec_t > 0 else None,
+        "prefill_linear_tflops": round(pre_fl / pre_t / 1e12, 1) if pre_t > 0 else None,
         "roofline": roof,
         "cases": per_case,
         "wall_s_timed": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(cases, xs, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
 

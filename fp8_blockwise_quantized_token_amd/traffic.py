@@ -1,0 +1,174 @@
+"""HBM traffic per kernel launch from rocprofv3 counters (run on an MI355X).
+
+Two steps, each under its own rocprofv3 counter pass:
+
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o p -- \\
+      python3 -m fp8_blockwise_quantized_token_amd.traffic run
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_w> -o p -- \\
+      python3 -m fp8_blockwise_quantized_token_amd.traffic run
+  python3 -m fp8_blockwise_quantized_token_amd.traffic summarize <dir_f> <dir_w> \\
+      --out profiles/hbm_traffic.json
+
+``run`` launches every case of the workload once through fp8_linear (and
+once through fp8_block_gemm on pre-quantized input, so the Standard GEMM
+kernel is seen alone) plus a plain device-to-device copy of a known size.
+``summarize`` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per
+kernel, scales each by what the same counter reads for the copy (bytes
+expected / bytes counted), and records the result keyed by the kernel name
+and by a hash of the kernel sources, so a reader can tell when the numbers
+no longer describe the code.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+COPY_BYTES = 1 << 30
+PREFIX = "void fp8blk::(anonymous namespace)::"
+
+
+def source_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_sources(symbol: str):
+    if symbol.startswith("k_gemm_lds"):
+        return ("gemm_standard.hip", "device_common.hpp")
+    if symbol.startswith("k_group_quant"):
+        return ("quant.hip", "device_common.hpp")
+    return ("gemm.hip", "device_common.hpp")
+
+
+def short_name(name: str) -> str:
+    if name.startswith(PREFIX):
+        name = name[len(PREFIX):]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def run(workload: str) -> None:
+    import numpy as np
+    import torch
+    import fp8_blockwise_quantized_token_amd as fb
+    from fp8_blockwise_quantized_token_amd import synth
+    sys.path.insert(0, ROOT)
+    import bench
+
+    dev = torch.device("cuda:0")
+    cases = bench.workload_cases(workload)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    wq = {}
+    for c in cases:
+        key = (c.N, c.K, c.ue8m0)
+        if key not in wq:
+            w = torch.from_numpy(synth.weights_f32(c.N, c.K)).to(dev)
+            wq[key] = fb.quantize_weight(w, ue8m0=c.ue8m0)
+            del w
+        qw, sw = wq[key]
+        x = torch.from_numpy(synth.activations_bf16(c).view(np.int16)).to(dev).view(torch.bfloat16)
+        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K)
+        print(f"[traffic] {c.cid} {cfg.as_dict()}", flush=True)
+        fb.linear(x, qw, sw, ue8m0=c.ue8m0, cfg=cfg)
+        if cfg.variant == fb.STANDARD:
+            qa, sa = fb.quantize_activations(x, ue8m0=c.ue8m0)
+            fb.block_gemm(qa, sa, qw, sw, cfg)
+        torch.cuda.synchronize()
+
+
+def _read_counter(d: str, counter: str) -> dict:
+    """Counter value of every dispatch (summed over the rows rocprofv3 writes
+    for it), grouped by kernel short name."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                k = (short_name(r["Kernel_Name"]), r.get("Dispatch_Id", ""))
+                per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize(dir_f: str, dir_w: str, out_path: str) -> None:
+    fetch = _read_counter(dir_f, "FETCH_SIZE")
+    write = _read_counter(dir_w, "WRITE_SIZE")
+    # the calibration copy is the largest device copy of the run
+    copy = [k for k in fetch if "copy" in k.lower()]
+    copy_f = max(max(fetch[k]) for k in copy)
+    copy_w = max(max(write[k]) for k in copy if k in write)
+    expected_kib = COPY_BYTES / 1024
+    f_fac = expected_kib / copy_f
+    w_fac = expected_kib / copy_w
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if not name.startswith("k_"):
+            continue
+        fb_ = sum(fetch[name]) / len(fetch[name]) * f_fac * 1024
+        wb_ = sum(write[name]) / len(write[name]) * w_fac * 1024
+        kernels[name] = {"fetch_bytes": round(fb_), "write_bytes": round(wb_),
+                         "bytes_per_launch": round(fb_ + wb_), "dispatches": len(fetch[name]),
+                         "source_hash": source_hash(*kernel_sources(name))}
+    data = {"counters": ["FETCH_SIZE", "WRITE_SIZE"], "unit": "bytes per dispatch (average)",
+            "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": copy,
+                            "fetch_kib_read": copy_f, "write_kib_read": copy_w,
+                            "fetch_factor": f_fac, "write_factor": w_fac},
+            "kernels": kernels}
+    with open(out_path, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(data["calibration"]))
+    for k, v in kernels.items():
+        print(f"{k:60s} fetch {v['fetch_bytes'] / 1e6:10.2f} MB  write {v['write_bytes'] / 1e6:9.2f} MB "
+              f"({v['dispatches']} dispatches)")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="qwen3_8b")
+    s = sub.add_parser("summarize")
+    s.add_argument("dir_fetch")
+    s.add_argument("dir_write")
+    s.add_argument("--out", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run(a.workload)
+    else:
+        summarize(a.dir_fetch, a.dir_write, a.out)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -10,6 +10,11 @@ weights rotated over enough copies that no launch re-reads a weight from the
 256 MB Infinity Cache, and records the fastest.  ``--write-table`` turns a
 result file into ``csrc/dispatch_table.inc`` (buckets of M keyed on (N, K)).
 
+By default the whole layer is timed (``fp8_linear``: activation quantization
+included, fused into the GEMM for Swap-AB configurations), since that is the
+call the table serves on the hot path; ``--op gemm`` times
+``fp8_block_gemm`` on pre-quantized activations instead.
+
   python -m fp8_blockwise_quantized_token_amd.tune --shapes all --out tune.json
   python -m fp8_blockwise_quantized_token_amd.tune --write-table tune.json
 """
@@ -63,24 +68,36 @@ def candidates(M: int, N: int, K: int):
     return out
 
 
-def time_config(fb, torch, bufs, cfg, reps: int) -> float:
-    """Microseconds per launch: a graph of `reps` launches over rotating
-    weight copies, replayed 3 times; the best replay counts."""
+def workspace_bytes(fb, op: str, M: int, N: int, K: int, cfg) -> int:
+    if op == "linear":
+        return fb.fp8_linear_workspace_size(M, N, K, cfg)
+    return fb.fp8_block_gemm_workspace_size(M, N, K, cfg)
+
+
+def time_config(fb, torch, bufs, cfg, reps: int, op: str) -> float:
+    """Microseconds per call: a graph of `reps` calls over rotating weight
+    copies, replayed 3 times; the best replay counts."""
     M, N, K = bufs["M"], bufs["N"], bufs["K"]
-    n = fb.fp8_block_gemm_workspace_size(M, N, K, cfg)
+    n = workspace_bytes(fb, op, M, N, K, cfg)
     ws = bufs["ws_pool"][: max(n, 16)] if n else None
     stream = bufs["stream"]
     copies = bufs["w"]
+
+    def call(i):
+        qw, sw = copies[i % len(copies)]
+        if op == "linear":
+            fb.fp8_linear(bufs["x"], qw, sw, bufs["y"], cfg=cfg, workspace=ws, stream=stream)
+        else:
+            fb.fp8_block_gemm(bufs["a"], bufs["sa"], qw, sw, bufs["y"], cfg, ws, stream=stream)
+
     with torch.cuda.stream(stream):
         for i in range(2):
-            qw, sw = copies[i % len(copies)]
-            fb.fp8_block_gemm(bufs["a"], bufs["sa"], qw, sw, bufs["y"], cfg, ws, stream=stream)
+            call(i)
     stream.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(reps):
-            qw, sw = copies[i % len(copies)]
-            fb.fp8_block_gemm(bufs["a"], bufs["sa"], qw, sw, bufs["y"], cfg, ws, stream=stream)
+            call(i)
     best = float("inf")
     for _ in range(3):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -104,7 +121,7 @@ def run_sweep(args) -> dict:
     stream = torch.cuda.Stream()
     shapes = shape_sets(args.shapes)
     ms = [int(m) for m in args.ms.split(",")] if args.ms else M_VALUES
-    results = {"device": torch.cuda.get_device_name(0), "entries": []}
+    results = {"device": torch.cuda.get_device_name(0), "op": args.op, "entries": []}
     ws_pool = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)  # 1 GiB split-K workspace pool
     t0 = time.time()
     for (N, K) in shapes:
@@ -124,15 +141,16 @@ def run_sweep(args) -> dict:
             a[a == 0x7F] = 0x38
             a[a == 0xFF] = 0xB8
             sa = torch.rand((M, K // 128), device=dev, generator=gen) + 0.5
+            x = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            bufs = dict(M=M, N=N, K=K, a=a, sa=sa, y=y, w=copies, stream=stream, ws_pool=ws_pool)
+            bufs = dict(M=M, N=N, K=K, a=a, sa=sa, x=x, y=y, w=copies, stream=stream, ws_pool=ws_pool)
             flops = 2.0 * M * N * K
             reps = int(min(50, max(4, 2e-3 / max(flops / 2.0e15, wbytes / 6.0e12))))
             timings = []
             for cfg in candidates(M, N, K):
-                if fb.fp8_block_gemm_workspace_size(M, N, K, cfg) > ws_pool.numel():
+                if workspace_bytes(fb, args.op, M, N, K, cfg) > ws_pool.numel():
                     continue
-                us = time_config(fb, torch, bufs, cfg, reps)
+                us = time_config(fb, torch, bufs, cfg, reps, args.op)
                 timings.append((us, cfg.as_dict()))
             timings.sort(key=lambda t: t[0])
             disp = fb.fp8_block_gemm_select(M, N, K).as_dict()
@@ -145,7 +163,7 @@ def run_sweep(args) -> dict:
                   f"({flops / best_us / 1e6:7.1f} TFLOP/s, "
                   f"{(wbytes + M * K + 2 * M * N) / best_us / 1e3:7.1f} GB/s) {best}  "
                   f"dispatch {disp_us} {disp}  [{time.time() - t0:.0f}s]", flush=True)
-            del a, sa, y, bufs
+            del a, sa, x, y, bufs
         del copies
         torch.cuda.empty_cache()
     return results
@@ -159,7 +177,8 @@ def write_table(path: str, out_inc: str) -> None:
         by_shape.setdefault((e["N"], e["K"]), []).append(e)
     lines = ["// dispatch_table.inc -- per-shape GEMM configurations measured on MI355X",
              "// by fp8_blockwise_quantized_token_amd/tune.py (HIP-graph replay, weights",
-             "// rotated past the Infinity Cache).  Entry: {N, K, M_lo, M_hi,",
+             f"// rotated past the Infinity Cache; timed call: {data.get('op', 'gemm')}).",
+             "// Entry: {N, K, M_lo, M_hi,",
              "// CFG(variant, tile_m, tile_n, split_k, kwaves)}; the first bucket",
              "// containing M wins.",
              "static const Entry kTable[] = {"]
@@ -186,6 +205,7 @@ def main() -> int:
     ap.add_argument("--shapes", default="all", help="all or a comma list of 1.7b,8b,32b")
     ap.add_argument("--ms", default="", help="comma list of M values (default: the standard set)")
     ap.add_argument("--out", default="tune.json")
+    ap.add_argument("--op", choices=("linear", "gemm"), default="linear")
     ap.add_argument("--write-table", metavar="RESULTS", help="write csrc/dispatch_table.inc from a result file")
     args = ap.parse_args()
     if args.write_table:
