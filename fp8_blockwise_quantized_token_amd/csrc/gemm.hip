@@ -49,16 +49,28 @@ struct SwapParams {
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const u32x4*)p; }
 
-// Fused variant (FUSED): the activation operand is quantized here from bf16
-// x with exactly the group rule of fp8_group_quant (same amax, scale,
+// Fused variants (FQ != 0): the activation operand is quantized here from
+// bf16 x with exactly the group rule of fp8_group_quant (same amax, scale,
 // division and encoder), so the GEMM sees the bytes and scales the separate
-// quantizer would have produced.  Lane l holds 32 of the 128 values of group
-// (token, kb); the group amax is reduced over the four lanes l, l^16, l^32,
-// l^48 that hold the same token.
-template <int TOKT, int RN, bool SPLIT, bool FUSED>
+// quantizer would have produced.
+//   FQ = 16: lane l holds 32 of the 128 values of group (token l & 15, kb)
+//     in operand order; the group amax is reduced over the four lanes l,
+//     l^16, l^32, l^48 that hold the same token.
+//   FQ = 1, 2, 4, 8 (M <= FQ, one token tile): only the FQ tokens that can
+//     be valid are quantized, 64/FQ lanes per token and 2 FQ values per lane
+//     (the work of the 16 - FQ padding rows is not done); the codes go to a
+//     wave-private 16 x 128-byte LDS tile (rows >= FQ stay zero) and are
+//     read back in operand order.
+template <int TOKT, int RN, bool SPLIT, int FQ>
 __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
+  constexpr bool FUSED = FQ != 0;
+  constexpr bool LEAN = FQ > 0 && FQ < 16;
+  static_assert(!LEAN || TOKT == 1, "the lean quantizer serves one token tile");
+  constexpr int LPT = LEAN ? 64 / FQ : 1;      // lanes per token
+  constexpr int EPL = LEAN ? 128 / LPT : 2;    // values per lane (2 FQ)
   constexpr int UNR = (RN + TOKT <= 3) ? 2 : 1;  // K blocks per register batch
   __shared__ float red[8 * RN * TOKT * 4 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t xq_all[LEAN ? 8 * 2112 : 16];  // per wave: codes, scales
   const GemmArgs& g = p.g;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -99,6 +111,18 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
   }
   const float* swsrc = g.sw + (n0 >> 7) * g.ldsw;
 
+  // lean quantizer: lane (lt, lp) loads values [lp EPL, (lp+1) EPL) of token lt
+  const int lt = lane / LPT, lp = lane % LPT;
+  const bool lvalid = lt < g.M;
+  const uint16_t* lsrc = LEAN ? g.x + (int64_t)(lvalid ? lt : 0) * g.ldx + lp * EPL : nullptr;
+  uint8_t* xq = xq_all + (LEAN ? wave * 2112 : 0);  // 16 rows x 128 code bytes, then 16 scales
+  if (LEAN) {
+    u32x4* z = (u32x4*)xq;
+    z[lane] = u32x4{0u, 0u, 0u, 0u};
+    z[lane + 64] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 4) z[128 + lane] = u32x4{0u, 0u, 0u, 0u};
+  }
+
   v4f acc[RN][TOKT];
 #pragma unroll
   for (int r = 0; r < RN; ++r)
@@ -114,7 +138,8 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
     v8i wf[UNR][RN];
     v8i xf[UNR][TOKT];       // quantized operands (separate-quant path)
     float gsc[UNR][TOKT];
-    u32x4 xr[UNR][TOKT][4];  // fused: 32 raw bf16 values per lane and token tile
+    u32x4 xr[UNR][TOKT][4];             // fused (FQ = 16): 32 raw bf16 values of this lane
+    u32x4 xl[UNR][LEAN && FQ == 8 ? 2 : 1];  // lean: 2 FQ raw bf16 values
     float swv[UNR];
   };
   const int kblast = kb1 - 1;
@@ -129,6 +154,25 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
         b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
       const float swv = k <= kblast ? swsrc[kc] : 0.f;
       if (FUSED) b.swv[u] = swv;
+      if (LEAN) {
+        u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = u32x4{0u, 0u, 0u, 0u};
+        if (lvalid) {
+          const uint16_t* src = lsrc + ko;
+          if (FQ == 1) {
+            v0.x = *(const uint32_t*)src;
+          } else if (FQ == 2) {
+            const uint2 t2 = *(const uint2*)src;
+            v0.x = t2.x;
+            v0.y = t2.y;
+          } else {
+            v0 = *(const u32x4*)src;
+            if (FQ == 8) v1 = *(const u32x4*)(src + 8);
+          }
+        }
+        b.xl[u][0] = v0;
+        if (FQ == 8) b.xl[u][LEAN && FQ == 8 ? 1 : 0] = v1;
+        continue;
+      }
 #pragma unroll
       for (int t = 0; t < TOKT; ++t) {
         if (FUSED) {
@@ -174,6 +218,58 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
                                    div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
     }
   };
+  // lean: quantize this lane's 2 FQ values, stage the codes and the scale in
+  // the wave's LDS tile, read back this lane's operand row and its scale
+  auto lean_operand = [&](const u32x4 (&xl)[LEAN && FQ == 8 ? 2 : 1], v8i& op, float& sc) {
+    constexpr int NW = EPL / 2;  // 32-bit words of bf16 pairs
+    uint32_t wd[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) wd[i] = xl[i >> 2][i & 3];
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) am = max(am, max(wd[i] & 0x7FFFu, wd[i] >> 16 & 0x7FFFu));
+    // maximum over the LPT lanes of this token: DPP inside 16-lane rows,
+    // then across rows through scalar reads of one lane per row
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    if (LPT >= 16) am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x140, 0xF, 0xF, false));  // row_mirror
+    if (LPT == 32) {
+      const uint32_t r0 = max((uint32_t)__builtin_amdgcn_readlane((int)am, 0), (uint32_t)__builtin_amdgcn_readlane((int)am, 16));
+      const uint32_t r1 = max((uint32_t)__builtin_amdgcn_readlane((int)am, 32), (uint32_t)__builtin_amdgcn_readlane((int)am, 48));
+      am = lane < 32 ? r0 : r1;
+    } else if (LPT == 64) {
+      am = max(max((uint32_t)__builtin_amdgcn_readlane((int)am, 0), (uint32_t)__builtin_amdgcn_readlane((int)am, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)am, 32), (uint32_t)__builtin_amdgcn_readlane((int)am, 48)));
+    }
+    const float s_own = scale_from_amax(__uint_as_float(am << 16), g.eps, g.ue8m0 != 0);
+    const float rc = 1.0f / s_own;
+    uint32_t code[NW / 2 > 0 ? NW / 2 : 1];
+    if (NW == 1) {
+      code[0] = encode4(div_by_scale(bf16_lo(wd[0]), s_own, rc), div_by_scale(bf16_hi(wd[0]), s_own, rc), 0.f, 0.f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW / 2; ++i)
+        code[i] = encode4(div_by_scale(bf16_lo(wd[2 * i]), s_own, rc), div_by_scale(bf16_hi(wd[2 * i]), s_own, rc),
+                          div_by_scale(bf16_lo(wd[2 * i + 1]), s_own, rc),
+                          div_by_scale(bf16_hi(wd[2 * i + 1]), s_own, rc));
+    }
+    uint8_t* dst = xq + lt * 128 + lp * EPL;
+    if (FQ == 1) {
+      *(uint16_t*)dst = (uint16_t)code[0];
+    } else if (FQ == 2) {
+      *(uint32_t*)dst = code[0];
+    } else if (FQ == 4) {
+      *(uint2*)dst = make_uint2(code[0], code[NW / 2 > 1 ? 1 : 0]);
+    } else {
+      *(u32x4*)dst = u32x4{code[0], code[NW / 2 > 1 ? 1 : 0], code[NW / 2 > 2 ? 2 : 0], code[NW / 2 > 3 ? 3 : 0]};
+    }
+    if (lp == 0) *(float*)(xq + 2048 + lt * 4) = s_own;
+    __builtin_amdgcn_wave_barrier();
+    op = make_v8i(*(const u32x4*)(xq + row * 128 + kq), *(const u32x4*)(xq + row * 128 + kq + 64));
+    sc = *(const float*)(xq + 2048 + row * 4);
+    __builtin_amdgcn_wave_barrier();
+  };
   auto comp = [&](const Batch& b) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -181,7 +277,11 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
       float gs[TOKT];
 #pragma unroll
       for (int t = 0; t < TOKT; ++t) {
-        if (FUSED) {
+        if constexpr (LEAN) {
+          float sc;
+          lean_operand(b.xl[u], xo[t], sc);
+          gs[t] = sc * b.swv[u];
+        } else if constexpr (FUSED) {
           float sc;
           quant_operand(b.xr[u][t], xo[t], sc);
           gs[t] = sc * b.swv[u];
@@ -285,12 +385,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
-template <int TOKT, int RN, bool FUSED>
+template <int TOKT, int RN, int FQ>
 hipError_t run_swap3(const SwapParams& p, dim3 grid, int kwaves, bool split, hipStream_t stream) {
   if (split)
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true, FUSED>), grid, dim3(64 * kwaves), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true, FQ>), grid, dim3(64 * kwaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false, FUSED>), grid, dim3(64 * kwaves), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false, FQ>), grid, dim3(64 * kwaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -301,8 +401,15 @@ hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stre
   p.kb_total = (int)(g.K / 128);
   p.kb_per_split = (p.kb_total + split_k - 1) / split_k;
   dim3 grid((unsigned)(g.N / (16 * RN)), (unsigned)split_k);
-  if (g.x != nullptr) return run_swap3<TOKT, RN, true>(p, grid, kwaves, split_k > 1, stream);
-  return run_swap3<TOKT, RN, false>(p, grid, kwaves, split_k > 1, stream);
+  const bool sp = split_k > 1;
+  if (g.x == nullptr) return run_swap3<TOKT, RN, 0>(p, grid, kwaves, sp, stream);
+  if (TOKT == 1) {  // quantize only the tokens that can be valid
+    if (g.M <= 1) return run_swap3<TOKT, RN, TOKT == 1 ? 1 : 16>(p, grid, kwaves, sp, stream);
+    if (g.M <= 2) return run_swap3<TOKT, RN, TOKT == 1 ? 2 : 16>(p, grid, kwaves, sp, stream);
+    if (g.M <= 4) return run_swap3<TOKT, RN, TOKT == 1 ? 4 : 16>(p, grid, kwaves, sp, stream);
+    if (g.M <= 8) return run_swap3<TOKT, RN, TOKT == 1 ? 8 : 16>(p, grid, kwaves, sp, stream);
+  }
+  return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
 }
 
 }  // namespace
