@@ -60,14 +60,16 @@ def quant_bytes(c) -> int:
     return 2 * c.M * c.K + c.M * c.K + 4 * c.M * c.K // 128
 
 
-def kernel_symbol(cfg, fused: bool = False) -> str:
+def kernel_symbol(cfg, fused: bool = False, M: int = 0) -> str:
     """Name of the GEMM kernel a configuration launches, as rocprofv3 prints it."""
     b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
-        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}>"
-    return (f"k_gemm_swapab<{cfg.tile_m // 16}, {cfg.tile_n // 16}, "
-            f"{b(cfg.split_k > 1)}, {b(fused)}>")
+        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}>"
+    fq = 0
+    if fused:  # the fused quantizer variant the launcher picks for this M
+        fq = 16 if cfg.tile_m > 16 or M > 8 else (1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8)
+    return f"k_gemm_swapab<{cfg.tile_m // 16}, {cfg.tile_n // 16}, {b(cfg.split_k > 1)}, {fq}>"
 
 
 def kernel_sources(symbol: str):
@@ -280,7 +282,7 @@ def main() -> int:
         fl = c.flops()
         gb = gemm_bytes(c) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
         lb = gemm_bytes(c) + quant_bytes(c) if not b["fused"] else gb
-        sym = kernel_symbol(b["cfg"], b["fused"])
+        sym = kernel_symbol(b["cfg"], b["fused"], c.M)
         sym_time[sym] = sym_time.get(sym, 0.0) + tg
         w = sym_work.setdefault(sym, [0.0, 0.0, 0, 0])
         w[0] += fl

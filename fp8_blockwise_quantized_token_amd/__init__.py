@@ -38,20 +38,22 @@ _STATUS = {0: "ok", -1: "null pointer", -2: "unsupported shape", -3: "misaligned
 class GemmConfig(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("kwaves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("kwaves", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self) -> dict:
         return {"variant": "swapab" if self.variant == SWAPAB else "standard",
                 "tile_m": self.tile_m, "tile_n": self.tile_n,
-                "split_k": self.split_k, "kwaves": self.kwaves}
+                "split_k": self.split_k, "kwaves": self.kwaves, "stages": self.stages}
 
     def __repr__(self) -> str:
         return f"GemmConfig({self.as_dict()})"
 
 
-def make_config(variant: int, tile_m: int, tile_n: int, split_k: int = 1, kwaves: int = 1) -> GemmConfig:
+def make_config(variant: int, tile_m: int, tile_n: int, split_k: int = 1, kwaves: int = 1,
+                stages: int = 0) -> GemmConfig:
     c = GemmConfig()
-    c.variant, c.tile_m, c.tile_n, c.split_k, c.kwaves = variant, tile_m, tile_n, split_k, kwaves
+    c.variant, c.tile_m, c.tile_n, c.split_k, c.kwaves, c.stages = variant, tile_m, tile_n, split_k, kwaves, stages
     return c
 
 

@@ -23,11 +23,11 @@ int to_status(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HI
 
 int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   const int64_t kb = K / kG;
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
     if (c.reserved[i] != 0) return FP8BLK_ERR_BAD_CONFIG;
   if (c.split_k < 1 || c.split_k > 256 || c.split_k > kb) return FP8BLK_ERR_BAD_CONFIG;
   if (c.variant == FP8BLK_STANDARD) {
-    if (!fp8blk::standard_tile_supported(c.tile_m, c.tile_n)) return FP8BLK_ERR_BAD_CONFIG;
+    if (!fp8blk::standard_tile_supported(c.tile_m, c.tile_n, c.stages)) return FP8BLK_ERR_BAD_CONFIG;
     if (N % c.tile_n != 0) return FP8BLK_ERR_BAD_CONFIG;
     // one workgroup per (tile, split): the grid must fit a 32-bit count
     const int64_t blocks = ((M + c.tile_m - 1) / c.tile_m) * (N / c.tile_n) * c.split_k;
@@ -35,7 +35,8 @@ int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
     return FP8BLK_OK;
   }
   if (c.variant == FP8BLK_SWAPAB) {
-    if (!fp8blk::swapab_tile_supported(c.tile_m, c.tile_n, c.kwaves)) return FP8BLK_ERR_BAD_CONFIG;
+    if (!fp8blk::swapab_tile_supported(c.tile_m, c.tile_n, c.kwaves) || c.stages != 0)
+      return FP8BLK_ERR_BAD_CONFIG;
     if (M > c.tile_m) return FP8BLK_ERR_BAD_CONFIG;
     return FP8BLK_OK;
   }
@@ -211,7 +212,7 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   g.ws = need > 0 ? (float*)workspace : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
-    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, s));
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
 }
 
@@ -287,7 +288,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   g.sa = sc;
   g.lda = K;
   g.ldsa = K / kG;
-  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, s));
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, s));
 }
 
 }  // extern "C"

@@ -22,7 +22,8 @@ struct Entry {
   fp8blk_gemm_config cfg;
 };
 
-#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, {0, 0, 0}}
+#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, 0, {0, 0}}
+#define CFGS(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, {0, 0}}
 
 // Measured table (MI355X).  Entries are checked in order; the first bucket
 // containing M wins.

@@ -31,6 +31,8 @@
 //   * Split-K: grid x split_k; split s covers a contiguous range of K blocks
 //     and writes fp32 partials to the workspace [split][M][N]; a separate
 //     kernel sums them in split order.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -70,15 +72,70 @@ struct Shape {
   static_assert(SW_WAVE < WAVES, "one scale load per wave at most");
 };
 
-template <int BM, int BN, int WM, int WN, bool SPLIT>
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// f(ic<0>{}), ..., f(ic<N-1>{}) in order: every stage index is a constant.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(ic<N - 1>{});
+  }
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// NS LDS stages: the direct-to-LDS loads of K blocks kb+1 .. kb+NS-1 are in
+// flight while the matrix cores work on block kb.  Two stages suit the
+// MFMA-bound tiles; decode-sized problems, where each workgroup does little
+// work per K block and the loop would otherwise wait one memory latency per
+// block, use three or four.
+template <int BM, int BN, int WM, int WN, bool SPLIT, int NS>
 __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams p) {
   using S = Shape<BM, BN, WM, WN>;
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+  // separate objects per stage, so that the compiler sees that the stage
+  // being filled and the stage being read never alias
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a2[NS > 2 ? BM * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a3[NS > 3 ? BM * 128 : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[BN * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b2[NS > 2 ? BN * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b3[NS > 3 ? BN * 128 : 16];
   __shared__ __attribute__((aligned(256))) float lds_s0[S::S_FLOATS];
   __shared__ __attribute__((aligned(256))) float lds_s1[S::S_FLOATS];
+  __shared__ __attribute__((aligned(256))) float lds_s2[NS > 2 ? S::S_FLOATS : 4];
+  __shared__ __attribute__((aligned(256))) float lds_s3[NS > 3 ? S::S_FLOATS : 4];
+  auto stage_a = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(st)::value;
+    if constexpr (i == 0) return lds_a0;
+    else if constexpr (i == 1) return lds_a1;
+    else if constexpr (i == 2) return lds_a2;
+    else return lds_a3;
+  };
+  auto stage_b = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(st)::value;
+    if constexpr (i == 0) return lds_b0;
+    else if constexpr (i == 1) return lds_b1;
+    else if constexpr (i == 2) return lds_b2;
+    else return lds_b3;
+  };
+  auto stage_s = [&](auto st) __attribute__((always_inline)) -> float* {
+    constexpr int i = decltype(st)::value;
+    if constexpr (i == 0) return lds_s0;
+    else if constexpr (i == 1) return lds_s1;
+    else if constexpr (i == 2) return lds_s2;
+    else return lds_s3;
+  };
+  constexpr int PER = S::A_INSTR + S::B_INSTR + 1;  // direct-to-LDS instructions per wave and stage
 
   const GemmArgs& g = p.g;
   const int lane = threadIdx.x & 63;
@@ -136,7 +193,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const uint32_t sc_off = sa_wave ? sa_off : sw_off;
   const int sc_dst = sa_wave ? wave * 64 : BM;
 
-  auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) {
+  auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
     const uint8_t* ab = a_base + (int64_t)kb * 128;
     const uint8_t* bb = b_base + (int64_t)kb * 128;
 #pragma unroll
@@ -184,7 +241,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   v4f P[2][S::TN];
   float swv;
 
-  auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) {
+  auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
     swv = ls[sw_slot];
 #pragma unroll
     for (int j = 0; j < S::TN; ++j) {
@@ -199,7 +256,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // registers; afterwards refill that stage (ra, rb, rs) with block kb_refill
   // and read the first fragments of the next stage (na, nb, ns).
   auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
-                    int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns) {
+                    int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
@@ -229,9 +287,10 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // this wave's loads into the next stage have landed; after the barrier
-    // every wave's have, and nobody reads the stage just consumed any more
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // this wave's loads into the next stage have landed (the NS-2 younger
+    // stages may still be in flight); after the barrier every wave's have,
+    // and nobody reads the stage just consumed any more
+    wait_vmcnt<(NS - 2) * PER>();
     __syncthreads();
     issue(ra, rb, rs, kb_refill);
     read_first(na, nb, ns);
@@ -244,26 +303,37 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Stage 0 <- block kb0 (waited), stage 1 <- kb0+1 (in flight).  Two K
-  // blocks per trip so that every LDS buffer is a static object (the
-  // compiler then knows the stage being read and the stage being filled
-  // never alias and inserts no early wait); no branch inside a trip: block
-  // indices are clamped to the last block (re-loading it into an idle stage
-  // is harmless).  An empty K range (a trailing split) loads the last block
-  // and computes nothing.
+  // Stage s <- block kb0+s for every stage; stage 0 is waited for, the others
+  // stay in flight.  NS K blocks per trip so that every LDS buffer is a
+  // static object (the compiler then knows the stage being read and the
+  // stages being filled never alias and inserts no early wait); no branch
+  // inside a trip: block indices are clamped to the last block (re-loading it
+  // into an idle stage is harmless).  An empty K range (a trailing split)
+  // loads the last block and computes nothing.
   const int kblast = kb1 - 1;
-  issue(lds_a0, lds_b0, lds_s0, min(kb0, kblast));
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  static_for<NS>([&](auto st) __attribute__((always_inline)) {
+    issue(stage_a(st), stage_b(st), stage_s(st), min(kb0 + (int)decltype(st)::value, kblast));
+  });
+  wait_vmcnt<(NS - 1) * PER>();
   __syncthreads();
-  issue(lds_a1, lds_b1, lds_s1, min(kb0 + 1, kblast));
   read_first(lds_a0, lds_b0, lds_s0);
   int kb = kb0;
-  for (; kb + 1 < kb1; kb += 2) {
-    kblock(lds_a0, lds_s0, lds_a0, lds_b0, lds_s0, min(kb + 2, kblast), lds_a1, lds_b1, lds_s1);
-    kblock(lds_a1, lds_s1, lds_a1, lds_b1, lds_s1, min(kb + 3, kblast), lds_a0, lds_b0, lds_s0);
+  for (; kb + NS - 1 < kb1; kb += NS) {
+    static_for<NS>([&](auto st) __attribute__((always_inline)) {
+      constexpr int i = decltype(st)::value;
+      constexpr int nx = (i + 1) % NS;
+      kblock(stage_a(st), stage_s(st), stage_a(st), stage_b(st), stage_s(st), min(kb + i + NS, kblast),
+             stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+    });
   }
-  if (kb < kb1) kblock(lds_a0, lds_s0, lds_a0, lds_b0, lds_s0, kblast, lds_a1, lds_b1, lds_s1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  static_for<NS - 1>([&](auto st) __attribute__((always_inline)) {  // the remaining kb1 - kb < NS blocks
+    constexpr int i = decltype(st)::value;
+    constexpr int nx = (i + 1) % NS;
+    if (kb + i < kb1)
+      kblock(stage_a(st), stage_s(st), stage_a(st), stage_b(st), stage_s(st), kblast,
+             stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+  });
+  wait_vmcnt<0>();
 
   // ---- epilogue: lane holds rows orow..orow+3 and column frow of each tile ----
 #pragma unroll
@@ -284,7 +354,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 hipError_t run(const GemmArgs& g, int split_k, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   StdParams p;
@@ -296,33 +366,42 @@ hipError_t run(const GemmArgs& g, int split_k, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * split_k;
   p.remap = (blocks % kXcds == 0) ? 1 : 0;
   if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool standard_tile_supported(int tile_m, int tile_n) {
-  return (tile_m == 64 && tile_n == 128) || (tile_m == 128 && tile_n == 128) ||
-         (tile_m == 256 && tile_n == 128) || (tile_m == 128 && tile_n == 256) ||
-         (tile_m == 256 && tile_n == 256);
+// (tile_m, tile_n, LDS stages) combinations that are compiled; stages 0
+// means the default, 2.
+bool standard_tile_supported(int tile_m, int tile_n, int stages) {
+  const int ns = stages == 0 ? 2 : stages;
+  if (tile_m == 64 && tile_n == 128) return ns >= 2 && ns <= 4;
+  if (tile_m == 128 && tile_n == 128) return ns == 2 || ns == 3;
+  if (tile_m == 256 && tile_n == 128) return ns == 2 || ns == 3;
+  if (tile_m == 128 && tile_n == 256) return ns == 2;
+  if (tile_m == 256 && tile_n == 256) return ns == 2;
+  return false;
 }
 
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k,
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
                                 hipStream_t stream) {
+  const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
   if (tile_m == 64 && tile_n == 128)
-    e = run<64, 128, 32, 64>(g, split_k, stream);
+    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, stream)
+      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, stream)
+                : run<64, 128, 32, 64, 2>(g, split_k, stream);
   else if (tile_m == 128 && tile_n == 128)
-    e = run<128, 128, 64, 64>(g, split_k, stream);
+    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, stream) : run<128, 128, 64, 64, 2>(g, split_k, stream);
   else if (tile_m == 256 && tile_n == 128)
-    e = run<256, 128, 64, 64>(g, split_k, stream);
+    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, stream) : run<256, 128, 64, 64, 2>(g, split_k, stream);
   else if (tile_m == 128 && tile_n == 256)
-    e = run<128, 256, 64, 64>(g, split_k, stream);
+    e = run<128, 256, 64, 64, 2>(g, split_k, stream);
   else if (tile_m == 256 && tile_n == 256)
-    e = run<256, 256, 128, 64>(g, split_k, stream);
+    e = run<256, 256, 128, 64, 2>(g, split_k, stream);
   if (e != hipSuccess || split_k == 1) return e;
   return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
 }

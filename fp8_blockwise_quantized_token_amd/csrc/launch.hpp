@@ -37,9 +37,9 @@ struct GemmArgs {
   int ue8m0;
 };
 
-// Standard variant: (tile_m, tile_n) among the compiled tiles.
-bool standard_tile_supported(int tile_m, int tile_n);
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k,
+// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones.
+bool standard_tile_supported(int tile_m, int tile_n, int stages);
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
                                 hipStream_t stream);
 
 // Swap-AB variant.

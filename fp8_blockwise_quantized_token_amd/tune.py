@@ -57,6 +57,7 @@ def candidates(M: int, N: int, K: int):
                 for sk in (1, 2, 4, 8, 16):
                     if sk * kw <= kb:
                         out.append(fb.make_config(fb.SWAPAB, tm, tn, sk, kw))
+    stages = {(64, 128): (2, 3, 4), (128, 128): (2, 3), (256, 128): (2, 3), (128, 256): (2,), (256, 256): (2,)}
     for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
         if N % tn or (tm >= 128 and M <= 32):
             continue
@@ -64,7 +65,10 @@ def candidates(M: int, N: int, K: int):
         for sk in (1, 2, 4, 8):
             if sk > 1 and (tiles >= 512 or sk * 2 > kb):
                 continue
-            out.append(fb.make_config(fb.STANDARD, tm, tn, sk))
+            for ns in stages[(tm, tn)]:
+                if ns > 2 and (tiles * sk >= 2048 or kb // sk < ns):
+                    continue  # deep pipelines are for few, short K loops
+                out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, 0 if ns == 2 else ns))
     return out
 
 
@@ -179,8 +183,8 @@ def write_table(path: str, out_inc: str) -> None:
              "// by fp8_blockwise_quantized_token_amd/tune.py (HIP-graph replay, weights",
              f"// rotated past the Infinity Cache; timed call: {data.get('op', 'gemm')}).",
              "// Entry: {N, K, M_lo, M_hi,",
-             "// CFG(variant, tile_m, tile_n, split_k, kwaves)}; the first bucket",
-             "// containing M wins.",
+             "// CFG(variant, tile_m, tile_n, split_k, kwaves) or CFGS(..., stages)};",
+             "// the first bucket containing M wins.",
              "static const Entry kTable[] = {"]
     for (N, K), ents in sorted(by_shape.items()):
         ents.sort(key=lambda e: e["M"])
@@ -191,8 +195,10 @@ def write_table(path: str, out_inc: str) -> None:
             hi = e["M"]
             if e is ents[-1]:
                 hi = 2147483647 if b["variant"] == "standard" else e["M"]
-            lines.append(f"    {{{N}, {K}, {lo + 1}, {hi}, CFG({var}, {b['tile_m']}, {b['tile_n']}, "
-                         f"{b['split_k']}, {b['kwaves']})}},  // {e['best_us']:.2f} us at M={e['M']}")
+            ns = b.get("stages", 0)
+            cfg = (f"CFG({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']})" if ns == 0 else
+                   f"CFGS({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})")
+            lines.append(f"    {{{N}, {K}, {lo + 1}, {hi}, {cfg}}},  // {e['best_us']:.2f} us at M={e['M']}")
             lo = e["M"]
     lines.append("};")
     with open(out_inc, "w") as f:

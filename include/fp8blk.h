@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 1
+#define FP8BLK_ABI_VERSION 2
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
 
@@ -76,11 +76,15 @@ extern "C" {
  * are divided among split_k groups of workgroups, each writing an fp32
  * partial product to the workspace, then a second kernel sums the partials
  * in a fixed order and writes bf16 (deterministic, no atomics).
- *   STANDARD: tile_m in {64, 128, 256}, tile_n in {128, 256}.
+ *   STANDARD: tile_m in {64, 128, 256}, tile_n in {128, 256}; stages = LDS
+ *             pipeline depth (K blocks staged ahead): 0 (default, = 2) or
+ *             2..4 where compiled (64x128: 2-4; 128x128, 256x128: 2-3;
+ *             others: 2).  Deeper pipelines hide memory latency in
+ *             decode-sized problems.
  *   SWAPAB:   tile_m (tokens per workgroup) in {16, 32, 64} and >= M,
  *             tile_n (weight rows per workgroup) in {16, 32, 64},
  *             kwaves (waves sharing one tile, each on its own K range,
- *             summed in the workgroup) in {1, 2, 4, 8}.
+ *             summed in the workgroup) in {1, 2, 4, 8}; stages must be 0.
  *   split_k: 1 .. min(256, K/128). */
 typedef struct fp8blk_gemm_config {
     int32_t variant;
@@ -88,7 +92,8 @@ typedef struct fp8blk_gemm_config {
     int32_t tile_n;
     int32_t split_k;
     int32_t kwaves;
-    int32_t reserved[3]; /* must be 0 */
+    int32_t stages;
+    int32_t reserved[2]; /* must be 0 */
 } fp8blk_gemm_config;
 
 /* Library ABI version (FP8BLK_ABI_VERSION of the build). */

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fb.fp8_abi_version() == 1
+    assert fb.fp8_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert fb.fp8_status_string(st) != "unknown status"
     assert fb.fp8_status_string(-99) == "unknown status"
@@ -131,6 +131,12 @@ def test_gemm_argument_errors():
     bad = fb.make_config(fb.STANDARD, 128, 128)
     bad.reserved[1] = 5
     assert _gemm(cfg=bad) == CFG
+    # LDS pipeline depth: compiled per tile; Swap-AB takes none
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 256, 256, stages=3)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, stages=4)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 64, 128, stages=5)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 64, 128, stages=1)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, stages=2)) == CFG
     # split-K needs a workspace of split * M * N * 4 bytes
     sk = fb.make_config(fb.STANDARD, 128, 128, split_k=2)
     assert fb.fp8_block_gemm_workspace_size(8, 256, 256, sk) == 2 * 8 * 256 * 4

@@ -29,6 +29,13 @@ def _configs(M, N, K):
         for sk in (1, 2, 3):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk))
+    # deeper LDS pipelines (3 and 4 stages), with and without split-K
+    for tm, tn, ns in ((64, 128, 3), (64, 128, 4), (128, 128, 3), (256, 128, 3)):
+        if N % tn:
+            continue
+        for sk in (1, 3):
+            if sk <= kb:
+                out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, ns))
     for tm in (16, 32, 64):
         if M > tm:
             continue
