@@ -56,8 +56,9 @@ int64_t workspace_for(const fp8blk_gemm_config& c, int64_t M, int64_t N) {
 
 int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 
-// fp8_linear's workspace: Swap-AB quantizes in the GEMM and needs only the
-// split-K partials; the other variants first quantize into the workspace:
+// fp8_linear's workspace: Swap-AB with up to two token tiles (tile_m <= 32)
+// quantizes in the GEMM and needs only the split-K partials; the other
+// configurations first quantize into the workspace:
 // [q: M x K bytes][s: M x K/128 floats][split-K partials], each 256-aligned.
 struct LinearLayout {
   bool fused;
@@ -66,7 +67,7 @@ struct LinearLayout {
 
 LinearLayout linear_layout(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   LinearLayout L;
-  L.fused = c.variant == FP8BLK_SWAPAB;
+  L.fused = c.variant == FP8BLK_SWAPAB && c.tile_m <= 32;
   const int64_t split = workspace_for(c, M, N);
   if (L.fused) {
     L.q_off = L.s_off = L.ws_off = 0;
@@ -288,6 +289,8 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   g.sa = sc;
   g.lda = K;
   g.ldsa = K / kG;
+  if (c.variant == FP8BLK_SWAPAB)
+    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
   return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, s));
 }
 

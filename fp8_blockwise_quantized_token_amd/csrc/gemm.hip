@@ -403,13 +403,16 @@ hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stre
   dim3 grid((unsigned)(g.N / (16 * RN)), (unsigned)split_k);
   const bool sp = split_k > 1;
   if (g.x == nullptr) return run_swap3<TOKT, RN, 0>(p, grid, kwaves, sp, stream);
-  if (TOKT == 1) {  // quantize only the tokens that can be valid
-    if (g.M <= 1) return run_swap3<TOKT, RN, TOKT == 1 ? 1 : 16>(p, grid, kwaves, sp, stream);
-    if (g.M <= 2) return run_swap3<TOKT, RN, TOKT == 1 ? 2 : 16>(p, grid, kwaves, sp, stream);
-    if (g.M <= 4) return run_swap3<TOKT, RN, TOKT == 1 ? 4 : 16>(p, grid, kwaves, sp, stream);
-    if (g.M <= 8) return run_swap3<TOKT, RN, TOKT == 1 ? 8 : 16>(p, grid, kwaves, sp, stream);
+  if constexpr (TOKT == 1) {  // fused: quantize only the tokens that can be valid
+    if (g.M <= 1) return run_swap3<TOKT, RN, 1>(p, grid, kwaves, sp, stream);
+    if (g.M <= 2) return run_swap3<TOKT, RN, 2>(p, grid, kwaves, sp, stream);
+    if (g.M <= 4) return run_swap3<TOKT, RN, 4>(p, grid, kwaves, sp, stream);
+    if (g.M <= 8) return run_swap3<TOKT, RN, 8>(p, grid, kwaves, sp, stream);
+    return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
+  } else if constexpr (TOKT == 2) {
+    return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
   }
-  return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
+  return hipErrorInvalidValue;  // the fused path serves up to two token tiles (M <= 32)
 }
 
 }  // namespace

@@ -193,20 +193,21 @@ int fp8_block_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
  * CustomOps", the SM120 benchmark comment), and the pages count kernel
  * launches per forward pass as the cost fusion cuts (page "Helion-Kernel in
  * vLLM", section "Welche Kernel wurden in vLLM integriert").
- *   SWAPAB configurations (the small-M choice of the dispatcher) quantize
- *   each 1x128 group of x inside the GEMM's operand load: one kernel (plus
- *   the split-K sum), and no fp8 copy of x is written.  Codes and scales are
- *   the ones fp8_group_quant would produce, bit for bit.
- *   STANDARD configurations run fp8_group_quant into the workspace, then the
- *   GEMM.
+ *   SWAPAB configurations with tile_m <= 32 (M <= 32, the small-M choices
+ *   of the dispatcher) quantize each 1x128 group of x inside the GEMM's
+ *   operand load: one kernel (plus the split-K sum), and no fp8 copy of x is
+ *   written.  Codes and scales are the ones fp8_group_quant would produce,
+ *   bit for bit.  Other configurations run fp8_group_quant into the
+ *   workspace, then the GEMM.
  *   x  bf16 [M][ldx], ldx >= K            w, sw, y, ldw, ldsw, ldy as in
  *                                           fp8_block_gemm
  *   eps, flags as in fp8_group_quant (flags: FP8BLK_FLAG_UE8M0 or 0).
  *   cfg NULL selects through fp8_block_gemm_select.
  *   workspace: device buffer of at least fp8_linear_workspace_size bytes,
  *   16-byte aligned (may be NULL when that is 0); concurrent calls must not
- *   share one.  Layout (STANDARD): fp8 x [M][K], then its scales
- *   [M][K/128], then the split-K partials, each at a 256-byte boundary.
+ *   share one.  Layout: fp8 x [M][K] and its scales [M][K/128] (unless the
+ *   quantizer is fused), then the split-K partials, each at a 256-byte
+ *   boundary.
  * Requires K % 128 == 0, K <= 2^22, N % 128 == 0, M >= 0.
  */
 int64_t fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K,

@@ -202,8 +202,11 @@ def test_linear_argument_errors():
     assert _lin(x=A + 2, cfg=sw1) == MISAL
     assert _lin(ldx=260, cfg=sw1) == MISAL
     assert _lin(M=40, cfg=sw1) == CFG  # Swap-AB tile_m < M
-    # Swap-AB quantizes in the GEMM: workspace only for split-K partials
+    # Swap-AB with one token tile quantizes in the GEMM: workspace only for split-K partials
     assert fb.fp8_linear_workspace_size(8, 256, 256, sw1) == 0
+    # four token tiles quantize first: q [M][K] and s [M][K/128], each padded to 256 bytes
+    assert fb.fp8_linear_workspace_size(20, 256, 256, fb.make_config(fb.SWAPAB, 32, 16, 1, 2)) == 0
+    assert fb.fp8_linear_workspace_size(40, 256, 256, fb.make_config(fb.SWAPAB, 64, 16, 1, 2)) == 40 * 256 + 512
     sk = fb.make_config(fb.SWAPAB, 16, 16, 2, 1)
     assert fb.fp8_linear_workspace_size(8, 256, 256, sk) == 2 * 8 * 256 * 4
     assert _lin(cfg=sk) == WS

@@ -69,16 +69,18 @@ def test_every_config_equals_separate_quant_and_gemm(M, N, K):
 
 
 def test_ue8m0_and_distributions():
-    M, N, K = 24, 512, 768
+    N, K = 512, 768
     qw, sw = oracle_weight(N, K, True)
-    for dist in ("normal", "normal_outlier", "student_t3"):
-        x = _x(M, K, dist, key=3)
-        qa_ref, sa_ref = oracle.group_quant(x, ue8m0=True)
-        ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
-        for cfg in (fb.make_config(fb.SWAPAB, 32, 16, 1, 2), fb.make_config(fb.SWAPAB, 32, 32, 2, 1)):
-            y1, y2 = _two_paths(to_dev_bf16(x), to_dev(qw), to_dev(sw), cfg, ue8m0=True)
-            assert np.array_equal(y1, y2), f"{dist} {cfg}"
-            assert_close(y1, ref, f"{dist} {cfg}")
+    for M in (3, 12, 24, 40):  # lean fused, full fused (1 and 2 token tiles), separate quantizer
+        tm = 16 if M <= 16 else (32 if M <= 32 else 64)
+        for dist in ("normal", "normal_outlier", "student_t3"):
+            x = _x(M, K, dist, key=3)
+            qa_ref, sa_ref = oracle.group_quant(x, ue8m0=True)
+            ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
+            for cfg in (fb.make_config(fb.SWAPAB, tm, 16, 1, 2), fb.make_config(fb.SWAPAB, tm, 32, 2, 1)):
+                y1, y2 = _two_paths(to_dev_bf16(x), to_dev(qw), to_dev(sw), cfg, ue8m0=True)
+                assert np.array_equal(y1, y2), f"M={M} {dist} {cfg}"
+                assert_close(y1, ref, f"M={M} {dist} {cfg}")
 
 
 def test_degenerate_groups():
