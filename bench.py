@@ -65,7 +65,8 @@ def kernel_symbol(cfg, fused: bool = False, M: int = 0) -> str:
     b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
-        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}>"
+        return (f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}, "
+                f"{b(cfg.scale_mode == 1)}>")
     fq = 0
     if fused:  # the fused quantizer variant the launcher picks for this M
         fq = 16 if cfg.tile_m > 16 or M > 8 else (1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8)
@@ -199,7 +200,7 @@ def main() -> int:
         qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
         sa = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
-        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K)
+        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, fb.FLAG_UE8M0 if c.ue8m0 else 0)
         ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]

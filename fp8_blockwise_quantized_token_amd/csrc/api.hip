@@ -23,8 +23,9 @@ int to_status(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HI
 
 int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   const int64_t kb = K / kG;
-  for (int i = 0; i < 2; ++i)
-    if (c.reserved[i] != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.reserved[0] != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.scale_mode != FP8BLK_SCALES_FP32 && c.scale_mode != FP8BLK_SCALES_POW2) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.scale_mode == FP8BLK_SCALES_POW2 && c.variant != FP8BLK_STANDARD) return FP8BLK_ERR_BAD_CONFIG;
   if (c.split_k < 1 || c.split_k > 256 || c.split_k > kb) return FP8BLK_ERR_BAD_CONFIG;
   if (c.variant == FP8BLK_STANDARD) {
     if (!fp8blk::standard_tile_supported(c.tile_m, c.tile_n, c.stages)) return FP8BLK_ERR_BAD_CONFIG;
@@ -213,7 +214,8 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   g.ws = need > 0 ? (float*)workspace : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
-    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, s));
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
+                                                  c.scale_mode == FP8BLK_SCALES_POW2, s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
 }
 
@@ -245,7 +247,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   if (cfg) {
     c = *cfg;
   } else {
-    fp8blk::select_config(M, N, K, 0, &c);
+    fp8blk::select_config(M, N, K, flags, &c);
   }
   st = check_config(c, M, N, K);
   if (st != FP8BLK_OK) return st;
@@ -291,7 +293,8 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   g.ldsa = K / kG;
   if (c.variant == FP8BLK_SWAPAB)
     return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
-  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, s));
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
+                                                c.scale_mode == FP8BLK_SCALES_POW2, s));
 }
 
 }  // extern "C"

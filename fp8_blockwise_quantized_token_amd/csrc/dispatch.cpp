@@ -22,8 +22,8 @@ struct Entry {
   fp8blk_gemm_config cfg;
 };
 
-#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, 0, {0, 0}}
-#define CFGS(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, {0, 0}}
+#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, 0, 0, {0}}
+#define CFGS(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, 0, {0}}
 
 // Measured table (MI355X).  Entries are checked in order; the first bucket
 // containing M wins.
@@ -75,14 +75,18 @@ void heuristic(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* c) {
 }  // namespace
 
 void select_config(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8blk_gemm_config* out) {
-  (void)flags;
+  bool found = false;
   for (const Entry& e : kTable) {
     if (e.n == N && e.k == K && M >= e.m_lo && M <= e.m_hi) {
       *out = e.cfg;
-      return;
+      found = true;
+      break;
     }
   }
-  heuristic(M, N, K, out);
+  if (!found) heuristic(M, N, K, out);
+  // UE8M0 scales are powers of two: the Standard kernels apply them in the
+  // matrix core (v_mfma_scale) instead of one VALU rescale per K block.
+  if ((flags & FP8BLK_FLAG_UE8M0) && out->variant == FP8BLK_STANDARD) out->scale_mode = FP8BLK_SCALES_POW2;
 }
 
 }  // namespace fp8blk

@@ -96,7 +96,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // MFMA-bound tiles; decode-sized problems, where each workgroup does little
 // work per K block and the loop would otherwise wait one memory latency per
 // block, use three or four.
-template <int BM, int BN, int WM, int WN, bool SPLIT, int NS>
+//
+// P2 (power-of-two scales, the UE8M0 mode): every sa and sw is 2^e, so the
+// K-block scaling is exact in the matrix core itself:
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes an E8M0 exponent per A row (lane
+// l & 15; the same for the lane's four 32-wide K sub-blocks) and per B
+// column, multiplies the block product by 2^(ea + eb - 254) and accumulates
+// into the fp32 tile directly.  No VALU rescale and no product registers.
+template <int BM, int BN, int WM, int WN, bool SPLIT, int NS, bool P2>
 __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams p) {
   using S = Shape<BM, BN, WM, WN>;
   static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
@@ -240,6 +247,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   v4f gq[2];    // factors sa * sw of the rows in flight
   v4f P[2][S::TN];
   float swv;
+  uint32_t ea[S::TM];  // P2: E8M0 exponents of sa for row frow of each tile row
+  const int erow = wave_m * WM + frow;
 
   auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
     swv = ls[sw_slot];
@@ -249,7 +258,12 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
     }
     af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
-    scl = *(const v4f*)(ls + srow);
+    if constexpr (P2) {
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i) ea[i] = __float_as_uint(ls[erow + i * 16]) >> 23;
+    } else {
+      scl = *(const v4f*)(ls + srow);
+    }
   };
 
   // One K block from the stage (la, ls) whose first fragments are already in
@@ -258,6 +272,27 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
                     int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns)
                     __attribute__((always_inline)) {
+    if constexpr (P2) {
+      const uint32_t eb = __float_as_uint(swv) >> 23;  // this wave's 128 columns share sw
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i) {
+        const int cur = i & 1, prv = cur ^ 1;
+        if (i + 1 < S::TM)
+          af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
+                             *(const u32x4*)(la + a_hi + (i + 1) * 2048));
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
+                                                                       (int)ea[i], 0, (int)eb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vmcnt<(NS - 2) * PER>();
+      __syncthreads();
+      issue(ra, rb, rs, kb_refill);
+      read_first(na, nb, ns);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
@@ -354,8 +389,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
-hipError_t run(const GemmArgs& g, int split_k, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int NS, bool P2>
+hipError_t run_p(const GemmArgs& g, int split_k, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   StdParams p;
   p.g = g;
@@ -366,10 +401,16 @@ hipError_t run(const GemmArgs& g, int split_k, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * split_k;
   p.remap = (blocks % kXcds == 0) ? 1 : 0;
   if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS, P2>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS, P2>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t run(const GemmArgs& g, int split_k, bool pow2, hipStream_t stream) {
+  return pow2 ? run_p<BM, BN, WM, WN, NS, true>(g, split_k, stream)
+              : run_p<BM, BN, WM, WN, NS, false>(g, split_k, stream);
 }
 
 }  // namespace
@@ -387,21 +428,21 @@ bool standard_tile_supported(int tile_m, int tile_n, int stages) {
 }
 
 hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                hipStream_t stream) {
+                                bool pow2, hipStream_t stream) {
   const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
   if (tile_m == 64 && tile_n == 128)
-    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, stream)
-      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, stream)
-                : run<64, 128, 32, 64, 2>(g, split_k, stream);
+    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, pow2, stream)
+      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, pow2, stream)
+                : run<64, 128, 32, 64, 2>(g, split_k, pow2, stream);
   else if (tile_m == 128 && tile_n == 128)
-    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, stream) : run<128, 128, 64, 64, 2>(g, split_k, stream);
+    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, pow2, stream) : run<128, 128, 64, 64, 2>(g, split_k, pow2, stream);
   else if (tile_m == 256 && tile_n == 128)
-    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, stream) : run<256, 128, 64, 64, 2>(g, split_k, stream);
+    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, pow2, stream) : run<256, 128, 64, 64, 2>(g, split_k, pow2, stream);
   else if (tile_m == 128 && tile_n == 256)
-    e = run<128, 256, 64, 64, 2>(g, split_k, stream);
+    e = run<128, 256, 64, 64, 2>(g, split_k, pow2, stream);
   else if (tile_m == 256 && tile_n == 256)
-    e = run<256, 256, 128, 64, 2>(g, split_k, stream);
+    e = run<256, 256, 128, 64, 2>(g, split_k, pow2, stream);
   if (e != hipSuccess || split_k == 1) return e;
   return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
 }

@@ -37,10 +37,11 @@ struct GemmArgs {
   int ue8m0;
 };
 
-// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones.
+// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones;
+// pow2: every scale is a power of two and the matrix core applies them.
 bool standard_tile_supported(int tile_m, int tile_n, int stages);
 hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                hipStream_t stream);
+                                bool pow2, hipStream_t stream);
 
 // Swap-AB variant.
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);

@@ -67,6 +67,12 @@ extern "C" {
                                 vLLM", section "Praktische Einschränkungen";
                                 RFC page, H100 end-to-end settings */
 
+/* How the GEMM applies the K-block scales (fp8blk_gemm_config.scale_mode) */
+#define FP8BLK_SCALES_FP32 0 /* any fp32 scales: one fp32 rescale per K block */
+#define FP8BLK_SCALES_POW2 1 /* every sa and sw is a power of two (UE8M0):
+                                applied exactly by the matrix core (STANDARD
+                                only; results unspecified for other scales) */
+
 /* GEMM variants (autotuning page, section "Kernel Implementation") */
 #define FP8BLK_STANDARD 0 /* tiles over (M, N), loop over K */
 #define FP8BLK_SWAPAB 1   /* computes (W A^T)^T: weight rows on the matrix-core
@@ -93,7 +99,8 @@ typedef struct fp8blk_gemm_config {
     int32_t split_k;
     int32_t kwaves;
     int32_t stages;
-    int32_t reserved[2]; /* must be 0 */
+    int32_t scale_mode;  /* FP8BLK_SCALES_FP32 or FP8BLK_SCALES_POW2 */
+    int32_t reserved[1]; /* must be 0 */
 } fp8blk_gemm_config;
 
 /* Library ABI version (FP8BLK_ABI_VERSION of the build). */
@@ -149,7 +156,9 @@ int fp8_e4m3_encode(const float *t, uint8_t *q, int64_t n, void *stream);
  * Per-shape dispatch: the configuration fp8_block_gemm uses when cfg is NULL.
  * A table tuned on MI355X keyed on (N, K) and a bucket of M, with a
  * heuristic for shapes not in the table (autotuning page, "Hybrid Dispatch"
- * and "Per-shape Config Tuning").  Deterministic, host-only, O(1).
+ * and "Per-shape Config Tuning").  With FP8BLK_FLAG_UE8M0 in flags (the
+ * caller guarantees power-of-two scales) STANDARD choices get
+ * scale_mode = FP8BLK_SCALES_POW2.  Deterministic, host-only.
  * Returns FP8BLK_OK or FP8BLK_ERR_BAD_SHAPE / FP8BLK_ERR_NULL_PTR.
  */
 int fp8_block_gemm_select(int64_t M, int64_t N, int64_t K, uint32_t flags,
@@ -173,7 +182,9 @@ int64_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
  *   a  uint8 e4m3fn [M][lda], lda >= K      sa fp32 [M][ldsa], ldsa >= K/128
  *   w  uint8 e4m3fn [N][ldw], ldw >= K      sw fp32 [N/128][ldsw], ldsw >= K/128
  *   y  bf16 [M][ldy], ldy >= N
- *   cfg NULL selects through fp8_block_gemm_select.
+ *   cfg NULL selects through fp8_block_gemm_select (flags 0: fp32 scale
+ *   mode; pass a configuration from fp8_block_gemm_select(..., UE8M0, ...)
+ *   to use the power-of-two mode).
  *   workspace: device buffer of at least fp8_block_gemm_workspace_size bytes
  *   (may be NULL when that is 0).  Concurrent calls must not share one.
  * Requires K % 128 == 0, N % 128 == 0, M >= 0.

@@ -129,8 +129,11 @@ def test_gemm_argument_errors():
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 3)) == CFG         # kwaves
     assert _gemm(M=40, cfg=fb.make_config(fb.SWAPAB, 32, 16, 1, 4)) == CFG   # M > tile_m
     bad = fb.make_config(fb.STANDARD, 128, 128)
-    bad.reserved[1] = 5
+    bad.reserved[0] = 5
     assert _gemm(cfg=bad) == CFG
+    # scale modes: fp32 or power-of-two (Standard only)
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=2)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, scale_mode=fb.SCALES_POW2)) == CFG
     # LDS pipeline depth: compiled per tile; Swap-AB takes none
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 256, 256, stages=3)) == CFG
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, stages=4)) == CFG
@@ -161,6 +164,19 @@ def test_select_and_workspace_queries():
             if c.variant == fb.SWAPAB:
                 assert case.M <= c.tile_m
             assert 1 <= c.split_k <= case.K // 128
+
+
+def test_select_ue8m0_flag_sets_power_of_two_mode():
+    for config in ("prefill_8b", "ue8m0_32b", "decode_8b"):
+        for case in synth.cases(config):
+            plain = fb.fp8_block_gemm_select(case.M, case.N, case.K, 0)
+            p2 = fb.fp8_block_gemm_select(case.M, case.N, case.K, fb.FLAG_UE8M0)
+            assert plain.scale_mode == fb.SCALES_FP32
+            want = fb.SCALES_POW2 if plain.variant == fb.STANDARD else fb.SCALES_FP32
+            assert p2.scale_mode == want
+            d1, d2 = plain.as_dict(), p2.as_dict()
+            d1.pop("scale_mode"), d2.pop("scale_mode")
+            assert d1 == d2
 
 
 def test_select_is_deterministic_and_swaps_small_m():

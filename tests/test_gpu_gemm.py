@@ -207,3 +207,56 @@ def test_hip_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(y), eager), f"replay {i}"
+
+
+def _pow2_configs(N, K):
+    kb = K // 128
+    out = []
+    for tm, tn, ns in ((64, 128, 0), (64, 128, 4), (128, 128, 0), (128, 128, 3), (256, 128, 0),
+                       (256, 128, 3), (128, 256, 0), (256, 256, 0)):
+        if N % tn:
+            continue
+        for sk in (1, 2):
+            if sk <= kb:
+                out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, ns, fb.SCALES_POW2))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (100, 256, 512), (257, 512, 384), (300, 768, 896)],
+                         ids=lambda v: str(v))
+def test_power_of_two_scale_mode_against_oracle(M, N, K):
+    """UE8M0 inputs (every scale a power of two) through the matrix-core
+    scaling path, against the oracle and against the fp32-scale path."""
+    x = synth.activations_bf16(synth.Case("ue8m0_32b", "p2", M, N, K, "student_t3", True, 40 + M))
+    qa, sa = oracle.group_quant(x, ue8m0=True)
+    qw, sw = oracle_weight(N, K, True)
+    assert np.all(np.frexp(sa)[0] == 0.5) and np.all(np.frexp(sw)[0] == 0.5)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    base = _run(qa, sa, qw, sw, fb.make_config(fb.STANDARD, 64, 128, 1))
+    for cfg in _pow2_configs(N, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        assert_close(y, ref, str(cfg))
+        assert_close(y, base, f"{cfg} vs fp32-scale path")
+
+
+def test_power_of_two_scale_mode_exact_cases():
+    # closed form with geometric activation scales 2^kb: 128 (2^(K/128) - 1)
+    M, N, K = 20, 256, 512
+    qa = np.full((M, K), 0x38, np.uint8)
+    qw = np.full((N, K), 0x38, np.uint8)
+    sa = np.tile((2.0 ** np.arange(K // 128)).astype(np.float32), (M, 1))
+    sw = np.ones((N // 128, K // 128), np.float32)
+    for cfg in _pow2_configs(N, K):
+        assert np.all(_run(qa, sa, qw, sw, cfg) == 1920.0), str(cfg)
+    # integer-exact operands: every path gives the same bits
+    ints = {0x38: 1, 0x40: 2, 0x44: 3, 0x48: 4, 0xB8: -1, 0xC0: -2, 0x00: 0, 0x50: 8}
+    codes = np.array(list(ints), dtype=np.uint8)
+    rng = synth.generator(703)
+    M, N, K = 64, 512, 1024
+    qa = rng.choice(codes, size=(M, K)).astype(np.uint8)
+    qw = rng.choice(codes, size=(N, K)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-3, 4, size=(M, K // 128))).astype(np.float32)
+    sw = (2.0 ** rng.integers(-3, 4, size=(N // 128, K // 128))).astype(np.float32)
+    first = _run(qa, sa, qw, sw, fb.make_config(fb.STANDARD, 64, 128, 1))
+    for cfg in _pow2_configs(N, K):
+        assert np.array_equal(_run(qa, sa, qw, sw, cfg), first), str(cfg)

@@ -179,3 +179,21 @@ def test_graph_replay_of_fused_linear():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(y), eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("case", [c for c in synth.cases("ue8m0_32b")], ids=lambda c: c.cid)
+def test_full_size_ue8m0_linear_dispatched(case):
+    """The UE8M0 layers through fp8_linear with the UE8M0 flag (Standard
+    configurations then scale in the matrix core), against the oracle on
+    sampled rows."""
+    import torch
+    x = synth.activations_bf16(case)
+    qw, sw = oracle_weight(case.N, case.K, True)
+    cfg = fb.fp8_block_gemm_select(case.M, case.N, case.K, fb.FLAG_UE8M0)
+    say("ue8m0 linear", case.cid, cfg.as_dict())
+    y = fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(case.M, 8)
+    qa_ref, sa_ref = oracle.group_quant(x[rows], ue8m0=True)
+    ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
+    assert_close(host(y)[rows].astype(np.float64), ref, case.cid)
