@@ -205,7 +205,7 @@ def main() -> int:
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
         bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, lws=lws, qw=qw, sw=sw,
-                         fused=cfg.variant == fb.SWAPAB))
+                         fused=cfg.variant == fb.SWAPAB and cfg.tile_m <= 32))
     torch.cuda.synchronize()
 
     def linear(b):
