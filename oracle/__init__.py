@@ -59,6 +59,12 @@ def _load():
     lib.orc_weight_block_quant_mt.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int]
     lib.orc_block_gemm.restype = ctypes.c_int
     lib.orc_block_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
+    lib.orc_token_quant_mt.restype = ctypes.c_int
+    lib.orc_token_quant_mt.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_float, ctypes.c_int, ctypes.c_int]
+    lib.orc_channel_quant.restype = None
+    lib.orc_channel_quant.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_scaled_mm.restype = ctypes.c_int
+    lib.orc_scaled_mm.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -156,6 +162,56 @@ def block_gemm(qa, sa, qw, sw, rows=None, nthreads: int | None = None) -> np.nda
     if nrows:
         lib.orc_block_gemm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
                            rows_ptr, nrows, _ptr(y), nthreads or default_threads())
+    return y
+
+
+def token_quant(x_bf16_bits: np.ndarray, eps=DEFAULT_EPS, ue8m0: bool = False,
+                nthreads: int | None = None):
+    """dynamic_per_token_scaled_fp8_quant (FP8_Dynamic activations) of bf16
+    X [M, K]: one scale per row.  Returns (q uint8 [M, K], s float32 [M])."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M,), dtype=np.float32)
+    lib.orc_token_quant_mt(_ptr(x), M, K, K, _ptr(q), K, _ptr(s), float(np.float32(eps)),
+                           int(ue8m0), nthreads or default_threads())
+    return q, s
+
+
+def channel_quant(w: np.ndarray, eps=DEFAULT_EPS, ue8m0: bool = False):
+    """Per-channel (per row of W [N, K]) quantization of fp32 weights (FP8_Dynamic
+    weights).  Returns (q uint8 [N, K], s float32 [N])."""
+    lib = _load()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((N,), dtype=np.float32)
+    lib.orc_channel_quant(_ptr(w), N, K, _ptr(q), _ptr(s), float(np.float32(eps)), int(ue8m0))
+    return q, s
+
+
+def scaled_mm(qa, sa, qw, sw, rows=None, nthreads: int | None = None) -> np.ndarray:
+    """fp64 scaled_mm with per-token sa [M] and per-channel sw [N]:
+    Y = (dec(A) * sa[:, None]) @ (dec(W) * sw[:, None])^T.  Float64 [rows, N]."""
+    lib = _load()
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = qa.shape
+    N, K2 = qw.shape
+    assert K == K2 and sa.shape == (M,) and sw.shape == (N,)
+    if rows is None:
+        nrows, rows_ptr = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows_arr.size == 0 or (rows_arr.min() >= 0 and rows_arr.max() < M)
+        nrows, rows_ptr = rows_arr.size, _ptr(rows_arr)
+    y = np.empty((nrows, N), dtype=np.float64)
+    if nrows:
+        lib.orc_scaled_mm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, rows_ptr, nrows,
+                          _ptr(y), nthreads or default_threads())
     return y
 
 

@@ -22,6 +22,14 @@
  *     plain GEMM of the "Kernel Implementation" section of the autotuning
  *     page, plus the quantization scales.
  *
+ *   - "FP8_Dynamic": FP8 with per-token activation scaling and per-channel
+ *     weight scaling (same page and section as Block_FP8).  Its activation
+ *     quantizer is dynamic_per_token_scaled_fp8_quant and its GEMM scaled_mm
+ *     (both among the nine kernels of the German page, section "Welche
+ *     Kernel wurden in vLLM integriert").  Here: one scale per row of X (the
+ *     group is the whole row) and one per row of W, the same amax / scale /
+ *     encode rule as the group quantizer.
+ *
  * The pages do not print the e4m3fn bit layout, the rounding mode, the
  * saturation rule, the all-zero-group rule or the scale layouts.  The
  * readings taken here (OCP e4m3fn, round to nearest with ties to even,
@@ -183,6 +191,46 @@ void orc_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
 }
 
 /* ------------------------------------------------------------------ */
+/* per-token and per-channel quantizers (FP8_Dynamic)                  */
+/* ------------------------------------------------------------------ */
+
+/* One row of n values, already converted to float: amax over the row,
+ * scale, then every value encoded with that scale. */
+static float quantize_row(const float *v, int64_t n, uint8_t *q, float eps, int ue8m0)
+{
+    float amax = 0.0f;
+    for (int64_t j = 0; j < n; ++j)
+        if (fabsf(v[j]) > amax)
+            amax = fabsf(v[j]);
+    float sc = orc_scale_from_amax(amax, eps, ue8m0);
+    for (int64_t j = 0; j < n; ++j)
+        q[j] = quantize_one(v[j], sc);
+    return sc;
+}
+
+/* dynamic_per_token_scaled_fp8_quant: x bf16 bits [M][ldx] -> q [M][ldq],
+ * s [M] (one scale per token, over all K values of its row). */
+void orc_token_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                     uint8_t *q, int64_t ldq, float *s, float eps, int ue8m0)
+{
+    float *v = (float *)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            v[k] = bf16_value(x[m * ldx + k]);
+        s[m] = quantize_row(v, K, q + m * ldq, eps, ue8m0);
+    }
+    free(v);
+}
+
+/* Per-channel weight quantization: w fp32 [N][K] -> q [N][K], s [N]. */
+void orc_channel_quant(const float *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                       float eps, int ue8m0)
+{
+    for (int64_t n = 0; n < N; ++n)
+        s[n] = quantize_row(w + n * K, K, q + n * K, eps, ue8m0);
+}
+
+/* ------------------------------------------------------------------ */
 /* 128x128 weight block quantizer                                      */
 /* ------------------------------------------------------------------ */
 
@@ -282,6 +330,127 @@ int orc_block_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
             continue;
         if (pthread_create(&tid[t], NULL, gemm_worker, j) != 0) {
             gemm_worker(j);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+    return nthreads;
+}
+
+/* scaled_mm with per-token / per-channel scales, fp64:
+ * y[r][n] = sum_k (dec(qa[m][k]) * sa[m]) * (dec(qw[n][k]) * sw[n]),
+ * m = rows[r] (or r), summed in increasing k.  qa [M][K], sa [M], qw [N][K],
+ * sw [N], y [nrows][N]. */
+typedef struct {
+    const uint8_t *qa;
+    const float *sa;
+    const uint8_t *qw;
+    const float *sw;
+    int64_t N, K;
+    const int64_t *rows;
+    int64_t r0, r1;
+    double *y;
+} smm_job;
+
+static void *smm_worker(void *arg)
+{
+    smm_job *j = (smm_job *)arg;
+    double dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = orc_e4m3_decode((uint8_t)c);
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        int64_t m = j->rows ? j->rows[r] : r;
+        const uint8_t *arow = j->qa + m * j->K;
+        double sa = (double)j->sa[m];
+        for (int64_t n = 0; n < j->N; ++n) {
+            const uint8_t *wrow = j->qw + n * j->K;
+            double sw = (double)j->sw[n];
+            double acc = 0.0;
+            for (int64_t k = 0; k < j->K; ++k)
+                acc += (dec[arow[k]] * sa) * (dec[wrow[k]] * sw);
+            j->y[r * j->N + n] = acc;
+        }
+    }
+    return NULL;
+}
+
+int orc_scaled_mm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
+                  int64_t M, int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                  double *y, int nthreads)
+{
+    int64_t total = rows ? nrows : M;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (total < nthreads)
+        nthreads = total > 0 ? (int)total : 1;
+    pthread_t tid[256];
+    smm_job jobs[256];
+    int64_t per = (total + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        smm_job *j = &jobs[t];
+        j->qa = qa; j->sa = sa; j->qw = qw; j->sw = sw;
+        j->N = N; j->K = K; j->rows = rows; j->y = y;
+        j->r0 = t * per;
+        j->r1 = (t + 1) * per < total ? (t + 1) * per : total;
+        tid[t] = 0;
+        if (j->r0 >= j->r1)
+            continue;
+        if (pthread_create(&tid[t], NULL, smm_worker, j) != 0) {
+            smm_worker(j);
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+    return nthreads;
+}
+
+/* Row-parallel token quantizer over threads. */
+typedef struct {
+    const uint16_t *x;
+    int64_t K, ldx, ldq, m0, m1;
+    uint8_t *q;
+    float *s;
+    float eps;
+    int ue8m0;
+} tq_job;
+
+static void *tq_worker(void *arg)
+{
+    tq_job *j = (tq_job *)arg;
+    orc_token_quant(j->x + j->m0 * j->ldx, j->m1 - j->m0, j->K, j->ldx,
+                    j->q + j->m0 * j->ldq, j->ldq, j->s + j->m0, j->eps, j->ue8m0);
+    return NULL;
+}
+
+int orc_token_quant_mt(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t *q, int64_t ldq, float *s, float eps, int ue8m0, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (M < nthreads)
+        nthreads = M > 0 ? (int)M : 1;
+    pthread_t tid[256];
+    tq_job jobs[256];
+    int64_t per = (M + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        tq_job *j = &jobs[t];
+        j->x = x; j->K = K; j->ldx = ldx; j->ldq = ldq;
+        j->q = q; j->s = s; j->eps = eps; j->ue8m0 = ue8m0;
+        j->m0 = t * per;
+        j->m1 = (t + 1) * per < M ? (t + 1) * per : M;
+        tid[t] = 0;
+        if (j->m0 >= j->m1)
+            continue;
+        if (pthread_create(&tid[t], NULL, tq_worker, j) != 0) {
+            tq_worker(j);
             tid[t] = 0;
         }
     }
