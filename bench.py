@@ -51,26 +51,28 @@ def workload_cases(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def gemm_bytes(c) -> int:
+def gemm_bytes(c, dynamic: bool = False) -> int:
     M, N, K = c.M, c.N, c.K
+    if dynamic:  # per-token / per-channel scales
+        return M * K + 4 * M + N * K + 4 * N + 2 * M * N
     return M * K + 4 * M * K // 128 + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N
 
 
-def quant_bytes(c) -> int:
-    return 2 * c.M * c.K + c.M * c.K + 4 * c.M * c.K // 128
+def quant_bytes(c, dynamic: bool = False) -> int:
+    return 2 * c.M * c.K + c.M * c.K + (4 * c.M if dynamic else 4 * c.M * c.K // 128)
 
 
-def kernel_symbol(cfg, fused: bool = False, M: int = 0) -> str:
+def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False) -> str:
     """Name of the GEMM kernel a configuration launches, as rocprofv3 prints it."""
     b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
-        return (f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}, "
-                f"{b(cfg.scale_mode == 1)}>")
+        sm = 2 if channel else cfg.scale_mode
+        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}, {sm}>"
     fq = 0
     if fused:  # the fused quantizer variant the launcher picks for this M
         fq = 16 if cfg.tile_m > 16 or M > 8 else (1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8)
-    return f"k_gemm_swapab<{cfg.tile_m // 16}, {cfg.tile_n // 16}, {b(cfg.split_k > 1)}, {fq}>"
+    return f"k_gemm_swapab<{cfg.tile_m // 16}, {cfg.tile_n // 16}, {b(cfg.split_k > 1)}, {fq}, {b(channel)}>"
 
 
 def kernel_sources(symbol: str):
@@ -104,7 +106,7 @@ def traffic_from_profiles(symbol: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(cases, xs, budget_s: float):
+def cpu_baseline(cases, xs, budget_s: float, dynamic: bool = False):
     """The oracle (untuned) on a bounded sample: every case's quantization and
     fp64 GEMM on its first rows, doubling the rows until one pass takes
     about half the budget (or every row of every case is covered)."""
@@ -117,8 +119,9 @@ def cpu_baseline(cases, xs, budget_s: float):
     for c in cases:
         key = (c.N, c.K, c.ue8m0)
         if key not in wcache:
-            wcache[key] = oracle.weight_block_quant(synth.weights_f32(c.N, c.K), ue8m0=c.ue8m0,
-                                                    nthreads=threads)
+            w = synth.weights_f32(c.N, c.K)
+            wcache[key] = (oracle.channel_quant(w, ue8m0=c.ue8m0) if dynamic else
+                           oracle.weight_block_quant(w, ue8m0=c.ue8m0, nthreads=threads))
     nrows = 1
     while True:
         f = 0.0
@@ -129,8 +132,12 @@ def cpu_baseline(cases, xs, budget_s: float):
             qw, sw = wcache[(c.N, c.K, c.ue8m0)]
             rows = np.ascontiguousarray(x[:r])
             t0 = time.perf_counter()
-            qa, sa = oracle.group_quant(rows, ue8m0=c.ue8m0, nthreads=threads)
-            oracle.block_gemm(qa, sa, qw, sw, nthreads=threads)
+            if dynamic:
+                qa, sa = oracle.token_quant(rows, ue8m0=c.ue8m0, nthreads=threads)
+                oracle.scaled_mm(qa, sa, qw, sw, nthreads=threads)
+            else:
+                qa, sa = oracle.group_quant(rows, ue8m0=c.ue8m0, nthreads=threads)
+                oracle.block_gemm(qa, sa, qw, sw, nthreads=threads)
             t_total += time.perf_counter() - t0
             f += 2.0 * r * c.N * c.K
             r_used += r
@@ -153,6 +160,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--format", choices=("block", "dynamic"), default="block",
+                    help="block: Block_FP8 (1x128 / 128x128 scales, the default); "
+                         "dynamic: FP8_Dynamic (per-token / per-channel scales)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -172,6 +182,7 @@ def main() -> int:
     cases = workload_cases(args.workload)
     print(f"[bench] workload {args.workload}: {len(cases)} cases", file=sys.stderr, flush=True)
 
+    dynamic = args.format == "dynamic"
     # weights: quantized on the GPU, WEIGHT_COPIES buffers per shape
     wq = {}
     with torch.cuda.stream(stream):
@@ -183,8 +194,12 @@ def main() -> int:
             copies = []
             for _ in range(WEIGHT_COPIES):
                 q = torch.empty((c.N, c.K), dtype=torch.uint8, device=dev)
-                s = torch.empty((c.N // 128, c.K // 128), dtype=torch.float32, device=dev)
-                fb.fp8_weight_block_quant(w, q, s, ue8m0=c.ue8m0, stream=stream)
+                if dynamic:
+                    s = torch.empty((c.N,), dtype=torch.float32, device=dev)
+                    fb.fp8_weight_channel_quant(w, q, s, ue8m0=c.ue8m0, stream=stream)
+                else:
+                    s = torch.empty((c.N // 128, c.K // 128), dtype=torch.float32, device=dev)
+                    fb.fp8_weight_block_quant(w, q, s, ue8m0=c.ue8m0, stream=stream)
                 copies.append((q, s))
             wq[key] = copies
             del w
@@ -198,19 +213,35 @@ def main() -> int:
         xs.append(xh)
         x = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
         qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
-        sa = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
+        sa = torch.empty((c.M,) if dynamic else (c.M, c.K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
         cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, fb.FLAG_UE8M0 if c.ue8m0 else 0)
         ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
         bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, lws=lws, qw=qw, sw=sw,
-                         fused=cfg.variant == fb.SWAPAB and cfg.tile_m <= 32))
+                         fused=cfg.variant == fb.SWAPAB and cfg.tile_m <= 32 and not dynamic))
     torch.cuda.synchronize()
 
+    def quant(b):
+        if dynamic:
+            fb.fp8_token_quant(b["x"], b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+        else:
+            fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+
+    def gemm(b):
+        if dynamic:
+            fb.fp8_scaled_mm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+        else:
+            fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+
     def linear(b):
-        fb.fp8_linear(b["x"], b["qw"], b["sw"], b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
-                      workspace=b["lws"], stream=stream)
+        if dynamic:  # FP8_Dynamic: per-token quantization, then scaled_mm
+            quant(b)
+            gemm(b)
+        else:
+            fb.fp8_linear(b["x"], b["qw"], b["sw"], b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
+                          workspace=b["lws"], stream=stream)
 
     def step():
         for b in bufs:
@@ -273,17 +304,13 @@ def main() -> int:
     sym_work = {}
     for b in bufs:
         c = b["case"]
-        tq = timed(lambda: fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=c.ue8m0, stream=stream))
+        tq = timed(lambda: quant(b))
         tl = timed(lambda: linear(b))
-        if b["fused"]:
-            tg = tl
-        else:
-            tg = timed(lambda: fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"],
-                                                 b["ws"], stream=stream))
+        tg = tl if b["fused"] else timed(lambda: gemm(b))
         fl = c.flops()
-        gb = gemm_bytes(c) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
-        lb = gemm_bytes(c) + quant_bytes(c) if not b["fused"] else gb
-        sym = kernel_symbol(b["cfg"], b["fused"], c.M)
+        gb = gemm_bytes(c, dynamic) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
+        lb = gemm_bytes(c, dynamic) + quant_bytes(c, dynamic) if not b["fused"] else gb
+        sym = kernel_symbol(b["cfg"], b["fused"], c.M, dynamic)
         sym_time[sym] = sym_time.get(sym, 0.0) + tg
         w = sym_work.setdefault(sym, [0.0, 0.0, 0, 0])
         w[0] += fl
@@ -322,10 +349,10 @@ def main() -> int:
     if dsplit:
         roof["note"] = "split-K calls: duration includes the reduce kernel"
 
-    qb = sum(quant_bytes(b["case"]) for b in bufs)
+    qb = sum(quant_bytes(b["case"], dynamic) for b in bufs)
     qt = sum(p["quant_us"] for p in per_case) * 1e-6
     dec = [(p, b) for p, b in zip(per_case, bufs) if b["case"].M <= 64]
-    dec_bytes = sum(gemm_bytes(b["case"]) for _, b in dec)
+    dec_bytes = sum(gemm_bytes(b["case"], dynamic) for _, b in dec)
     dec_t = sum(p["linear_us"] for p, _ in dec) * 1e-6
     pre = [(p, b) for p, b in zip(per_case, bufs) if b["case"].M >= 4096]
     pre_fl = sum(b["case"].flops() for _, b in pre)
@@ -347,7 +374,9 @@ def main() -> int:
         "config": {"workload": args.workload, "cases": len(cases),
                    "m_values": sorted({b["case"].M for b in bufs}),
                    "nk": sorted({(b["case"].N, b["case"].K) for b in bufs}),
-                   "call": "fp8_linear", "graph_replay": graph is not None,
+                   "format": args.format,
+                   "call": "fp8_token_quant + fp8_scaled_mm" if dynamic else "fp8_linear",
+                   "graph_replay": graph is not None,
                    "weight_copies": WEIGHT_COPIES},
         "quant_gbps": round(qb / qt / 1e9, 1) if qt > 0 else None,
         "decode_linear_gbps": round(dec_bytes / dec_t / 1e9, 1) if dec_t > 0 else None,
@@ -358,7 +387,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cases, xs, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(cases, xs, args.cpu_budget, dynamic)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
   fp8_block_gemm         blockwise-scaled FP8 GEMM, bf16 out
   fp8_linear_workspace_size
   fp8_linear             the whole layer (quantize x, then the GEMM; fused for Swap-AB)
+  fp8_token_quant        per-token quantization (FP8_Dynamic activations)
+  fp8_weight_channel_quant  per-channel weight quantization (FP8_Dynamic weights)
+  fp8_scaled_mm          GEMM with per-token / per-channel scales
 """
 from __future__ import annotations
 
@@ -99,6 +102,13 @@ def lib() -> ctypes.CDLL:
     L.fp8_block_gemm.restype = ctypes.c_int
     L.fp8_block_gemm.argtypes = [P, P, I64, I64, P, P, I64, I64, P, I64, I64, I64, I64,
                                  ctypes.POINTER(GemmConfig), P, I64, P]
+    L.fp8_token_quant.restype = ctypes.c_int
+    L.fp8_token_quant.argtypes = [P, I64, I64, I64, P, I64, P, F, U32, P]
+    L.fp8_weight_channel_quant.restype = ctypes.c_int
+    L.fp8_weight_channel_quant.argtypes = [P, I64, I64, I64, P, I64, P, F, U32, P]
+    L.fp8_scaled_mm.restype = ctypes.c_int
+    L.fp8_scaled_mm.argtypes = [P, P, I64, P, P, I64, P, I64, I64, I64, I64,
+                                ctypes.POINTER(GemmConfig), P, I64, P]
     L.fp8_linear_workspace_size.restype = I64
     L.fp8_linear_workspace_size.argtypes = [I64, I64, I64, ctypes.POINTER(GemmConfig)]
     L.fp8_linear.restype = ctypes.c_int
@@ -224,6 +234,41 @@ def fp8_linear(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
     _check(st, "fp8_linear")
 
 
+def fp8_token_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
+    """dynamic_per_token_scaled_fp8_quant: x bf16 [M, K] -> q 1-byte [M, K], s float32 [M]."""
+    M, K = x.shape
+    if q.shape != (M, K) or s.numel() != M or x.element_size() != 2 or q.element_size() != 1:
+        raise ValueError("fp8_token_quant: shape/dtype mismatch")
+    st = lib().fp8_token_quant(x.data_ptr(), M, K, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
+                               s.data_ptr(), eps, FLAG_UE8M0 if ue8m0 else 0, _stream(stream))
+    _check(st, "fp8_token_quant")
+
+
+def fp8_weight_channel_quant(w, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
+    """Per-channel quantization of float32 W [N, K] -> q [N, K], s float32 [N]."""
+    N, K = w.shape
+    if q.shape != (N, K) or s.numel() != N or w.element_size() != 4 or q.element_size() != 1:
+        raise ValueError("fp8_weight_channel_quant: shape/dtype mismatch")
+    st = lib().fp8_weight_channel_quant(w.data_ptr(), N, K, _ld(w, "w"), q.data_ptr(), _ld(q, "q"),
+                                        s.data_ptr(), eps, FLAG_UE8M0 if ue8m0 else 0, _stream(stream))
+    _check(st, "fp8_weight_channel_quant")
+
+
+def fp8_scaled_mm(a, sa, w, sw, y, cfg: GemmConfig | None = None, workspace=None, stream=None) -> None:
+    """y[M, N] (bf16) = (a @ w^T) * sa[:, None] * sw[None, :] (per-token / per-channel scales)."""
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or y.shape != (M, N) or sa.numel() != M or sw.numel() != N:
+        raise ValueError("fp8_scaled_mm: shape mismatch")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_scaled_mm(a.data_ptr(), sa.data_ptr(), _ld(a, "a"), w.data_ptr(), sw.data_ptr(),
+                             _ld(w, "w"), y.data_ptr(), _ld(y, "y"), M, N, K,
+                             ctypes.byref(cfg) if cfg is not None else None,
+                             ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "fp8_scaled_mm")
+
+
 # -- conveniences that allocate their outputs with torch (plumbing only) ----
 
 def quantize_activations(x, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
@@ -276,3 +321,37 @@ def linear(x, qw, sw, eps: float = DEFAULT_EPS, ue8m0: bool = False, cfg: GemmCo
     ws = linear_workspace(M, N, K, cfg, x.device)
     fp8_linear(x, qw, sw, y, eps, ue8m0, cfg, ws, stream)
     return y
+
+
+def quantize_tokens(x, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
+    import torch
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    fp8_token_quant(x, q, s, eps, ue8m0, stream)
+    return q, s
+
+
+def quantize_weight_channels(w, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
+    import torch
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N,), dtype=torch.float32, device=w.device)
+    fp8_weight_channel_quant(w, q, s, eps, ue8m0, stream)
+    return q, s
+
+
+def scaled_mm(a, sa, w, sw, cfg: GemmConfig | None = None, stream=None):
+    import torch
+    M, K = a.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ws = workspace_for(M, N, K, cfg, a.device)
+    fp8_scaled_mm(a, sa, w, sw, y, cfg, ws, stream)
+    return y
+
+
+def dynamic_linear(x, qw, sw, eps: float = DEFAULT_EPS, cfg: GemmConfig | None = None, stream=None):
+    """The FP8_Dynamic linear layer: per-token quantization of x, then scaled_mm."""
+    qa, sa = quantize_tokens(x, eps, False, stream)
+    return scaled_mm(qa, sa, qw, sw, cfg, stream)

@@ -215,7 +215,9 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
     return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
-                                                  c.scale_mode == FP8BLK_SCALES_POW2, s));
+                                                  c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
+                                                                                       : fp8blk::kScalesBlock,
+                                                  s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
 }
 
@@ -294,7 +296,83 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   if (c.variant == FP8BLK_SWAPAB)
     return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
   return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
-                                                c.scale_mode == FP8BLK_SCALES_POW2, s));
+                                                c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
+                                                                                       : fp8blk::kScalesBlock,
+                                                  s));
+}
+
+int fp8_token_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                    float* s, float eps, uint32_t flags, void* stream) {
+  if (M < 0 || K <= 0 || K % kG != 0 || K > fp8blk::kRowQuantMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  const int st = check_quant_args(eps, flags);
+  if (st != FP8BLK_OK) return st;
+  if (ldx < K || ldq < K) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(s) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_row_quant(x, true, M, K, ldx, q, ldq, s, eps,
+                                            (flags & FP8BLK_FLAG_UE8M0) != 0, (hipStream_t)stream));
+}
+
+int fp8_weight_channel_quant(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                             int64_t ldq, float* s, float eps, uint32_t flags, void* stream) {
+  if (N < 0 || K <= 0 || K % kG != 0 || K > fp8blk::kRowQuantMaxK || N >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  const int st = check_quant_args(eps, flags);
+  if (st != FP8BLK_OK) return st;
+  if (ldw < K || ldq < K) return FP8BLK_ERR_BAD_STRIDE;
+  if (N == 0) return FP8BLK_OK;
+  if (!w || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(w) || !aligned16(q) || !aligned4(s) || (ldw * 4) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_row_quant(w, false, N, K, ldw, q, ldq, s, eps,
+                                            (flags & FP8BLK_FLAG_UE8M0) != 0, (hipStream_t)stream));
+}
+
+int fp8_scaled_mm(const uint8_t* a, const float* sa, int64_t lda, const uint8_t* w, const float* sw,
+                  int64_t ldw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                  const fp8blk_gemm_config* cfg, void* workspace, int64_t workspace_bytes,
+                  void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    fp8blk::select_config(M, N, K, 0, &c);
+  }
+  st = check_config(c, M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (c.scale_mode != FP8BLK_SCALES_FP32) return FP8BLK_ERR_BAD_CONFIG;  // the scale layout is fixed here
+  if (lda < K || ldw < K || ldy < N) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!a || !sa || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned4(sa) || !aligned4(sw) ||
+      lda % 16 != 0 || ldw % 16 != 0 || (ldy * 2) % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  const int64_t need = workspace_for(c, M, N);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8BLK_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
+  }
+  fp8blk::GemmArgs g{};
+  g.a = a;
+  g.sa = sa;
+  g.lda = lda;
+  g.w = w;
+  g.sw = sw;
+  g.ldw = ldw;
+  g.y = y;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ws = need > 0 ? (float*)workspace : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if (c.variant == FP8BLK_STANDARD)
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
+                                                  fp8blk::kScalesChannel, s));
+  return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s, true));
 }
 
 }  // extern "C"

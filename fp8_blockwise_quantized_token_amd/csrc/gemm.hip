@@ -61,8 +61,13 @@ __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *(const u32x
 //     (the work of the 16 - FQ padding rows is not done); the codes go to a
 //     wave-private 16 x 128-byte LDS tile (rows >= FQ stay zero) and are
 //     read back in operand order.
-template <int TOKT, int RN, bool SPLIT, int FQ>
+//
+// CH: per-token / per-channel scales (FP8_Dynamic, separate quantizer): the
+// K loop accumulates in the matrix core without rescaling and the epilogue
+// multiplies by sw[n] * sa[m].
+template <int TOKT, int RN, bool SPLIT, int FQ, bool CH>
 __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
+  static_assert(!CH || FQ == 0, "per-token scales need the whole row: quantize first");
   constexpr bool FUSED = FQ != 0;
   constexpr bool LEAN = FQ > 0 && FQ < 16;
   static_assert(!LEAN || TOKT == 1, "the lean quantizer serves one token tile");
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
 #pragma unroll
       for (int r = 0; r < RN; ++r)
         b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
-      const float swv = k <= kblast ? swsrc[kc] : 0.f;
+      const float swv = CH ? 0.f : (k <= kblast ? swsrc[kc] : 0.f);
       if (FUSED) b.swv[u] = swv;
       if (LEAN) {
         u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = u32x4{0u, 0u, 0u, 0u};
@@ -188,7 +193,8 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
           }
         } else if (tvalid[t]) {
           b.xf[u][t] = make_v8i(gload16(xsrc[t] + ko), gload16(xsrc[t] + ko + 64));
-          b.gsc[u][t] = sasrc[t][kc] * swv;
+          // CH: no per-block factor; a K block past the range must add nothing
+          b.gsc[u][t] = CH ? (k <= kblast ? 1.f : 0.f) : sasrc[t][kc] * swv;
         } else {
           b.xf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           b.gsc[u][t] = 0.f;
@@ -335,6 +341,11 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
       const int64_t m = t * 16 + (ln & 15);
       const int64_t n = n0 + r * 16 + (ln >> 4) * 4;
       if (m < g.M) {
+        if (CH) {
+          const float sam = g.sa[m];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * g.sw[n + q];
+        }
         if (SPLIT)
           *(float4*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
         else
@@ -351,7 +362,12 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
         const int64_t m = t * 16 + row;
         const int64_t n = n0 + r * 16 + (lane >> 4) * 4;
         if (m < g.M) {
-          const v4f v = acc[r][t];
+          v4f v = acc[r][t];
+          if (CH) {
+            const float sam = g.sa[m];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * g.sw[n + q];
+          }
           if (SPLIT)
             *(float4*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
           else
@@ -385,23 +401,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
-template <int TOKT, int RN, int FQ>
+template <int TOKT, int RN, int FQ, bool CH = false>
 hipError_t run_swap3(const SwapParams& p, dim3 grid, int kwaves, bool split, hipStream_t stream) {
   if (split)
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true, FQ>), grid, dim3(64 * kwaves), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, true, FQ, CH>), grid, dim3(64 * kwaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false, FQ>), grid, dim3(64 * kwaves), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_swapab<TOKT, RN, false, FQ, CH>), grid, dim3(64 * kwaves), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int TOKT, int RN>
-hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, hipStream_t stream) {
+hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, bool ch, hipStream_t stream) {
   SwapParams p;
   p.g = g;
   p.kb_total = (int)(g.K / 128);
   p.kb_per_split = (p.kb_total + split_k - 1) / split_k;
   dim3 grid((unsigned)(g.N / (16 * RN)), (unsigned)split_k);
   const bool sp = split_k > 1;
+  if (ch) return run_swap3<TOKT, RN, 0, true>(p, grid, kwaves, sp, stream);
   if (g.x == nullptr) return run_swap3<TOKT, RN, 0>(p, grid, kwaves, sp, stream);
   if constexpr (TOKT == 1) {  // fused: quantize only the tokens that can be valid
     if (g.M <= 1) return run_swap3<TOKT, RN, 1>(p, grid, kwaves, sp, stream);
@@ -425,11 +442,11 @@ bool swapab_tile_supported(int tile_m, int tile_n, int kwaves) {
 }
 
 hipError_t launch_gemm_swapab(const GemmArgs& g, int tile_m, int tile_n, int kwaves, int split_k,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool channel_scales) {
   const int tokt = tile_m / 16, rn = tile_n / 16;
   hipError_t e = hipErrorInvalidValue;
 #define FP8BLK_SWAP_CASE(T, R) \
-  if (tokt == T && rn == R) e = run_swap<T, R>(g, kwaves, split_k, stream);
+  if (tokt == T && rn == R) e = run_swap<T, R>(g, kwaves, split_k, channel_scales, stream);
   FP8BLK_SWAP_CASE(1, 1)
   FP8BLK_SWAP_CASE(1, 2)
   FP8BLK_SWAP_CASE(1, 4)

@@ -97,15 +97,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 // work per K block and the loop would otherwise wait one memory latency per
 // block, use three or four.
 //
+// SM: 0 = blockwise fp32 scales (one VALU rescale per K block), 1 = P2,
+// 2 = CH (per-token / per-channel scales, FP8_Dynamic: the K loop is plain
+// matrix-core accumulation and the epilogue multiplies by sa[m] * sw[n]).
+//
 // P2 (power-of-two scales, the UE8M0 mode): every sa and sw is 2^e, so the
 // K-block scaling is exact in the matrix core itself:
 // v_mfma_scale_f32_16x16x128_f8f6f4 takes an E8M0 exponent per A row (lane
 // l & 15; the same for the lane's four 32-wide K sub-blocks) and per B
 // column, multiplies the block product by 2^(ea + eb - 254) and accumulates
 // into the fp32 tile directly.  No VALU rescale and no product registers.
-template <int BM, int BN, int WM, int WN, bool SPLIT, int NS, bool P2>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int NS, int SM>
 __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams p) {
   using S = Shape<BM, BN, WM, WN>;
+  constexpr bool P2 = SM == 1;
+  constexpr bool CH = SM == 2;
   static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
   // separate objects per stage, so that the compiler sees that the stage
   // being filled and the stage being read never alias
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     else if constexpr (i == 2) return lds_s2;
     else return lds_s3;
   };
-  constexpr int PER = S::A_INSTR + S::B_INSTR + 1;  // direct-to-LDS instructions per wave and stage
+  constexpr int PER = S::A_INSTR + S::B_INSTR + (CH ? 0 : 1);  // direct-to-LDS instructions per wave and stage
 
   const GemmArgs& g = p.g;
   const int lane = threadIdx.x & 63;
@@ -213,7 +219,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
                                        (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16, 0, 0);
     // one 4-byte scale load per wave: waves < SA_INSTR load activation
     // scales, the others the weight scales (the same values, harmless)
-    __builtin_amdgcn_global_load_lds((const void*)(sc_base + kb + sc_off), (lds_void*)(ls + sc_dst), 4, 0, 0);
+    if constexpr (!CH)
+      __builtin_amdgcn_global_load_lds((const void*)(sc_base + kb + sc_off), (lds_void*)(ls + sc_dst), 4, 0, 0);
   };
 
   v4f acc[S::TM][S::TN];
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     if constexpr (P2) {
 #pragma unroll
       for (int i = 0; i < S::TM; ++i) ea[i] = __float_as_uint(ls[erow + i * 16]) >> 23;
-    } else {
+    } else if constexpr (!CH) {
       scl = *(const v4f*)(ls + srow);
     }
   };
@@ -272,8 +279,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
                     int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns)
                     __attribute__((always_inline)) {
-    if constexpr (P2) {
-      const uint32_t eb = __float_as_uint(swv) >> 23;  // this wave's 128 columns share sw
+    if constexpr (P2 || CH) {
+      const uint32_t eb = P2 ? __float_as_uint(swv) >> 23 : 0u;  // this wave's 128 columns share sw
 #pragma unroll
       for (int i = 0; i < S::TM; ++i) {
         const int cur = i & 1, prv = cur ^ 1;
@@ -281,9 +288,14 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
           af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                              *(const u32x4*)(la + a_hi + (i + 1) * 2048));
 #pragma unroll
-        for (int j = 0; j < S::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
-                                                                       (int)ea[i], 0, (int)eb);
+        for (int j = 0; j < S::TN; ++j) {
+          if constexpr (P2)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
+                                                                         (int)ea[i], 0, (int)eb);
+          else  // unscaled accumulate (zero scale operands select the plain instruction)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
+                                                                         0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_vmcnt<(NS - 2) * PER>();
@@ -371,25 +383,32 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   wait_vmcnt<0>();
 
   // ---- epilogue: lane holds rows orow..orow+3 and column frow of each tile ----
+  float swc[S::TN];  // CH: per-channel weight scales of this lane's columns
+  if constexpr (CH) {
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) swc[j] = g.sw[n0 + wave_n * WN + j * 16 + frow];
+  }
 #pragma unroll
   for (int i = 0; i < S::TM; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t m = m0 + wave_m * WM + i * 16 + orow + q;
       if (m >= g.M) continue;
+      const float sam = CH ? g.sa[m] : 1.0f;
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
         const int64_t n = n0 + wave_n * WN + j * 16 + frow;
+        const float v = CH ? acc[i][j][q] * sam * swc[j] : acc[i][j][q];
         if (SPLIT)
-          g.ws[((int64_t)split * g.M + m) * g.N + n] = acc[i][j][q];
+          g.ws[((int64_t)split * g.M + m) * g.N + n] = v;
         else
-          g.y[m * g.ldy + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
+          g.y[m * g.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool P2>
+template <int BM, int BN, int WM, int WN, int NS, int SM>
 hipError_t run_p(const GemmArgs& g, int split_k, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   StdParams p;
@@ -401,16 +420,17 @@ hipError_t run_p(const GemmArgs& g, int split_k, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * split_k;
   p.remap = (blocks % kXcds == 0) ? 1 : 0;
   if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS, P2>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS, SM>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS, P2>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS, SM>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
-hipError_t run(const GemmArgs& g, int split_k, bool pow2, hipStream_t stream) {
-  return pow2 ? run_p<BM, BN, WM, WN, NS, true>(g, split_k, stream)
-              : run_p<BM, BN, WM, WN, NS, false>(g, split_k, stream);
+hipError_t run(const GemmArgs& g, int split_k, int sm, hipStream_t stream) {
+  if (sm == 1) return run_p<BM, BN, WM, WN, NS, 1>(g, split_k, stream);
+  if (sm == 2) return run_p<BM, BN, WM, WN, NS, 2>(g, split_k, stream);
+  return run_p<BM, BN, WM, WN, NS, 0>(g, split_k, stream);
 }
 
 }  // namespace
@@ -428,7 +448,8 @@ bool standard_tile_supported(int tile_m, int tile_n, int stages) {
 }
 
 hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                bool pow2, hipStream_t stream) {
+                                int scale_mode, hipStream_t stream) {
+  const int pow2 = scale_mode;  // 0 block fp32, 1 block power-of-two, 2 per-token / per-channel
   const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
   if (tile_m == 64 && tile_n == 128)

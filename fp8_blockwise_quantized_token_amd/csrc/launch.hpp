@@ -17,6 +17,13 @@ hipError_t launch_weight_block_quant(const float* w, int64_t N, int64_t K, int64
 
 hipError_t launch_e4m3_encode(const float* t, uint8_t* q, int64_t n, hipStream_t stream);
 
+// One scale per row (per token for bf16 activations, per channel for fp32
+// weights); K <= kRowQuantMaxK (the row is held in registers).
+constexpr int64_t kRowQuantMaxK = 32768;
+hipError_t launch_row_quant(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ldx,
+                            uint8_t* q, int64_t ldq, float* s, float eps, bool ue8m0,
+                            hipStream_t stream);
+
 struct GemmArgs {
   const uint8_t* a;
   const float* sa;
@@ -37,16 +44,19 @@ struct GemmArgs {
   int ue8m0;
 };
 
-// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones;
-// pow2: every scale is a power of two and the matrix core applies them.
+// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones.
+// scale_mode: kScalesBlock (sa [M][K/128], sw [N/128][K/128], any fp32),
+// kScalesBlockPow2 (same layout, every scale a power of two, applied by the
+// matrix core), kScalesChannel (sa [M], sw [N]: per token / per channel).
+constexpr int kScalesBlock = 0, kScalesBlockPow2 = 1, kScalesChannel = 2;
 bool standard_tile_supported(int tile_m, int tile_n, int stages);
 hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                bool pow2, hipStream_t stream);
+                                int scale_mode, hipStream_t stream);
 
 // Swap-AB variant.
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);
 hipError_t launch_gemm_swapab(const GemmArgs& g, int tile_m, int tile_n, int kwaves,
-                              int split_k, hipStream_t stream);  // fused when g.x != nullptr
+                              int split_k, hipStream_t stream, bool channel_scales = false);  // fused when g.x != nullptr
 
 // Fixed-order sum of split_k fp32 partials -> bf16.
 hipError_t launch_splitk_reduce(const float* ws, int split_k, int64_t M, int64_t N,

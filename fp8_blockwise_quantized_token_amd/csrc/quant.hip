@@ -130,6 +130,69 @@ __global__ __launch_bounds__(256) void k_weight_block_quant(
   if (t == 0) s[nb * lds + kb] = sc;
 }
 
+// Per-token / per-channel quantization (FP8_Dynamic): one workgroup per
+// row, the row held in registers (read once): up to 16 vectors of 16 bytes
+// per thread.  amax over the row: |x| bit patterns (ordered like the
+// magnitudes) reduced with DPP inside 16-lane rows, readlane across rows and
+// LDS across waves; one scale; every value divided and encoded.  bf16 rows
+// use the 3-instruction correctly rounded division (exact for 8-bit
+// significands); fp32 rows (weights, offline) use IEEE division.
+constexpr int kRowVec = 16;
+
+template <bool BF16, bool UE8M0, int NT>
+__global__ __launch_bounds__(NT) void k_row_quant(const uint8_t* __restrict__ x, int64_t ldx_bytes,
+                                                  uint8_t* __restrict__ q, int64_t ldq,
+                                                  float* __restrict__ s, int nvec, float eps) {
+  __shared__ uint32_t red[NT / 64];
+  constexpr int EV = BF16 ? 8 : 4;  // values per 16-byte vector
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const uint8_t* src = x + row * ldx_bytes;
+  u32x4 v[kRowVec];
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < kRowVec; ++i) {
+    const int idx = t + i * NT;
+    v[i] = idx < nvec ? load_nt16(src + (int64_t)idx * 16) : u32x4{0u, 0u, 0u, 0u};
+    if (BF16) {
+      const uint32_t a = max(max(v[i].x & 0x7FFFu, v[i].x >> 16 & 0x7FFFu), max(v[i].y & 0x7FFFu, v[i].y >> 16 & 0x7FFFu));
+      const uint32_t b = max(max(v[i].z & 0x7FFFu, v[i].z >> 16 & 0x7FFFu), max(v[i].w & 0x7FFFu, v[i].w >> 16 & 0x7FFFu));
+      am = max(am, max(a, b) << 16);
+    } else {
+      am = max(am, max(max(v[i].x & 0x7FFFFFFFu, v[i].y & 0x7FFFFFFFu), max(v[i].z & 0x7FFFFFFFu, v[i].w & 0x7FFFFFFFu)));
+    }
+  }
+  am = row16_max_u32(am);
+  am = max(max((uint32_t)__builtin_amdgcn_readlane((int)am, 0), (uint32_t)__builtin_amdgcn_readlane((int)am, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)am, 32), (uint32_t)__builtin_amdgcn_readlane((int)am, 48)));
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) am = max(am, red[w]);
+  const float sc = scale_from_amax(__uint_as_float(am), eps, UE8M0);
+  const float rc = 1.0f / sc;
+  uint8_t* dst = q + row * ldq;
+#pragma unroll
+  for (int i = 0; i < kRowVec; ++i) {
+    const int idx = t + i * NT;
+    if (idx >= nvec) continue;
+    const u32x4 w = v[i];
+    if (BF16) {
+      const uint32_t lo = encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+                                  div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
+      const uint32_t hi = encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+                                  div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
+      *(uint2*)(dst + (int64_t)idx * EV) = make_uint2(lo, hi);
+    } else {
+      *(uint32_t*)(dst + (int64_t)idx * EV) =
+          encode4(__uint_as_float(w.x) / sc, __uint_as_float(w.y) / sc, __uint_as_float(w.z) / sc,
+                  __uint_as_float(w.w) / sc);
+    }
+  }
+  if (t == 0) s[row] = sc;
+}
+
 __global__ __launch_bounds__(256) void k_e4m3_encode(const float* __restrict__ t,
                                                      uint8_t* __restrict__ q, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
@@ -212,6 +275,34 @@ hipError_t launch_weight_block_quant(const float* w, int64_t N, int64_t K, int64
       hipLaunchKernelGGL(k_weight_block_quant<true>, grid, block, 0, stream, wb, ldw, qb, ldq, sb, lds, eps);
     else
       hipLaunchKernelGGL(k_weight_block_quant<false>, grid, block, 0, stream, wb, ldw, qb, ldq, sb, lds, eps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_row_quant(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ldx,
+                            uint8_t* q, int64_t ldq, float* s, float eps, bool ue8m0,
+                            hipStream_t stream) {
+  const int ev = bf16 ? 8 : 4;
+  const int nvec = (int)(K / ev);
+  const int64_t ldx_bytes = ldx * (bf16 ? 2 : 4);
+  for (int64_t r0 = 0; r0 < rows; r0 += 2147483647) {
+    const int64_t nr = (rows - r0) < 2147483647 ? (rows - r0) : 2147483647;
+    const uint8_t* xr = (const uint8_t*)x + r0 * ldx_bytes;
+    uint8_t* qr = q + r0 * ldq;
+    float* sr = s + r0;
+    if (bf16) {
+      if (ue8m0)
+        hipLaunchKernelGGL((k_row_quant<true, true, 256>), dim3((unsigned)nr), dim3(256), 0, stream, xr, ldx_bytes, qr, ldq, sr, nvec, eps);
+      else
+        hipLaunchKernelGGL((k_row_quant<true, false, 256>), dim3((unsigned)nr), dim3(256), 0, stream, xr, ldx_bytes, qr, ldq, sr, nvec, eps);
+    } else {
+      if (ue8m0)
+        hipLaunchKernelGGL((k_row_quant<false, true, 512>), dim3((unsigned)nr), dim3(512), 0, stream, xr, ldx_bytes, qr, ldq, sr, nvec, eps);
+      else
+        hipLaunchKernelGGL((k_row_quant<false, false, 512>), dim3((unsigned)nr), dim3(512), 0, stream, xr, ldx_bytes, qr, ldq, sr, nvec, eps);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

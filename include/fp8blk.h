@@ -230,6 +230,54 @@ int fp8_linear(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw
                const fp8blk_gemm_config *cfg, void *workspace,
                int64_t workspace_bytes, void *stream);
 
+/*
+ * FP8_Dynamic: per-token activation scales and per-channel weight scales
+ * (autotuning page, "Helion Linear Backend" / "Scope": the first of its
+ * three formats).  Quantizer dynamic_per_token_scaled_fp8_quant and GEMM
+ * scaled_mm (German page, "Welche Kernel wurden in vLLM integriert").
+ */
+
+/*
+ * dynamic_per_token_scaled_fp8_quant: the group rule of fp8_group_quant with
+ * the whole row as one group -- for every row m: amax over its K values,
+ * s[m] = max(amax, eps)/448 (power-of-two ceiling with FP8BLK_FLAG_UE8M0),
+ * q[m][k] = e4m3fn_rne(clamp(x / s[m], -448, 448)).
+ *   x bf16 [M][ldx], ldx >= K;  q uint8 [M][ldq], ldq >= K;  s fp32 [M].
+ *   Requires K % 128 == 0 and K <= 32768 (a row is held in registers);
+ *   x and q 16-byte aligned with 16-byte row pitches, s 4-byte aligned.
+ */
+int fp8_token_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                    uint8_t *q, int64_t ldq, float *s, float eps,
+                    uint32_t flags, void *stream);
+
+/*
+ * Per-channel weight quantization (offline preparation of FP8_Dynamic
+ * weights): for every row n of W, s[n] = max(amax_row, eps)/448 [power-of-
+ * two ceiling], q = e4m3fn_rne(clamp(w / s[n], -448, 448)) (IEEE division).
+ *   w fp32 [N][ldw], ldw >= K;  q uint8 [N][ldq];  s fp32 [N].
+ *   Requires K % 128 == 0 and K <= 32768.
+ */
+int fp8_weight_channel_quant(const float *w, int64_t N, int64_t K, int64_t ldw,
+                             uint8_t *q, int64_t ldq, float *s, float eps,
+                             uint32_t flags, void *stream);
+
+/*
+ * scaled_mm with per-token / per-channel scales, bf16 out:
+ *   y[m][n] = bf16_rne( (sum_k dec(a[m][k]) * dec(w[n][k])) * sa[m] * sw[n] )
+ * with fp32 accumulation.  The K loop is plain matrix-core accumulation; the
+ * scales are applied once in the epilogue.
+ *   a uint8 [M][lda], sa fp32 [M];  w uint8 [N][ldw], sw fp32 [N];
+ *   y bf16 [M][ldy].  cfg as in fp8_block_gemm (NULL: fp8_block_gemm_select;
+ *   scale_mode must be FP8BLK_SCALES_FP32); the workspace size is
+ *   fp8_block_gemm_workspace_size's for the same configuration.
+ * Requires K % 128 == 0, N % 128 == 0, M >= 0.
+ */
+int fp8_scaled_mm(const uint8_t *a, const float *sa, int64_t lda,
+                  const uint8_t *w, const float *sw, int64_t ldw,
+                  uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                  const fp8blk_gemm_config *cfg, void *workspace,
+                  int64_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

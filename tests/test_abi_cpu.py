@@ -241,3 +241,31 @@ def test_linear_argument_errors():
             assert fb.fp8_linear_workspace_size(case.M, case.N, case.K) == \
                 fb.fp8_linear_workspace_size(case.M, case.N, case.K,
                                              fb.fp8_block_gemm_select(case.M, case.N, case.K))
+
+
+def test_dynamic_entry_argument_errors():
+    L = fb.lib()
+    tq = lambda x=A, M=4, K=256, ldx=256, q=B, ldq=256, s=C, eps=1e-10, flags=0: \
+        L.fp8_token_quant(x, M, K, ldx, q, ldq, s, eps, flags, None)
+    assert tq(x=None) == NULL and tq(q=None) == NULL and tq(s=None) == NULL
+    assert tq(K=200, ldx=256, ldq=256) == SHAPE
+    assert tq(K=32768 + 128, ldx=40000, ldq=40000) == SHAPE
+    assert tq(M=-1) == SHAPE and tq(eps=0.0) == SHAPE and tq(flags=2) == CFG
+    assert tq(ldx=128) == STRIDE and tq(ldq=128) == STRIDE
+    assert tq(x=A + 2) == MISAL and tq(ldx=260) == MISAL and tq(s=C + 2) == MISAL
+    assert tq(M=0, x=None, q=None, s=None) == OK
+    cq = lambda w=A, N=128, K=256, ldw=256, q=B, ldq=256, s=C, eps=1e-10, flags=0: \
+        L.fp8_weight_channel_quant(w, N, K, ldw, q, ldq, s, eps, flags, None)
+    assert cq(w=None) == NULL and cq(K=100, ldw=256, ldq=256) == SHAPE and cq(ldw=200) == STRIDE
+    assert cq(ldw=258) == MISAL and cq(N=0, w=None, q=None, s=None) == OK
+    sm = lambda a=A, sa=B, lda=256, w=C, sw=D, ldw=256, y=E, ldy=256, M=8, N=256, K=256, cfg=None, ws=None, n=0: \
+        L.fp8_scaled_mm(a, sa, lda, w, sw, ldw, y, ldy, M, N, K,
+                        ctypes.byref(cfg) if cfg is not None else None, ws, n, None)
+    std = fb.make_config(fb.STANDARD, 128, 128)
+    assert sm(a=None, cfg=std) == NULL and sm(sa=None, cfg=std) == NULL and sm(sw=None, cfg=std) == NULL
+    assert sm(K=200, cfg=std) == SHAPE and sm(N=200, cfg=std) == SHAPE
+    assert sm(lda=128, cfg=std) == STRIDE and sm(ldy=128, cfg=std) == STRIDE
+    assert sm(sa=B + 2, cfg=std) == MISAL and sm(a=A + 1, cfg=std) == MISAL
+    assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=fb.SCALES_POW2)) == CFG
+    assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=2)) == WS
+    assert sm(M=0, a=None, sa=None, w=None, sw=None, y=None, cfg=std) == OK
