@@ -150,14 +150,24 @@ def fp8_status_string(status: int) -> str:
     return lib().fp8_status_string(status).decode()
 
 
-def fp8_group_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
-    """x: bf16 [M, K] (cuda), q: 1-byte [M, K], s: float32 [M, K/128]; outputs overwritten."""
+FLAG_SCALE_E8M0 = 2
+FLAG_SCALE_MN_MAJOR = 4
+
+
+def fp8_group_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None,
+                    scale_e8m0: bool = False, scale_mn_major: bool = False) -> None:
+    """x: bf16 [M, K] (cuda), q: 1-byte [M, K], s: float32 [M, K/128] (MN-major:
+    [K/128, >= M]; E8M0: 1-byte elements); outputs overwritten."""
     M, K = x.shape
-    if q.shape != (M, K) or s.shape[0] != M or x.element_size() != 2 or q.element_size() != 1:
+    srows = K // GROUP if scale_mn_major else M
+    if q.shape != (M, K) or s.shape[0] != srows or x.element_size() != 2 or q.element_size() != 1:
         raise ValueError("fp8_group_quant: shape/dtype mismatch")
+    if s.element_size() != (1 if scale_e8m0 else 4):
+        raise ValueError("fp8_group_quant: scale dtype mismatch")
+    flags = (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_SCALE_E8M0 if scale_e8m0 else 0) | \
+        (FLAG_SCALE_MN_MAJOR if scale_mn_major else 0)
     st = lib().fp8_group_quant(x.data_ptr(), M, K, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
-                               s.data_ptr(), _ld(s, "s"), GROUP, eps,
-                               FLAG_UE8M0 if ue8m0 else 0, _stream(stream))
+                               s.data_ptr(), _ld(s, "s"), GROUP, eps, flags, _stream(stream))
     _check(st, "fp8_group_quant")
 
 

@@ -109,19 +109,23 @@ const char* fp8_status_string(int status) {
 }
 
 int fp8_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
-                    float* s, int64_t lds, int32_t group, float eps, uint32_t flags, void* stream) {
+                    void* s, int64_t lds, int32_t group, float eps, uint32_t flags, void* stream) {
   if (group != kG) return FP8BLK_ERR_BAD_SHAPE;
   if (M < 0 || K <= 0 || K % kG != 0 || K > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
   if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
-  if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
-  if (ldx < K || ldq < K || lds < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  const uint32_t known = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_SCALE_E8M0 | FP8BLK_FLAG_SCALE_MN_MAJOR;
+  if ((flags & ~known) != 0) return FP8BLK_ERR_BAD_CONFIG;
+  const bool e8m0 = (flags & FP8BLK_FLAG_SCALE_E8M0) != 0;
+  const bool mn = (flags & FP8BLK_FLAG_SCALE_MN_MAJOR) != 0;
+  if (e8m0 && !(flags & FP8BLK_FLAG_UE8M0)) return FP8BLK_ERR_BAD_CONFIG;  // E8M0 holds powers of two only
+  if (ldx < K || ldq < K || lds < (mn ? M : K / kG)) return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;
   if (!x || !q || !s) return FP8BLK_ERR_NULL_PTR;
-  if (!aligned16(x) || !aligned16(q) || !aligned4(s) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+  if (!aligned16(x) || !aligned16(q) || (!e8m0 && !aligned4(s)) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
     return FP8BLK_ERR_MISALIGNED;
   return to_status(fp8blk::launch_group_quant(x, M, K, ldx, q, ldq, s, lds, eps,
                                               (flags & FP8BLK_FLAG_UE8M0) != 0,
-                                              (hipStream_t)stream));
+                                              (mn ? 1 : 0) | (e8m0 ? 2 : 0), (hipStream_t)stream));
 }
 
 int fp8_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
@@ -287,7 +291,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   }
   uint8_t* q = (uint8_t*)(base + L.q_off);
   float* sc = (float*)(base + L.s_off);
-  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, s);
+  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, 0, s);
   if (e != hipSuccess) return FP8BLK_ERR_HIP;
   g.a = q;
   g.sa = sc;

@@ -7,9 +7,10 @@
 
 namespace fp8blk {
 
+// scale_format: bit 0 = MN-major scales [K/128][lds], bit 1 = E8M0 bytes.
 hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                              uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                              float eps, bool ue8m0, hipStream_t stream);
+                              uint8_t* q, int64_t ldq, void* s, int64_t lds,
+                              float eps, bool ue8m0, int scale_format, hipStream_t stream);
 
 hipError_t launch_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw,
                                      uint8_t* q, int64_t ldq, float* s, int64_t lds,

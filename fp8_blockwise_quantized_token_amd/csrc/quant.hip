@@ -45,11 +45,16 @@ constexpr int kQuantThreads = 256;
 constexpr int kQuantUnroll = 4;
 constexpr uint32_t kGroupsPerIter = (kQuantThreads / 16) * kQuantUnroll;
 
-template <bool UE8M0, bool CONTIG>
+// SF (scale output format): 0 fp32 [M][lds]; 1 fp32 MN-major [K/128][lds];
+// 2 and 3: the same layouts with one E8M0 byte per scale (the biased
+// exponent of a power-of-two scale, value 2^(b - 127)).
+template <bool UE8M0, bool CONTIG, int SF>
 __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s,
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, void* __restrict__ s,
     uint32_t total_groups, uint32_t gpr, uint64_t magic, int64_t ldx, int64_t ldq,
     int64_t lds, float eps) {
+  constexpr bool MN = (SF & 1) != 0;
+  constexpr bool E8M0 = (SF & 2) != 0;
   const uint32_t sub = threadIdx.x & 15u;
   const uint32_t slot = threadIdx.x >> 4;
   const uint32_t step = gridDim.x * kGroupsPerIter;
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
         const uint32_t col = g - row * gpr;
         xo = (int64_t)row * ldx + (int64_t)col * kGroup + sub * 8;
         qo[u] = (int64_t)row * ldq + (int64_t)col * kGroup + sub * 8;
-        so[u] = (int64_t)row * lds + col;
+        so[u] = MN ? (int64_t)col * lds + row : (int64_t)row * lds + col;
       }
       v[u] = valid[u] ? load_nt16(x + xo) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -87,7 +92,12 @@ __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
                                   div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
       if (valid[u]) {
         *(uint2*)(q + qo[u]) = make_uint2(lo, hi);
-        if (sub == 0) s[so[u]] = sc;
+        if (sub == 0) {
+          if (E8M0)
+            ((uint8_t*)s)[so[u]] = (uint8_t)(__float_as_uint(sc) >> 23);
+          else
+            ((float*)s)[so[u]] = sc;
+        }
       }
     }
   }
@@ -218,11 +228,21 @@ int device_cu_count() {
 
 }  // namespace
 
+template <bool UE8M0, bool CONTIG, int SF>
+void launch_gq(dim3 grid, dim3 block, hipStream_t stream, const uint16_t* xr, uint8_t* qr, void* sr,
+               uint32_t total, uint32_t gpr, uint64_t magic, int64_t ldx, int64_t ldq, int64_t lds,
+               float eps) {
+  hipLaunchKernelGGL((k_group_quant<UE8M0, CONTIG, SF>), grid, block, 0, stream, xr, qr, sr, total, gpr,
+                     magic, ldx, ldq, lds, eps);
+}
+
 hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                              int64_t ldq, float* s, int64_t lds, float eps, bool ue8m0,
-                              hipStream_t stream) {
+                              int64_t ldq, void* s, int64_t lds, float eps, bool ue8m0,
+                              int scale_format, hipStream_t stream) {
   const int64_t gpr = K / kGroup;
-  const bool contig = (ldx == K) && (ldq == K) && (lds == gpr);
+  const bool mn = (scale_format & 1) != 0;
+  const int64_t selt = (scale_format & 2) ? 1 : 4;  // bytes per stored scale
+  const bool contig = scale_format == 0 && (ldx == K) && (ldq == K) && (lds == gpr);
   const int max_blocks = device_cu_count() * 8;
   // Contiguous: one flat launch per 2^31 groups.  Strided: row chunks with
   // fewer than 2^24 groups, so that row = (g * ceil(2^40/gpr)) >> 40 is exact.
@@ -237,23 +257,23 @@ hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
     if (blocks > max_blocks) blocks = max_blocks;
     const uint16_t* xr = x + r0 * ldx;
     uint8_t* qr = q + r0 * ldq;
-    float* sr = s + r0 * lds;
+    void* sr = (char*)s + (mn ? r0 : r0 * lds) * selt;
     dim3 grid((unsigned)blocks), block(kQuantThreads);
+    const uint32_t g32 = (uint32_t)gpr;
+#define FP8BLK_GQ(U, C, F) launch_gq<U, C, F>(grid, block, stream, xr, qr, sr, total, g32, magic, ldx, ldq, lds, eps)
     if (contig) {
-      if (ue8m0)
-        hipLaunchKernelGGL((k_group_quant<true, true>), grid, block, 0, stream, xr, qr, sr, total,
-                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
-      else
-        hipLaunchKernelGGL((k_group_quant<false, true>), grid, block, 0, stream, xr, qr, sr, total,
-                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+      if (ue8m0) FP8BLK_GQ(true, true, 0); else FP8BLK_GQ(false, true, 0);
+    } else if (ue8m0) {
+      switch (scale_format) {
+        case 0: FP8BLK_GQ(true, false, 0); break;
+        case 1: FP8BLK_GQ(true, false, 1); break;
+        case 2: FP8BLK_GQ(true, false, 2); break;
+        default: FP8BLK_GQ(true, false, 3); break;
+      }
     } else {
-      if (ue8m0)
-        hipLaunchKernelGGL((k_group_quant<true, false>), grid, block, 0, stream, xr, qr, sr, total,
-                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
-      else
-        hipLaunchKernelGGL((k_group_quant<false, false>), grid, block, 0, stream, xr, qr, sr, total,
-                           (uint32_t)gpr, magic, ldx, ldq, lds, eps);
+      if (mn) FP8BLK_GQ(false, false, 1); else FP8BLK_GQ(false, false, 0);
     }
+#undef FP8BLK_GQ
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -73,6 +73,14 @@ extern "C" {
                                 applied exactly by the matrix core (STANDARD
                                 only; results unspecified for other scales) */
 
+/* Scale output of fp8_group_quant for other consumers (German page,
+ * "Praktische Einschränkungen": UE8M0 scales for GEMMs that take them) */
+#define FP8BLK_FLAG_SCALE_E8M0 2u     /* one byte per scale: the biased exponent
+                                        b of the power-of-two scale 2^(b-127);
+                                        requires FP8BLK_FLAG_UE8M0 */
+#define FP8BLK_FLAG_SCALE_MN_MAJOR 4u /* scales stored [K/128][lds] (token index
+                                        contiguous), lds >= M */
+
 /* GEMM variants (autotuning page, section "Kernel Implementation") */
 #define FP8BLK_STANDARD 0 /* tiles over (M, N), loop over K */
 #define FP8BLK_SWAPAB 1   /* computes (W A^T)^T: weight rows on the matrix-core
@@ -125,10 +133,13 @@ const char *fp8_status_string(int status);
  *
  *   x     bf16 [M][ldx], ldx >= K        q  uint8 [M][ldq], ldq >= K
  *   s     fp32 [M][lds], lds >= K/128    group must be 128
+ *         (FP8BLK_FLAG_SCALE_MN_MAJOR: [K/128][lds], lds >= M;
+ *          FP8BLK_FLAG_SCALE_E8M0: uint8 E8M0 bytes in that layout)
+ *   flags: FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_SCALE_E8M0 | FP8BLK_FLAG_SCALE_MN_MAJOR.
  *   Requires K % 128 == 0, M >= 0, eps > 0 and finite.
  */
 int fp8_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                    uint8_t *q, int64_t ldq, float *s, int64_t lds,
+                    uint8_t *q, int64_t ldq, void *s, int64_t lds,
                     int32_t group, float eps, uint32_t flags, void *stream);
 
 /*

@@ -269,3 +269,11 @@ def test_dynamic_entry_argument_errors():
     assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=fb.SCALES_POW2)) == CFG
     assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=2)) == WS
     assert sm(M=0, a=None, sa=None, w=None, sw=None, y=None, cfg=std) == OK
+
+
+def test_group_quant_scale_format_flags():
+    # E8M0 bytes hold powers of two only; MN-major needs lds >= M; unknown bits rejected
+    assert _gq(flags=2) == CFG
+    assert _gq(flags=8) == CFG
+    assert _gq(M=4, flags=4, lds=3) == STRIDE
+    assert _gq(M=0, flags=1 | 2 | 4, x=None, q=None, s=None, lds=0) == OK

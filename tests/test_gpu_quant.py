@@ -199,3 +199,33 @@ def test_weight_block_quant(N, K, ue8m0):
     q, s = host(q), host(s)
     rq, rs = oracle.weight_block_quant(w, ue8m0=ue8m0) if N == 256 else oracle_weight(N, K, ue8m0)
     assert np.array_equal(s, rs) and np.array_equal(q, rq)
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (37, 1152), (8192, 4096)])
+def test_scale_output_formats(M, K):
+    """Packed E8M0 scale bytes and MN-major scale layout: the same codes, and
+    scales that are the oracle's fp32 scales re-laid out (E8M0 byte = the
+    biased exponent of the power-of-two scale)."""
+    import torch
+    case = synth.Case("sweep", "fmt", M, 128, K, "student_t3", True, 77)
+    x = synth.activations_bf16(case)
+    q_ref, s_ref = oracle.group_quant(x, ue8m0=True)
+    e8_ref = (s_ref.view(np.uint32) >> 23).astype(np.uint8)
+    xd = to_dev_bf16(x)
+    G = K // 128
+    for e8m0 in (False, True):
+        for mn in (False, True):
+            say("scale format", M, K, "e8m0" if e8m0 else "fp32", "mn" if mn else "row")
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev())
+            dt = torch.uint8 if e8m0 else torch.float32
+            pad = 8
+            s = torch.full((G, M + pad) if mn else (M, G + pad), 0x5A if e8m0 else -1.0, dtype=dt, device=dev())
+            sv = s[:, :M] if mn else s[:, :G]
+            fb.fp8_group_quant(xd, q, sv, ue8m0=True, scale_e8m0=e8m0, scale_mn_major=mn)
+            sh = host(s)
+            assert np.array_equal(host(q), q_ref)
+            want = e8_ref if e8m0 else s_ref
+            got = sh[:, :M].T if mn else sh[:, :G]
+            assert np.array_equal(got, want)
+            padv = sh[:, M:] if mn else sh[:, G:]
+            assert np.all(padv == (0x5A if e8m0 else -1.0)), "padding written"
