@@ -63,6 +63,10 @@ def _load():
     lib.orc_token_quant_mt.argtypes = [P, I64, I64, I64, P, I64, P, ctypes.c_float, ctypes.c_int, ctypes.c_int]
     lib.orc_channel_quant.restype = None
     lib.orc_channel_quant.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_rms_norm_per_block_quant.restype = None
+    lib.orc_rms_norm_per_block_quant.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_silu_and_mul_per_block_quant.restype = None
+    lib.orc_silu_and_mul_per_block_quant.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int]
     lib.orc_scaled_mm.restype = ctypes.c_int
     lib.orc_scaled_mm.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
     _lib = lib
@@ -213,6 +217,36 @@ def scaled_mm(qa, sa, qw, sw, rows=None, nthreads: int | None = None) -> np.ndar
         lib.orc_scaled_mm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, rows_ptr, nrows,
                           _ptr(y), nthreads or default_threads())
     return y
+
+
+def rms_norm_per_block_quant(x_bf16_bits: np.ndarray, w: np.ndarray, eps_norm=1e-6,
+                             eps=DEFAULT_EPS, ue8m0: bool = False):
+    """rms_norm_per_block_quant: RMSNorm of bf16 X [M, H] with fp32 weight [H],
+    then the 1x128 group quantizer.  Returns (q uint8 [M, H], s float32 [M, H/128])."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    M, H = x.shape
+    assert H % GROUP == 0 and w.shape == (H,)
+    q = np.empty((M, H), dtype=np.uint8)
+    s = np.empty((M, H // GROUP), dtype=np.float32)
+    lib.orc_rms_norm_per_block_quant(_ptr(x), _ptr(w), M, H, float(np.float32(eps_norm)), _ptr(q), _ptr(s),
+                                 float(np.float32(eps)), int(ue8m0))
+    return q, s
+
+
+def silu_and_mul_per_block_quant(x_bf16_bits: np.ndarray, eps=DEFAULT_EPS, ue8m0: bool = False):
+    """silu_and_mul_per_block_quant of bf16 X [M, 2I] = [gate | up]: SiLU(gate) * up,
+    then the 1x128 group quantizer.  Returns (q uint8 [M, I], s float32 [M, I/128])."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, I2 = x.shape
+    I = I2 // 2
+    assert I2 % 2 == 0 and I % GROUP == 0
+    q = np.empty((M, I), dtype=np.uint8)
+    s = np.empty((M, I // GROUP), dtype=np.float32)
+    lib.orc_silu_and_mul_per_block_quant(_ptr(x), M, I, _ptr(q), _ptr(s), float(np.float32(eps)), int(ue8m0))
+    return q, s
 
 
 def lib_path() -> str:

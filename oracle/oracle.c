@@ -30,6 +30,19 @@
  *     group is the whole row) and one per row of W, the same amax / scale /
  *     encode rule as the group quantizer.
  *
+ *   - The fused producers rms_norm_per_block_quant and
+ *     silu_and_mul_per_block_quant (German page, section "Welche Kernel
+ *     wurden in vLLM integriert"; RFC page, section "Motivation"): RMSNorm,
+ *     respectively SiLU(gate) * up, followed by the 1x128 group quantizer.
+ *     RMSNorm follows the fp8 RMSNorm example of the Chinese Helion article
+ *     (zdabc.icu), section "自己写一个 Helion kernel 并接入 vLLM": variance =
+ *     sum of squares / hidden size, rms = sqrt(variance + eps), normalized =
+ *     x / rms times the weight, the weight in fp32 as in that example.  The
+ *     pages fix no precision, so: the variance and
+ *     1/rms in double, 1/rms rounded once to float, then (x * (1/rms)) * w in
+ *     float; SiLU(g) * u = g / (1 + exp(-g)) * u in double, rounded once to
+ *     float.  The quantizer then divides by the scale in IEEE float.
+ *
  * The pages do not print the e4m3fn bit layout, the rounding mode, the
  * saturation rule, the all-zero-group rule or the scale layouts.  The
  * readings taken here (OCP e4m3fn, round to nearest with ties to even,
@@ -228,6 +241,55 @@ void orc_channel_quant(const float *w, int64_t N, int64_t K, uint8_t *q, float *
 {
     for (int64_t n = 0; n < N; ++n)
         s[n] = quantize_row(w + n * K, K, q + n * K, eps, ue8m0);
+}
+
+/* ------------------------------------------------------------------ */
+/* fused producers: RMSNorm / SiLU-and-mul, then the group quantizer   */
+/* ------------------------------------------------------------------ */
+
+/* Group quantization of one row of float values already computed. */
+static void group_quant_row(const float *y, int64_t n, uint8_t *q, float *s, float eps, int ue8m0)
+{
+    for (int64_t g = 0; g < n / ORC_GROUP; ++g)
+        s[g] = quantize_row(y + g * ORC_GROUP, ORC_GROUP, q + g * ORC_GROUP, eps, ue8m0);
+}
+
+/* rms_norm_per_block_quant: x bf16 [M][H], w fp32 [H] -> q [M][H], s [M][H/128]. */
+void orc_rms_norm_per_block_quant(const uint16_t *x, const float *w, int64_t M, int64_t H,
+                              float eps_norm, uint8_t *q, float *s, float eps, int ue8m0)
+{
+    float *y = (float *)malloc((size_t)H * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * H;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = (double)bf16_value(xr[j]);
+            ss += v * v;
+        }
+        double var = ss / (double)H;
+        float r = (float)(1.0 / sqrt(var + (double)eps_norm));
+        for (int64_t j = 0; j < H; ++j)
+            y[j] = (bf16_value(xr[j]) * r) * w[j];
+        group_quant_row(y, H, q + m * H, s + m * (H / ORC_GROUP), eps, ue8m0);
+    }
+    free(y);
+}
+
+/* silu_and_mul_per_block_quant: x bf16 [M][2I] = [gate | up] -> q [M][I], s [M][I/128]. */
+void orc_silu_and_mul_per_block_quant(const uint16_t *x, int64_t M, int64_t I, uint8_t *q, float *s,
+                              float eps, int ue8m0)
+{
+    float *y = (float *)malloc((size_t)I * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * 2 * I;
+        for (int64_t j = 0; j < I; ++j) {
+            double g = (double)bf16_value(xr[j]);
+            double u = (double)bf16_value(xr[I + j]);
+            y[j] = (float)(g / (1.0 + exp(-g)) * u);
+        }
+        group_quant_row(y, I, q + m * I, s + m * (I / ORC_GROUP), eps, ue8m0);
+    }
+    free(y);
 }
 
 /* ------------------------------------------------------------------ */
