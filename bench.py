@@ -150,6 +150,105 @@ def cpu_baseline(cases, xs, budget_s: float, dynamic: bool = False):
                       f"{threads} host threads"}
 
 
+PRODUCER_M = (1, 8, 32, 64, 8192)
+PRODUCER_H, PRODUCER_I = 4096, 12288  # Qwen3-8B hidden and intermediate sizes
+
+
+def producer_bytes(op: str, M: int) -> int:
+    """Algorithmic HBM bytes of one call: inputs read once, outputs written once."""
+    if op == "rms_norm_per_block_quant":
+        H = PRODUCER_H
+        return 2 * M * H + 4 * H + M * H + 4 * M * H // 128
+    I = PRODUCER_I
+    return 4 * M * I + M * I + 4 * M * I // 128
+
+
+def bench_producers(args) -> int:
+    """The fused producers of the GEMM's activation operand at Qwen3-8B sizes:
+    each call timed by replaying a graph of kernel_reps launches, HIP events
+    on the launch stream.  value = algorithmic GB/s over all cases."""
+    import torch
+    import numpy as np
+    import fp8_blockwise_quantized_token_amd as fb
+    import oracle
+    from fp8_blockwise_quantized_token_amd import synth
+
+    fb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    w = torch.from_numpy(synth.norm_weight_f32(PRODUCER_H)).to(dev)
+    cases = []
+    for op in ("rms_norm_per_block_quant", "silu_and_mul_per_block_quant"):
+        for M in PRODUCER_M:
+            K = PRODUCER_H if op.startswith("rms") else 2 * PRODUCER_I
+            xh = synth.activations_bf16(synth.Case("prefill_8b", "producer", M, 128, K, "normal_outlier",
+                                                   False, 7))
+            x = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
+            Ko = K if op.startswith("rms") else K // 2
+            q = torch.empty((M, Ko), dtype=torch.uint8, device=dev)
+            s = torch.empty((M, Ko // 128), dtype=torch.float32, device=dev)
+            if op.startswith("rms"):
+                fn = (lambda x=x, q=q, s=s: fb.fp8_rms_norm_per_block_quant(x, w, q, s, stream=stream))
+            else:
+                fn = (lambda x=x, q=q, s=s: fb.fp8_silu_and_mul_per_block_quant(x, q, s, stream=stream))
+            cases.append((op, M, xh, fn))
+    torch.cuda.synchronize()
+    reps = max(args.kernel_reps, 10)
+    rows = []
+    tot_b = tot_t = 0.0
+    for op, M, _, fn in cases:
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                fn()
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / (args.steps * reps)
+        b = producer_bytes(op, M)
+        tot_b += b
+        tot_t += t
+        rows.append({"op": op, "M": M, "us": round(t * 1e6, 2), "gbps": round(b / t / 1e9, 1),
+                     "hbm_frac": round(b / t / 1e9 / PEAK_HBM_GBPS, 4)})
+        print(f"[bench] {op} M={M}: {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    big = [r for r in rows if r["M"] == max(PRODUCER_M)]
+    out = {"metric": "fused producer GB/s (rms_norm / silu_and_mul + 1x128 group quant), Qwen3-8B sizes",
+           "value": round(tot_b / tot_t / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16-in/fp32-compute/e4m3-out", "data": "synthetic (seeded)",
+           "config": {"workload": "producers_qwen3_8b", "H": PRODUCER_H, "I": PRODUCER_I,
+                      "m_values": list(PRODUCER_M), "graph_replay": True, "launches_per_graph": reps},
+           "roofline": [{"bound": "hbm", "kernel": r["op"], "achieved": r["gbps"], "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": r["hbm_frac"], "traffic": None} for r in big],
+           "cases": rows}
+    if not args.no_cpu_baseline:
+        t_cpu = b_cpu = 0.0
+        for op, M, xh, _ in cases:
+            r = min(M, 256)
+            t0 = time.perf_counter()
+            if op.startswith("rms"):
+                oracle.rms_norm_per_block_quant(xh[:r], synth.norm_weight_f32(PRODUCER_H))
+            else:
+                oracle.silu_and_mul_per_block_quant(xh[:r])
+            t_cpu += time.perf_counter() - t0
+            b_cpu += producer_bytes(op, r)
+        out["cpu_baseline"] = {"value": round(b_cpu / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"first min(M, 256) rows of each case, {t_cpu:.1f} s on 1 host thread"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,12 +262,17 @@ def main() -> int:
     ap.add_argument("--format", choices=("block", "dynamic"), default="block",
                     help="block: Block_FP8 (1x128 / 128x128 scales, the default); "
                          "dynamic: FP8_Dynamic (per-token / per-channel scales)")
+    ap.add_argument("--op", choices=("linear", "producers"), default="linear",
+                    help="linear: the FP8 linear layer (default); producers: the fused "
+                         "rms_norm / silu_and_mul group-quant producers")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); the multi-GPU path is "
-              "design-only in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
+              "multi-GPU path.", file=sys.stderr)
         return 2
+    if args.op == "producers":
+        return bench_producers(args)
 
     import torch
     import numpy as np

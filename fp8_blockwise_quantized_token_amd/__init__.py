@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   fp8_token_quant        per-token quantization (FP8_Dynamic activations)
   fp8_weight_channel_quant  per-channel weight quantization (FP8_Dynamic weights)
   fp8_scaled_mm          GEMM with per-token / per-channel scales
+  fp8_rms_norm_per_block_quant      RMSNorm fused with the 1x128 group quantizer
+  fp8_silu_and_mul_per_block_quant  SiLU(gate) * up fused with the 1x128 group quantizer
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
 
+ABI_VERSION = 3  # FP8BLK_ABI_VERSION of the header this binding follows
 GROUP = 128
 FLAG_UE8M0 = 1
 STANDARD = 0
@@ -114,6 +117,13 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear.restype = ctypes.c_int
     L.fp8_linear.argtypes = [P, I64, P, P, I64, I64, P, I64, I64, I64, I64, F, U32,
                              ctypes.POINTER(GemmConfig), P, I64, P]
+    L.fp8_rms_norm_per_block_quant.restype = ctypes.c_int
+    L.fp8_rms_norm_per_block_quant.argtypes = [P, I64, I64, I64, P, F, P, I64, P, I64, F, U32, P]
+    L.fp8_silu_and_mul_per_block_quant.restype = ctypes.c_int
+    L.fp8_silu_and_mul_per_block_quant.argtypes = [P, I64, I64, I64, P, I64, P, I64, F, U32, P]
+    if L.fp8_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.fp8_abi_version()}, the binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -169,6 +179,50 @@ def fp8_group_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stre
     st = lib().fp8_group_quant(x.data_ptr(), M, K, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
                                s.data_ptr(), _ld(s, "s"), GROUP, eps, flags, _stream(stream))
     _check(st, "fp8_group_quant")
+
+
+def _scale_flags(ue8m0: bool, scale_e8m0: bool, scale_mn_major: bool) -> int:
+    return (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_SCALE_E8M0 if scale_e8m0 else 0) | \
+        (FLAG_SCALE_MN_MAJOR if scale_mn_major else 0)
+
+
+def _check_group_out(what: str, M: int, K: int, q, s, scale_e8m0: bool, scale_mn_major: bool) -> None:
+    srows = K // GROUP if scale_mn_major else M
+    if q.shape != (M, K) or q.element_size() != 1 or s.dim() != 2 or s.shape[0] != srows:
+        raise ValueError(f"{what}: output shape/dtype mismatch")
+    if s.element_size() != (1 if scale_e8m0 else 4):
+        raise ValueError(f"{what}: scale dtype mismatch")
+
+
+def fp8_rms_norm_per_block_quant(x, weight, q, s, eps_norm: float = 1e-6, eps: float = DEFAULT_EPS,
+                                 ue8m0: bool = False, stream=None, scale_e8m0: bool = False,
+                                 scale_mn_major: bool = False) -> None:
+    """x: bf16 [M, H], weight: float32 [H] (contiguous), q: 1-byte [M, H],
+    s: float32 [M, H/128] (MN-major / E8M0 as fp8_group_quant)."""
+    M, H = x.shape
+    if x.element_size() != 2 or weight.element_size() != 4 or tuple(weight.shape) != (H,) \
+            or not weight.is_contiguous():
+        raise ValueError("fp8_rms_norm_per_block_quant: x/weight shape or dtype mismatch")
+    _check_group_out("fp8_rms_norm_per_block_quant", M, H, q, s, scale_e8m0, scale_mn_major)
+    st = lib().fp8_rms_norm_per_block_quant(x.data_ptr(), M, H, _ld(x, "x"), weight.data_ptr(), eps_norm,
+                                            q.data_ptr(), _ld(q, "q"), s.data_ptr(), _ld(s, "s"), eps,
+                                            _scale_flags(ue8m0, scale_e8m0, scale_mn_major), _stream(stream))
+    _check(st, "fp8_rms_norm_per_block_quant")
+
+
+def fp8_silu_and_mul_per_block_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None,
+                                     scale_e8m0: bool = False, scale_mn_major: bool = False) -> None:
+    """x: bf16 [M, 2I] = [gate | up], q: 1-byte [M, I], s: float32 [M, I/128]."""
+    M, I2 = x.shape
+    if x.element_size() != 2 or I2 % 2 != 0:
+        raise ValueError("fp8_silu_and_mul_per_block_quant: x shape or dtype mismatch")
+    I = I2 // 2
+    _check_group_out("fp8_silu_and_mul_per_block_quant", M, I, q, s, scale_e8m0, scale_mn_major)
+    st = lib().fp8_silu_and_mul_per_block_quant(x.data_ptr(), M, I, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
+                                                s.data_ptr(), _ld(s, "s"), eps,
+                                                _scale_flags(ue8m0, scale_e8m0, scale_mn_major),
+                                                _stream(stream))
+    _check(st, "fp8_silu_and_mul_per_block_quant")
 
 
 def fp8_weight_block_quant(w, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:
@@ -365,3 +419,24 @@ def dynamic_linear(x, qw, sw, eps: float = DEFAULT_EPS, cfg: GemmConfig | None =
     """The FP8_Dynamic linear layer: per-token quantization of x, then scaled_mm."""
     qa, sa = quantize_tokens(x, eps, False, stream)
     return scaled_mm(qa, sa, qw, sw, cfg, stream)
+
+
+def rms_norm_quant(x, weight, eps_norm: float = 1e-6, eps: float = DEFAULT_EPS, ue8m0: bool = False,
+                   stream=None):
+    """rms_norm_per_block_quant into new tensors: (q uint8 [M, H], s float32 [M, H/128])."""
+    import torch
+    M, H = x.shape
+    q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, H // GROUP), dtype=torch.float32, device=x.device)
+    fp8_rms_norm_per_block_quant(x, weight, q, s, eps_norm, eps, ue8m0, stream)
+    return q, s
+
+
+def silu_and_mul_quant(x, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None):
+    """silu_and_mul_per_block_quant into new tensors: (q uint8 [M, I], s float32 [M, I/128])."""
+    import torch
+    M, I2 = x.shape
+    q = torch.empty((M, I2 // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, I2 // 2 // GROUP), dtype=torch.float32, device=x.device)
+    fp8_silu_and_mul_per_block_quant(x, q, s, eps, ue8m0, stream)
+    return q, s

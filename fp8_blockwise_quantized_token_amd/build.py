@@ -17,7 +17,7 @@ OUT_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(OUT_DIR, "libfp8blk.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_standard.hip", "dispatch.cpp"]
+SOURCES = ["api.hip", "quant.hip", "fused.hip", "gemm.hip", "gemm_standard.hip", "dispatch.cpp"]
 ARCH = "gfx950"
 
 

@@ -82,6 +82,19 @@ LinearLayout linear_layout(const fp8blk_gemm_config& c, int64_t M, int64_t N, in
   return L;
 }
 
+// Scale output of the group quantizers: flags, layout and pitch.  *fmt gets
+// bit 0 = MN-major, bit 1 = E8M0 bytes.
+int check_group_scales(uint32_t flags, int64_t M, int64_t K, int64_t lds, int* fmt) {
+  const uint32_t known = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_SCALE_E8M0 | FP8BLK_FLAG_SCALE_MN_MAJOR;
+  if ((flags & ~known) != 0) return FP8BLK_ERR_BAD_CONFIG;
+  const bool e8m0 = (flags & FP8BLK_FLAG_SCALE_E8M0) != 0;
+  const bool mn = (flags & FP8BLK_FLAG_SCALE_MN_MAJOR) != 0;
+  if (e8m0 && !(flags & FP8BLK_FLAG_UE8M0)) return FP8BLK_ERR_BAD_CONFIG;  // E8M0 holds powers of two only
+  if (lds < (mn ? M : K / kG)) return FP8BLK_ERR_BAD_STRIDE;
+  *fmt = (mn ? 1 : 0) | (e8m0 ? 2 : 0);
+  return FP8BLK_OK;
+}
+
 int check_quant_args(float eps, uint32_t flags) {
   if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
   if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
@@ -113,19 +126,16 @@ int fp8_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_
   if (group != kG) return FP8BLK_ERR_BAD_SHAPE;
   if (M < 0 || K <= 0 || K % kG != 0 || K > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
   if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
-  const uint32_t known = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_SCALE_E8M0 | FP8BLK_FLAG_SCALE_MN_MAJOR;
-  if ((flags & ~known) != 0) return FP8BLK_ERR_BAD_CONFIG;
-  const bool e8m0 = (flags & FP8BLK_FLAG_SCALE_E8M0) != 0;
-  const bool mn = (flags & FP8BLK_FLAG_SCALE_MN_MAJOR) != 0;
-  if (e8m0 && !(flags & FP8BLK_FLAG_UE8M0)) return FP8BLK_ERR_BAD_CONFIG;  // E8M0 holds powers of two only
-  if (ldx < K || ldq < K || lds < (mn ? M : K / kG)) return FP8BLK_ERR_BAD_STRIDE;
+  int fmt = 0;
+  const int st = check_group_scales(flags, M, K, lds, &fmt);
+  if (st != FP8BLK_OK) return st;
+  if (ldx < K || ldq < K) return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;
   if (!x || !q || !s) return FP8BLK_ERR_NULL_PTR;
-  if (!aligned16(x) || !aligned16(q) || (!e8m0 && !aligned4(s)) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+  if (!aligned16(x) || !aligned16(q) || (!(fmt & 2) && !aligned4(s)) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
     return FP8BLK_ERR_MISALIGNED;
   return to_status(fp8blk::launch_group_quant(x, M, K, ldx, q, ldq, s, lds, eps,
-                                              (flags & FP8BLK_FLAG_UE8M0) != 0,
-                                              (mn ? 1 : 0) | (e8m0 ? 2 : 0), (hipStream_t)stream));
+                                              (flags & FP8BLK_FLAG_UE8M0) != 0, fmt, (hipStream_t)stream));
 }
 
 int fp8_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
@@ -377,6 +387,42 @@ int fp8_scaled_mm(const uint8_t* a, const float* sa, int64_t lda, const uint8_t*
     return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages,
                                                   fp8blk::kScalesChannel, s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s, true));
+}
+
+int fp8_rms_norm_per_block_quant(const uint16_t* x, int64_t M, int64_t H, int64_t ldx, const float* weight,
+                                 float eps_norm, uint8_t* q, int64_t ldq, void* s, int64_t lds, float eps,
+                                 uint32_t flags, void* stream) {
+  if (M < 0 || H <= 0 || H % kG != 0 || H > fp8blk::kRmsMaxH || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps > 0.0f) || !isfinite(eps) || !(eps_norm >= 0.0f) || !isfinite(eps_norm))
+    return FP8BLK_ERR_BAD_SHAPE;
+  int fmt = 0;
+  const int st = check_group_scales(flags, M, H, lds, &fmt);
+  if (st != FP8BLK_OK) return st;
+  if (ldx < H || ldq < H) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !weight || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(q) || (!(fmt & 2) && !aligned4(s)) ||
+      (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_rms_norm_quant(x, M, H, ldx, weight, eps_norm, q, ldq, s, lds, eps,
+                                                 (flags & FP8BLK_FLAG_UE8M0) != 0, fmt, (hipStream_t)stream));
+}
+
+int fp8_silu_and_mul_per_block_quant(const uint16_t* x, int64_t M, int64_t I, int64_t ldx, uint8_t* q,
+                                     int64_t ldq, void* s, int64_t lds, float eps, uint32_t flags,
+                                     void* stream) {
+  if (M < 0 || I <= 0 || I % kG != 0 || I > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  int fmt = 0;
+  const int st = check_group_scales(flags, M, I, lds, &fmt);
+  if (st != FP8BLK_OK) return st;
+  if (ldx < 2 * I || ldq < I) return FP8BLK_ERR_BAD_STRIDE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !q || !s) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(q) || (!(fmt & 2) && !aligned4(s)) || (ldx * 2) % 16 != 0 || ldq % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  return to_status(fp8blk::launch_silu_mul_quant(x, M, I, ldx, q, ldq, s, lds, eps,
+                                                 (flags & FP8BLK_FLAG_UE8M0) != 0, fmt, (hipStream_t)stream));
 }
 
 }  // extern "C"

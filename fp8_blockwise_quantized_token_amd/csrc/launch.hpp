@@ -25,6 +25,16 @@ hipError_t launch_row_quant(const void* x, bool bf16, int64_t rows, int64_t K, i
                             uint8_t* q, int64_t ldq, float* s, float eps, bool ue8m0,
                             hipStream_t stream);
 
+// Fused producers of the activation operand: RMSNorm (H <= kRmsMaxH) or
+// SiLU(gate) * up, then 1x128 group quantization (scale_format as above).
+constexpr int64_t kRmsMaxH = 32768;
+hipError_t launch_rms_norm_quant(const uint16_t* x, int64_t M, int64_t H, int64_t ldx, const float* w,
+                                 float eps_norm, uint8_t* q, int64_t ldq, void* s, int64_t lds,
+                                 float eps, bool ue8m0, int scale_format, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const uint16_t* x, int64_t M, int64_t I, int64_t ldx, uint8_t* q,
+                                 int64_t ldq, void* s, int64_t lds, float eps, bool ue8m0,
+                                 int scale_format, hipStream_t stream);
+
 struct GemmArgs {
   const uint8_t* a;
   const float* sa;

@@ -15,7 +15,10 @@ Kernel Performance"):
   ue8m0_32b     M in {64,4096} x Qwen3-32B (N,K), outliers, power-of-two scales
   sweep         M in {1,2,...,16384} x Qwen3-1.7B/8B/32B (N,K), X ~ Student-t(3)
 Weights are W ~ N(0, 0.02) in fp32 (standard deviation 0.02); the quantized
-weights are produced from them by a block quantizer (not here).
+weights are produced from them by a block quantizer (not here).  The fused
+producers take the same activation recipes: RMSNorm input X [M, H] with an
+fp32 weight 1 + 0.25 N(0,1); SiLU-and-mul input [M, 2I] = [gate | up] drawn
+as one activation matrix of width 2I.
 
 Real checkpoints and the pages' serving datasets are not available; these
 synthetic tensors of the same shapes stand in for them.
@@ -165,6 +168,12 @@ def weights_f32(case_or_n, K: int | None = None) -> np.ndarray:
     w = _chunked(N, K, (7, N, K, 1), _fill_normal)
     w *= np.float32(0.02)
     return w
+
+
+def norm_weight_f32(H: int) -> np.ndarray:
+    """RMSNorm weight [H] in fp32: 1 + 0.25 N(0, 1), one draw per H."""
+    w = _rng(8, H).standard_normal(H, dtype=np.float32)
+    return (np.float32(1.0) + np.float32(0.25) * w).astype(np.float32)
 
 
 def uniform_f32(shape, lo: float, hi: float, *key: int) -> np.ndarray:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 2
+#define FP8BLK_ABI_VERSION 3
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
 
@@ -288,6 +288,48 @@ int fp8_scaled_mm(const uint8_t *a, const float *sa, int64_t lda,
                   uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                   const fp8blk_gemm_config *cfg, void *workspace,
                   int64_t workspace_bytes, void *stream);
+
+/*
+ * rms_norm_per_block_quant -- RMSNorm fused with the 1x128 group quantizer
+ * (German page, "Welche Kernel wurden in vLLM integriert"; RFC page,
+ * "Motivation").  RMSNorm as in the fp8 RMSNorm example of the Chinese
+ * Helion article ("自己写一个 Helion kernel 并接入 vLLM"):
+ *   r       = fp32( 1 / sqrt( (sum_j x[m][j]^2) / H + eps_norm ) )   (fp64)
+ *   y[m][j] = (x[m][j] * r) * weight[j]                              (fp32)
+ * then, per 128-group of y, exactly fp8_group_quant's rule (the scale from
+ * the fp32 amax of y; the codes of y / s).  y is never stored.
+ *   x      bf16 [M][ldx], ldx >= H        weight fp32 [H]
+ *   q      uint8 [M][ldq], ldq >= H
+ *   s      as fp8_group_quant's with K = H (fp32 [M][lds], lds >= H/128;
+ *          MN-major / E8M0 by the same flags)
+ *   Requires H % 128 == 0, H <= 32768, M >= 0, eps > 0, eps_norm >= 0
+ *   (both finite).  x, weight, q 16-byte aligned; ldx * 2 and ldq multiples
+ *   of 16.  Finite inputs only.
+ */
+int fp8_rms_norm_per_block_quant(const uint16_t *x, int64_t M, int64_t H, int64_t ldx,
+                                 const float *weight, float eps_norm,
+                                 uint8_t *q, int64_t ldq, void *s, int64_t lds,
+                                 float eps, uint32_t flags, void *stream);
+
+/*
+ * silu_and_mul_per_block_quant -- SiLU(gate) * up fused with the 1x128
+ * group quantizer (German page, "Welche Kernel wurden in vLLM integriert";
+ * RFC page, "Motivation").  Row m of x holds [gate | up], I values each:
+ *   y[m][j] = silu(g) * u = (g * u) / (1 + exp(-g)),  g = x[m][j], u = x[m][I + j]
+ * in fp32, then fp8_group_quant's rule on every 128-group of y.  The
+ * division is corrected to within a fraction of an ulp and exp is within
+ * an ulp, so y may differ from the correctly rounded value by up to about
+ * 1.5 ulp; codes can then
+ * differ by one step next to a rounding midpoint.  exp(-g) is capped at
+ * exp(80): for g < -80, |y| < 1e-30 |g u| either way.
+ *   x  bf16 [M][ldx], ldx >= 2I          q uint8 [M][ldq], ldq >= I
+ *   s  as fp8_group_quant's with K = I
+ *   Requires I % 128 == 0, I <= 4194304, M >= 0, eps > 0 and finite; alignment as
+ *   fp8_group_quant.  Finite inputs only.
+ */
+int fp8_silu_and_mul_per_block_quant(const uint16_t *x, int64_t M, int64_t I, int64_t ldx,
+                                     uint8_t *q, int64_t ldq, void *s, int64_t lds,
+                                     float eps, uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fb.fp8_abi_version() == 2
+    assert fb.fp8_abi_version() == fb.ABI_VERSION == 3
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert fb.fp8_status_string(st) != "unknown status"
     assert fb.fp8_status_string(-99) == "unknown status"
@@ -277,3 +277,33 @@ def test_group_quant_scale_format_flags():
     assert _gq(flags=8) == CFG
     assert _gq(M=4, flags=4, lds=3) == STRIDE
     assert _gq(M=0, flags=1 | 2 | 4, x=None, q=None, s=None, lds=0) == OK
+
+
+def test_header_abi_version_matches_the_binding():
+    m = re.search(r"#define\s+FP8BLK_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == fb.ABI_VERSION
+
+
+def test_fused_producer_argument_errors():
+    L = fb.lib()
+    rq = lambda x=A, M=4, H=256, ldx=256, w=D, en=1e-6, q=B, ldq=256, s=C, lds=2, eps=1e-10, flags=0: \
+        L.fp8_rms_norm_per_block_quant(x, M, H, ldx, w, en, q, ldq, s, lds, eps, flags, None)
+    assert rq(x=None) == NULL and rq(w=None) == NULL and rq(q=None) == NULL and rq(s=None) == NULL
+    assert rq(H=200, ldx=256, ldq=256) == SHAPE and rq(H=0) == SHAPE and rq(M=-1) == SHAPE
+    assert rq(H=32768 + 128, ldx=40000, ldq=40000, lds=300) == SHAPE
+    assert rq(eps=0.0) == SHAPE and rq(en=-1.0) == SHAPE and rq(en=float("inf")) == SHAPE
+    assert rq(en=float("nan")) == SHAPE
+    assert rq(ldx=128) == STRIDE and rq(ldq=128) == STRIDE and rq(lds=1) == STRIDE
+    assert rq(flags=2) == CFG and rq(flags=8) == CFG and rq(flags=4, lds=3) == STRIDE
+    assert rq(x=A + 2) == MISAL and rq(w=D + 4) == MISAL and rq(q=B + 8) == MISAL
+    assert rq(s=C + 2) == MISAL and rq(ldx=260) == MISAL and rq(ldq=264) == MISAL
+    assert rq(M=0, x=None, w=None, q=None, s=None) == OK
+    sq = lambda x=A, M=4, I=256, ldx=512, q=B, ldq=256, s=C, lds=2, eps=1e-10, flags=0: \
+        L.fp8_silu_and_mul_per_block_quant(x, M, I, ldx, q, ldq, s, lds, eps, flags, None)
+    assert sq(x=None) == NULL and sq(q=None) == NULL and sq(s=None) == NULL
+    assert sq(I=200, ldx=512, ldq=256) == SHAPE and sq(I=0) == SHAPE and sq(M=-1) == SHAPE
+    assert sq(eps=0.0) == SHAPE and sq(flags=2) == CFG and sq(flags=16) == CFG
+    assert sq(ldx=511) == STRIDE and sq(ldx=256) == STRIDE and sq(ldq=128) == STRIDE
+    assert sq(lds=1) == STRIDE and sq(flags=4, lds=3) == STRIDE
+    assert sq(x=A + 2) == MISAL and sq(ldx=516) == MISAL and sq(s=C + 2) == MISAL
+    assert sq(M=0, x=None, q=None, s=None) == OK

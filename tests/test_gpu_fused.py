@@ -1,0 +1,224 @@
+"""GPU parity of the fused producers rms_norm_per_block_quant and
+silu_and_mul_per_block_quant against the CPU oracle, through the C ABI.
+
+RMSNorm: the kernel takes every precision decision the oracle takes (sum of
+squares of bf16 values in fp64, 1/sqrt in fp64 rounded once to fp32, two
+fp32 products, fp32 quotient by the scale), so codes and scales must match
+bit for bit.  The only freedom is the order of the fp64 additions; for the
+seeded inputs here that does not reach the fp32 rounding of 1/rms.
+
+SiLU-and-mul: the kernel's fp32 SiLU (expf within an ulp, corrected division)
+can differ from the oracle's once-rounded double by up to about 1.5 ulp, so a
+result is accepted
+when every scale is within 2 ulp of the oracle's (and most are identical)
+and every code equals the oracle's or is its neighbour, with neighbours in
+at most 1e-4 of the positions (codes flip only next to a rounding midpoint).
+"""
+import numpy as np
+import pytest
+
+import fp8_blockwise_quantized_token_amd as fb
+import oracle
+from fp8_blockwise_quantized_token_amd import synth
+
+from gpu_common import dev, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+EPS = np.float32(1e-10)
+
+
+def _x(M, K, key, dist="normal_outlier"):
+    return synth.activations_bf16(synth.Case("sweep", "fused", M, 128, K, dist, False, 500 + key))
+
+
+def _gpu_rms(x, w, eps_norm, ue8m0):
+    q, s = fb.rms_norm_quant(to_dev_bf16(x), to_dev(w), eps_norm=eps_norm, ue8m0=ue8m0)
+    return host(q), host(s)
+
+
+def _gpu_silu(x, ue8m0):
+    q, s = fb.silu_and_mul_quant(to_dev_bf16(x), ue8m0=ue8m0)
+    return host(q), host(s)
+
+
+def _assert_exact(q, s, rq, rs, what):
+    if not np.array_equal(s, rs):
+        bad = np.argwhere(s != rs)[:5]
+        raise AssertionError((what, "scales", [(tuple(i), s[tuple(i)], rs[tuple(i)]) for i in bad]))
+    if not np.array_equal(q, rq):
+        bad = np.argwhere(q != rq)[:5]
+        raise AssertionError((what, "codes", [(tuple(i), q[tuple(i)], rq[tuple(i)]) for i in bad]))
+
+
+def _assert_near(q, s, rq, rs, what, max_flip=1e-4):
+    rel = np.abs(s.astype(np.float64) - rs) / rs
+    assert np.all(rel <= 2.0 ** -22), (what, "scale off by more than 2 ulp", float(rel.max()))
+    if s.size >= 64:
+        assert np.mean(s == rs) > 0.9, (what, "too few identical scales", float(np.mean(s == rs)))
+    diff = q != rq
+    if diff.any():
+        same_sign = (q & 0x80) == (rq & 0x80)
+        step = np.abs((q & 0x7F).astype(np.int32) - (rq & 0x7F).astype(np.int32))
+        assert np.all(same_sign & (step <= 1)), (what, "a code differs by more than one step")
+        assert np.mean(diff) <= max_flip, (what, "too many neighbouring codes", float(np.mean(diff)))
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+# H covers every kernel shape: one wave per row with 1, 2, 4, 8, 12, 16
+# vectors per lane (partly masked for 384, 640, 5120), and four waves per
+# row (12288, 16384, 32768).  M covers 1, ragged multiples of the 4 rows a
+# workgroup holds, and several hundred rows.
+RMS_CASES = [(1, 128), (3, 384), (5, 640), (7, 2048), (17, 4096), (33, 5120), (2, 6144),
+             (9, 8192), (6, 12288), (4, 16384), (3, 32768), (301, 4096), (64, 2048)]
+
+
+@pytest.mark.parametrize("M,H", RMS_CASES)
+def test_rms_norm_quant_matches_oracle(M, H):
+    x = _x(M, H, H % 97)
+    w = synth.norm_weight_f32(H)
+    for ue8m0 in (False, True):
+        say("rms_norm_per_block_quant", M, H, "ue8m0" if ue8m0 else "fp32")
+        q, s = _gpu_rms(x, w, 1e-6, ue8m0)
+        rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6, ue8m0=ue8m0)
+        _assert_exact(q, s, rq, rs, (M, H, ue8m0))
+
+
+@pytest.mark.parametrize("M,H", [(8192, 4096), (4096, 5120), (16384, 2048)])
+def test_rms_norm_quant_full_size(M, H):
+    # Qwen3-8B / 32B / 1.7B hidden sizes at prefill token counts
+    x = _x(M, H, 7)
+    w = synth.norm_weight_f32(H)
+    say("rms_norm_per_block_quant full size", M, H)
+    q, s = _gpu_rms(x, w, 1e-6, False)
+    rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6)
+    _assert_exact(q, s, rq, rs, (M, H))
+
+
+def test_rms_norm_quant_edge_rows():
+    import torch
+    H = 1024
+    rows = np.zeros((6, H), np.float32)
+    rows[1] = 3.0                                   # constant row
+    rows[2, 100] = -96.0                            # one nonzero value
+    rows[3] = 2.0 ** -60                            # tiny values: eps_norm dominates
+    rows[4, ::2], rows[4, 1::2] = 448.0, -1e-3      # wide dynamic range
+    rows[5] = np.where(np.arange(H) % 3 == 0, -0.0, 0.0)  # signed zeros
+    x = synth.to_bf16_bits(rows)
+    w = synth.norm_weight_f32(H)
+    for eps_norm in (1e-6, 0.0, 1e-2):
+        for ue8m0 in (False, True):
+            if eps_norm == 0.0:
+                xs, wn = x[1:5], w                  # the zero rows would divide by zero
+            else:
+                xs, wn = x, w
+            say("rms edge rows", eps_norm, ue8m0)
+            q, s = _gpu_rms(xs, wn, eps_norm, ue8m0)
+            rq, rs = oracle.rms_norm_per_block_quant(xs, wn, eps_norm=eps_norm, ue8m0=ue8m0)
+            _assert_exact(q, s, rq, rs, ("edge", eps_norm, ue8m0))
+    # M = 0 is a no-op
+    q, s = fb.rms_norm_quant(torch.empty((0, H), dtype=torch.bfloat16, device=dev()), to_dev(w))
+    assert q.shape == (0, H)
+
+
+def test_rms_norm_quant_strided_formats_and_padding():
+    import torch
+    M, H = 37, 1152
+    G = H // 128
+    x = _x(M, H, 11)
+    w = synth.norm_weight_f32(H)
+    big = np.zeros((M, H + 64), np.uint16)
+    big[:, :H] = x
+    xd = to_dev_bf16(big)[:, :H]
+    wd = to_dev(w)
+    rq, rs = oracle.rms_norm_per_block_quant(x, w, ue8m0=True)
+    e8 = (rs.view(np.uint32) >> 23).astype(np.uint8)
+    for e8m0 in (False, True):
+        for mn in (False, True):
+            say("rms strided", "e8m0" if e8m0 else "fp32", "mn" if mn else "row")
+            q = torch.full((M, H + 48), 0xAB, dtype=torch.uint8, device=dev())
+            dt = torch.uint8 if e8m0 else torch.float32
+            s = torch.full((G, M + 8) if mn else (M, G + 8), 0x5A if e8m0 else -1.0, dtype=dt, device=dev())
+            sv = s[:, :M] if mn else s[:, :G]
+            fb.fp8_rms_norm_per_block_quant(xd, wd, q[:, :H], sv, ue8m0=True, scale_e8m0=e8m0,
+                                            scale_mn_major=mn)
+            qh, sh = host(q), host(s)
+            assert np.array_equal(qh[:, :H], rq) and np.all(qh[:, H:] == 0xAB)
+            got = sh[:, :M].T if mn else sh[:, :G]
+            assert np.array_equal(got, e8 if e8m0 else rs)
+            assert np.all((sh[:, M:] if mn else sh[:, G:]) == (0x5A if e8m0 else -1.0))
+
+
+# ------------------------------------------------------------ SiLU and mul
+
+SILU_CASES = [(1, 128), (3, 256), (5, 384), (64, 6144), (7, 12288), (2, 25600), (129, 1024)]
+
+
+@pytest.mark.parametrize("M,I", SILU_CASES)
+def test_silu_and_mul_quant_matches_oracle(M, I):
+    x = _x(M, 2 * I, I % 89)
+    for ue8m0 in (False, True):
+        say("silu_and_mul_per_block_quant", M, I, "ue8m0" if ue8m0 else "fp32")
+        q, s = _gpu_silu(x, ue8m0)
+        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
+        # power-of-two scales: the ceiling absorbs the few-ulp differences
+        if ue8m0:
+            assert np.array_equal(s, rs)
+        # tiny cases: a single flip would exceed the rate bound, allow one
+        _assert_near(q, s, rq, rs, (M, I, ue8m0), max_flip=max(1e-4, 1.0 / q.size))
+
+
+@pytest.mark.parametrize("M,I", [(8192, 12288), (4096, 25600)])
+def test_silu_and_mul_quant_full_size(M, I):
+    # Qwen3-8B / 32B intermediate sizes at prefill token counts
+    x = _x(M, 2 * I, 3)
+    say("silu_and_mul_per_block_quant full size", M, I)
+    q, s = _gpu_silu(x, False)
+    rq, rs = oracle.silu_and_mul_per_block_quant(x)
+    _assert_near(q, s, rq, rs, (M, I))
+
+
+def test_silu_and_mul_quant_special_gates():
+    # large positive gates (silu = gate), very negative gates (signed zeros),
+    # zero gates, mixed in one row: exact agreement expected
+    I = 512
+    gen = synth.generator(51)
+    gate = np.empty((4, I), np.float32)
+    gate[0] = gen.uniform(40.0, 200.0, I)
+    gate[1] = -gen.uniform(100.0, 3e4, I)
+    gate[2] = 0.0
+    gate[3, ::2], gate[3, 1::2] = 64.0, -90.0
+    up = gen.standard_normal((4, I)).astype(np.float32)
+    x = synth.to_bf16_bits(np.concatenate([gate, up], axis=1))
+    for ue8m0 in (False, True):
+        say("silu special gates", ue8m0)
+        q, s = _gpu_silu(x, ue8m0)
+        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
+        _assert_exact(q, s, rq, rs, ("special", ue8m0))
+
+
+def test_silu_and_mul_quant_strided_formats_and_padding():
+    import torch
+    M, I = 21, 640
+    G = I // 128
+    x = _x(M, 2 * I, 13)
+    big = np.zeros((M, 2 * I + 32), np.uint16)
+    big[:, :2 * I] = x
+    xd = to_dev_bf16(big)[:, :2 * I]
+    rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=True)
+    for e8m0 in (False, True):
+        for mn in (False, True):
+            say("silu strided", "e8m0" if e8m0 else "fp32", "mn" if mn else "row")
+            q = torch.full((M, I + 16), 0xAB, dtype=torch.uint8, device=dev())
+            dt = torch.uint8 if e8m0 else torch.float32
+            s = torch.full((G, M + 8) if mn else (M, G + 8), 0x5A if e8m0 else -1.0, dtype=dt, device=dev())
+            sv = s[:, :M] if mn else s[:, :G]
+            fb.fp8_silu_and_mul_per_block_quant(xd, q[:, :I], sv, ue8m0=True, scale_e8m0=e8m0,
+                                                scale_mn_major=mn)
+            qh, sh = host(q), host(s)
+            assert np.all(qh[:, I:] == 0xAB)
+            got = sh[:, :M].T if mn else sh[:, :G]
+            got_f = ((got.astype(np.uint32) << 23).view(np.float32)) if e8m0 else got
+            _assert_near(qh[:, :I], got_f, rq, rs, ("strided", e8m0, mn), max_flip=1e-3)
+            assert np.all((sh[:, M:] if mn else sh[:, G:]) == (0x5A if e8m0 else -1.0))
