@@ -43,30 +43,53 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return v;
 }
 
-// scale = max(amax, eps) / 448 (correctly rounded fp32 division), with the
-// optional power-of-two ceiling done on the exponent field.
+// RN(1/448) in fp32.
+constexpr float kInv448 = 0x1.24924ap-9f;
+
+// x / s, correctly rounded, from y = RN(1/s), for x with a significand of
+// at most 8 bits (bf16 values): q0 = RN(x y) is within one ulp of x/s, the
+// residual q0 s - x is exact under an FMA, and one correction
+// step RN(q0 - r y) rounds to RN(x/s) (Markstein's division theorem).  The
+// residual is taken as q0 s - x (not x - q0 s) so that the correction keeps
+// the sign IEEE division gives a zero or an underflowing quotient: x = -0
+// gives -0 + (-0) = -0, x = +0 gives +0.  The test-suite checks this against
+// IEEE division for every pair of bf16 value and bf16-derived scale
+// significands and for the signed-zero and tiny cases.
+__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-r, y, q0);
+}
+
+// x / s, correctly rounded, for any fp32 x (24-bit significand): with 24
+// bits, q0 = RN(x y) can be up to 1.5 ulp off, and then the one-step form's
+// residual is not exact.  A first correction makes the quotient faithful
+// (within one ulp), a second rounds it correctly (Markstein's theorem needs
+// a faithful quotient).  Same signed-zero behaviour as div_by_scale.
+__device__ __forceinline__ float div_by_scale_f32(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r0 = __builtin_fmaf(q0, s, -x);
+  const float q1 = __builtin_fmaf(-r0, y, q0);
+  const float r1 = __builtin_fmaf(q1, s, -x);
+  return __builtin_fmaf(-r1, y, q1);
+}
+
+// scale = max(amax, eps) / 448, correctly rounded, with the optional
+// power-of-two ceiling done on the exponent field.  The division by 448 is
+// the one-step corrected product with RN(1/448) (3 operations instead of
+// an IEEE divide): for the divisor 448 its residual is exact and its result
+// equals IEEE division for every fp32 significand (checked exhaustively by
+// the test-suite; exponents scale every step exactly).  Below 2^-100, where
+// the residual could lose bits to underflow, the IEEE divide is used.
 __device__ __forceinline__ float scale_from_amax(float amax, float eps, bool ue8m0) {
-  float a = amax > eps ? amax : eps;
-  float s = a / kE4M3Max;
+  const float a = amax > eps ? amax : eps;
+  float s = a >= 0x1p-100f ? div_by_scale(a, kE4M3Max, kInv448) : a / kE4M3Max;
   if (ue8m0) {
     uint32_t b = __float_as_uint(s);
     if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
     s = __uint_as_float(b);
   }
   return s;
-}
-
-// x / s, correctly rounded, from y = RN(1/s): q0 = RN(x y) is within one ulp
-// of x/s, the residual x - q0 s is exact under an FMA, and one correction
-// step RN(q0 + r y) rounds to RN(x/s) (Markstein's division theorem).  The
-// sign is copied from x so that x = -0 (and results that underflow) keep
-// the sign IEEE division gives them.  The test-suite checks this against
-// IEEE division for every pair of bf16 value and bf16-derived scale
-// significands.
-__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
-  float q0 = x * y;
-  float r = __builtin_fmaf(-q0, s, x);
-  return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
 }
 
 // Four already-scaled values -> four e4m3fn codes (byte i = value i), clamp

@@ -11,7 +11,8 @@
 // lane layout: 16 lanes own one 128-group, 8 contiguous values per lane
 // loaded with one 16-byte load, the group amax reduced with DPP inside the
 // 16-lane row, the scale computed once per group, every value divided with
-// the 3-instruction correctly rounded division, two values per fp8 convert.
+// the 5-instruction correctly rounded division for fp32 values, two values
+// per fp8 convert.
 //
 // RMSNorm (the fp8 RMSNorm example of the Chinese Helion article, section
 // "自己写一个 Helion kernel 并接入 vLLM": variance = mean of squares,
@@ -23,12 +24,16 @@
 //     correctly rounded sqrt and division, rounded once to fp32;
 //   - y = (x * (1/rms)) * weight in fp32, quantized straight from fp32
 //     (no bf16 rounding in between).
-//   Rows longer than 8192 are split over the four waves of the workgroup,
-//   whose partial sums meet in LDS.
+//   Rows longer than 4096 are split over the four waves of the workgroup,
+//   whose partial sums meet in LDS.  Rows are walked grid-stride and the
+//   next row is loaded while the current one is reduced and quantized.
 //
 // SiLU-and-mul: x row = [gate (I values) | up (I values)]; y = silu(g) * u
-// = (g u) / (1 + exp(-g)) in fp32 with the library expf (within an ulp) and
-// one corrected reciprocal division, quantized from fp32.
+// = (g u) / (1 + exp(-g)) in fp32 with the hardware exp2 plus a two-FMA
+// argument correction (about an ulp) and one corrected reciprocal division,
+// quantized from fp32.  The arithmetic is trimmed to the few instructions
+// that keep y within about 1.5 ulp: at 5 bytes per element the kernel needs
+// about 30 VALU cycles per element or less to stay on the HBM roofline.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -58,168 +63,139 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float eps, bool ue8
   const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
   const float rc = 1.0f / sc;
   *sc_out = sc;
-  const uint32_t lo = encode4(div_by_scale(y[0], sc, rc), div_by_scale(y[1], sc, rc),
-                              div_by_scale(y[2], sc, rc), div_by_scale(y[3], sc, rc));
-  const uint32_t hi = encode4(div_by_scale(y[4], sc, rc), div_by_scale(y[5], sc, rc),
-                              div_by_scale(y[6], sc, rc), div_by_scale(y[7], sc, rc));
+  const uint32_t lo = encode4(div_by_scale_f32(y[0], sc, rc), div_by_scale_f32(y[1], sc, rc),
+                              div_by_scale_f32(y[2], sc, rc), div_by_scale_f32(y[3], sc, rc));
+  const uint32_t hi = encode4(div_by_scale_f32(y[4], sc, rc), div_by_scale_f32(y[5], sc, rc),
+                              div_by_scale_f32(y[6], sc, rc), div_by_scale_f32(y[7], sc, rc));
   return make_uint2(lo, hi);
 }
 
+// 64-bit DPP move of a double (each 32-bit half moved with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes, the same value in every lane: DPP inside each
+// 16-lane row (quad swaps, half-row and row mirrors), then the four row sums
+// read out and added in a fixed order.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_f64<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp_f64<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 // ---------------------------------------------------------------- RMSNorm
 //
-// WPR waves per row (1 or 4), VPL vectors of 8 values per lane: vector i of
-// wave w, lane l covers elements 8 * ((i * WPR + w) * 64 + l) .. +8, i.e.
-// each vector instruction of a wave reads 4 whole groups (1 KiB).  A row
-// covers WPR * 512 * VPL elements; groups past H are masked (per 16 lanes).
-template <int VPL, int WPR>
+// WPR waves per row (1, 2 or 4; 4 / WPR rows per workgroup), VPL vectors of
+// 8 values per lane: vector i of wave w (of its row), lane l covers elements
+// 8 * ((i * WPR + w) * 64 + l) .. +8, so each vector instruction of a wave
+// reads 4 whole groups (1 KiB).  A row covers WPR * 512 * VPL elements;
+// FULL when that is exactly H, else groups past H are masked (per 16
+// lanes).  Workgroups walk their row slots grid-stride (one round of
+// resident workgroups), the next rows' loads issued before the current rows
+// are reduced and quantized (two register buffers used in turn), so HBM
+// reads overlap the arithmetic.  The walk is uniform over the workgroup
+// (its barriers); waves whose row is past M only skip their memory traffic.
+template <int VPL, int WPR, bool FULL>
+__device__ __forceinline__ void rms_load_row(u32x4 (&v)[VPL], const uint16_t* xr, bool active, int wv,
+                                             int lane, int ngroups) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = ((i * WPR + wv) * 64 + lane) * 8;
+    const bool ok = active && (FULL || (e >> 7) < ngroups);
+    v[i] = ok ? load_nt16(xr + e) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int VPL, int WPR, bool FULL>
 __global__ __launch_bounds__(256) void k_rms_norm_quant(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ w, uint8_t* __restrict__ q,
     int64_t ldq, void* __restrict__ s, int64_t lds, int64_t M, int H, float eps_norm, float eps,
     int ue8m0, int fmt) {
-  __shared__ double red[4];
+  __shared__ double red[2][4];
+  constexpr int kRowsPerBlock = 4 / WPR;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  constexpr int kRowsPerBlock = 4 / WPR;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (WPR == 1 ? wave : 0);
-  const int wv = WPR == 1 ? 0 : wave;
+  const int slot = wave / WPR;  // row slot of this wave in the workgroup
+  const int wv = wave % WPR;    // this wave's part of the row
   const int ngroups = H / kGroup;
-  // WPR == 1: a wave whose row is past M has nothing to do (no barrier below)
-  if (WPR == 1 && row >= M) return;
-  const uint16_t* xr = x + row * ldx;
-  u32x4 v[VPL];
-  double ss = 0.0;
+  const int64_t rstep = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
+  if (base >= M) return;  // uniform over the workgroup
+
+  auto process = [&](const u32x4(&v)[VPL], int64_t row, int it) __attribute__((always_inline)) {
+    const bool active = row < M;
+    double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = ((i * WPR + wv) * 64 + lane) * 8;
-    v[i] = (e >> 7) < ngroups ? load_nt16(xr + e) : u32x4{0u, 0u, 0u, 0u};
-  }
+    for (int i = 0; i < VPL; ++i) {
+      const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double a = (double)bf16_lo(c[k]), b = (double)bf16_hi(c[k]);
-      ss = __builtin_fma(a, a, ss);
-      ss = __builtin_fma(b, b, ss);
+      for (int k = 0; k < 4; ++k) {
+        const double a = (double)bf16_lo(c[k]), b = (double)bf16_hi(c[k]);
+        ss = __builtin_fma(a, a, ss);
+        ss = __builtin_fma(b, b, ss);
+      }
     }
-  }
-  ss = wave_sum_f64(ss);
-  if (WPR > 1) {
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    ss = (red[0] + red[1]) + (red[2] + red[3]);
-  }
-  const float r = (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)eps_norm));
-  uint8_t* qr = q + row * ldq;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = ((i * WPR + wv) * 64 + lane) * 8;
-    const int g = e >> 7;
-    if (g >= ngroups) continue;  // the 16 lanes of a group agree
-    const float4 w0 = *(const float4*)(w + e);
-    const float4 w1 = *(const float4*)(w + e + 4);
-    const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    float y[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      y[2 * k] = (bf16_lo(c[k]) * r) * wj[2 * k];
-      y[2 * k + 1] = (bf16_hi(c[k]) * r) * wj[2 * k + 1];
+    ss = wave_sum_f64(ss);
+    if (WPR > 1) {
+      // two buffers: a wave overwrites one only after every wave has passed
+      // the barrier of the iteration in between
+      if (lane == 0) red[it & 1][wave] = ss;
+      __syncthreads();
+      const double* rr = &red[it & 1][slot * WPR];
+      ss = WPR == 2 ? rr[0] + rr[1] : (rr[0] + rr[1]) + (rr[2] + rr[3]);
     }
-    float sc;
-    const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
-    *(uint2*)(qr + e) = codes;
-    if ((lane & 15) == 0) store_scale(s, fmt, lds, row, g, sc);
-  }
-}
-
-template <int VPL, int WPR>
-hipError_t launch_rms(const uint16_t* x, int64_t ldx, const float* w, uint8_t* q, int64_t ldq, void* s,
-                      int64_t lds, int64_t M, int H, float eps_norm, float eps, int ue8m0, int fmt,
-                      hipStream_t stream) {
-  constexpr int rpb = 4 / WPR;
-  const int64_t blocks = (M + rpb - 1) / rpb;
-  hipLaunchKernelGGL((k_rms_norm_quant<VPL, WPR>), dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx,
-                     w, q, ldq, s, lds, M, H, eps_norm, eps, ue8m0, fmt);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ SiLU and mul
-//
-// 16 lanes per group, kSiluUnroll groups per 16 lanes in flight; groups are
-// numbered row-major over (row, group column) and split into chunks of
-// fewer than 2^24 groups so that row = (g * ceil(2^40 / gpr)) >> 40 is exact.
-constexpr int kSiluThreads = 256;
-constexpr int kSiluUnroll = 2;
-constexpr uint32_t kSiluGroupsPerIter = (kSiluThreads / 16) * kSiluUnroll;
-
-// silu(g) * u = (g u) / (1 + e^-g).  g u is exact in fp32 (two 8-bit
-// significands).  1 + e is rounded to d with its error t recovered exactly
-// (Fast2Sum on the larger and smaller of 1 and e), the quotient by d taken
-// from the hardware reciprocal and corrected once with the exact residual
-// g u - q d, less q t for the rounding of the divisor.  The result is within
-// a fraction of an ulp of (g u) / (1 + e), so only exp's error remains
-// (within an ulp: the library expf, not the bare hardware exp2).  e^-g is
-// capped at e^80 so that d and 1/d stay normal; for g < -80 the true value
-// is below 1e-30 |g u| either way.  The sign is that of g u.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float gu = g * u;
-  const float e = expf(fminf(-g, 80.0f));
-  const float a = fmaxf(1.0f, e), b = fminf(1.0f, e);
-  const float d = a + b;
-  const float t = b - (d - a);
-  const float rd = __builtin_amdgcn_rcpf(d);
-  const float q = gu * rd;
-  const float r = __builtin_fmaf(-q, d, gu);
-  const float r2 = __builtin_fmaf(-q, t, r);
-  return __builtin_copysignf(__builtin_fmaf(r2, rd, q), gu);
-}
-
-__global__ __launch_bounds__(kSiluThreads) void k_silu_mul_quant(
-    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    void* __restrict__ s, int64_t lds, int64_t row0, uint32_t total, uint32_t gpr, uint64_t magic,
-    int I, float eps, int ue8m0, int fmt) {
-  const uint32_t sub = threadIdx.x & 15u;
-  const uint32_t slot = threadIdx.x >> 4;
-  const uint32_t step = gridDim.x * kSiluGroupsPerIter;
-  for (uint32_t base = blockIdx.x * kSiluGroupsPerIter; base < total; base += step) {
-    u32x4 gv[kSiluUnroll], uv[kSiluUnroll];
-    uint32_t rows[kSiluUnroll], cols[kSiluUnroll];
-    bool valid[kSiluUnroll];
+    if (!active) return;
+    const float r = (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)eps_norm));
+    uint8_t* qr = q + row * ldq;
 #pragma unroll
-    for (int k = 0; k < kSiluUnroll; ++k) {
-      const uint32_t g = base + k * 16u + slot;
-      valid[k] = g < total;
-      rows[k] = (uint32_t)(((uint64_t)g * magic) >> 40);
-      cols[k] = g - rows[k] * gpr;
-      const uint16_t* p = x + (int64_t)rows[k] * ldx + (int64_t)cols[k] * kGroup + sub * 8;
-      gv[k] = valid[k] ? load_nt16(p) : u32x4{0u, 0u, 0u, 0u};
-      uv[k] = valid[k] ? load_nt16(p + I) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < kSiluUnroll; ++k) {
-      const uint32_t gc[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
-      const uint32_t uc[4] = {uv[k].x, uv[k].y, uv[k].z, uv[k].w};
+    for (int i = 0; i < VPL; ++i) {
+      const int e = ((i * WPR + wv) * 64 + lane) * 8;
+      const int g = e >> 7;
+      if (!FULL && g >= ngroups) continue;  // the 16 lanes of a group agree
+      const float4 w0 = *(const float4*)(w + e);
+      const float4 w1 = *(const float4*)(w + e + 4);
+      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       float y[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[2 * j] = silu_mul(bf16_lo(gc[j]), bf16_lo(uc[j]));
-        y[2 * j + 1] = silu_mul(bf16_hi(gc[j]), bf16_hi(uc[j]));
+      for (int k = 0; k < 4; ++k) {
+        y[2 * k] = (bf16_lo(c[k]) * r) * wj[2 * k];
+        y[2 * k + 1] = (bf16_hi(c[k]) * r) * wj[2 * k + 1];
       }
       float sc;
       const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
-      if (valid[k]) {
-        const int64_t rr = row0 + rows[k];
-        *(uint2*)(q + rr * ldq + (int64_t)cols[k] * kGroup + sub * 8) = codes;
-        if (sub == 0) store_scale(s, fmt, lds, rr, cols[k], sc);
-      }
+      *(uint2*)(qr + e) = codes;
+      if ((lane & 15) == 0) store_scale(s, fmt, lds, row, g, sc);
     }
+  };
+
+  u32x4 va[VPL], vb[VPL];
+  rms_load_row<VPL, WPR, FULL>(va, x + (base + slot) * ldx, base + slot < M, wv, lane, ngroups);
+  for (int it = 0;; it += 2) {
+    int64_t nbase = base + rstep;
+    rms_load_row<VPL, WPR, FULL>(vb, x + (nbase + slot) * ldx, nbase + slot < M, wv, lane, ngroups);
+    process(va, base + slot, it);
+    base = nbase;
+    if (base >= M) break;
+    nbase = base + rstep;
+    rms_load_row<VPL, WPR, FULL>(va, x + (nbase + slot) * ldx, nbase + slot < M, wv, lane, ngroups);
+    process(vb, base + slot, it + 1);
+    base = nbase;
+    if (base >= M) break;
   }
 }
 
@@ -231,6 +207,143 @@ int cu_count() {
       cus = v;
   }
   return cus;
+}
+
+
+// Workgroups of an RMSNorm kernel instance that fit the device at once
+// (occupancy x CUs), queried once per instance (the devices this library
+// runs on are all the same part).
+template <int VPL, int WPR, bool FULL>
+int rms_resident_blocks() {
+  static const int cached = [] {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rms_norm_quant<VPL, WPR, FULL>, 256, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    return per_cu * cu_count();
+  }();
+  return cached;
+}
+
+template <int VPL, int WPR, bool FULL>
+hipError_t launch_rms(const uint16_t* x, int64_t ldx, const float* w, uint8_t* q, int64_t ldq, void* s,
+                      int64_t lds, int64_t M, int H, float eps_norm, float eps, int ue8m0, int fmt,
+                      hipStream_t stream) {
+  constexpr int rpb = 4 / WPR;
+  int64_t blocks = (M + rpb - 1) / rpb;
+  // persistent: one round of resident workgroups, each walking its row slots
+  const int max_blocks = rms_resident_blocks<VPL, WPR, FULL>();
+  if (blocks > max_blocks) blocks = max_blocks;
+  hipLaunchKernelGGL((k_rms_norm_quant<VPL, WPR, FULL>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                     ldx, w, q, ldq, s, lds, M, H, eps_norm, eps, ue8m0, fmt);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ SiLU and mul
+//
+// 16 lanes per group, kSiluUnroll groups per 16 lanes in flight; groups are
+// numbered row-major over (row, group column) and split into chunks of
+// fewer than 2^24 groups so that row = (g * ceil(2^40 / gpr)) >> 40 is exact.
+// Grid-stride over the groups, the next iteration's loads issued before the
+// current groups are computed.
+constexpr int kSiluThreads = 256;
+constexpr int kSiluUnroll = 2;
+constexpr uint32_t kSiluGroupsPerIter = (kSiluThreads / 16) * kSiluUnroll;
+
+constexpr float kLog2eHi = 0x1.715476p+0f;   // log2(e) rounded to fp32
+constexpr float kLog2eLo = 0x1.4ae0c0p-26f;  // log2(e) - kLog2eHi
+constexpr float kLn2 = 0x1.62e430p-1f;
+
+// e^n for n <= 80: 2^p with p = RN(n log2 e) from the hardware exp2, times
+// (1 + p_lo ln 2) for the part of n log2 e that p dropped (p_lo from two
+// FMAs: the exact residual of n * kLog2eHi plus n * kLog2eLo).  Within about
+// an ulp; underflows to 0 for n below about -87 (where 1 + e^n rounds to 1).
+__device__ __forceinline__ float exp_capped(float n) {
+  const float p = n * kLog2eHi;
+  const float plo = __builtin_fmaf(n, kLog2eLo, __builtin_fmaf(n, kLog2eHi, -p));
+  const float e0 = __builtin_amdgcn_exp2f(p);
+  return __builtin_fmaf(e0 * plo, kLn2, e0);
+}
+
+// silu(g) * u = (g u) / (1 + e^-g).  g u is exact in fp32 (two 8-bit
+// significands).  1 + e is rounded to d with its error t recovered exactly
+// (Fast2Sum on the larger and smaller of 1 and e), the quotient by d taken
+// from the hardware reciprocal and corrected once with the exact residual
+// g u - q d, less q t for the rounding of the divisor.  The result is within
+// a fraction of an ulp of (g u) / (1 + e), so only exp's error (about an
+// ulp) remains.  e^-g is capped at e^80 so that d and 1/d stay normal; for
+// g < -80 the true value is below 1e-30 |g u| either way.  The sign is that
+// of g u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float gu = g * u;
+  const float e = exp_capped(fminf(-g, 80.0f));
+  const float a = fmaxf(1.0f, e), b = fminf(1.0f, e);
+  const float d = a + b;
+  const float t = b - (d - a);
+  const float rd = __builtin_amdgcn_rcpf(d);
+  const float q = gu * rd;
+  const float r = __builtin_fmaf(-q, d, gu);
+  const float r2 = __builtin_fmaf(-q, t, r);
+  return __builtin_copysignf(__builtin_fmaf(r2, rd, q), gu);
+}
+
+struct SiluFrag {
+  u32x4 gv[kSiluUnroll], uv[kSiluUnroll];
+};
+
+__device__ __forceinline__ void silu_load(SiluFrag& f, const uint16_t* __restrict__ x, int64_t ldx,
+                                          uint32_t base, uint32_t slot, uint32_t sub, uint32_t total,
+                                          uint32_t gpr, uint64_t magic, int I) {
+#pragma unroll
+  for (int k = 0; k < kSiluUnroll; ++k) {
+    const uint32_t g = base + k * 16u + slot;
+    const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
+    const uint32_t col = g - row * gpr;
+    const uint16_t* p = x + (int64_t)row * ldx + (int64_t)col * kGroup + sub * 8;
+    f.gv[k] = g < total ? load_nt16(p) : u32x4{0u, 0u, 0u, 0u};
+    f.uv[k] = g < total ? load_nt16(p + I) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__global__ __launch_bounds__(kSiluThreads) void k_silu_mul_quant(
+    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    void* __restrict__ s, int64_t lds, int64_t row0, uint32_t total, uint32_t gpr, uint64_t magic,
+    int I, float eps, int ue8m0, int fmt) {
+  const uint32_t sub = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;
+  const uint32_t step = gridDim.x * kSiluGroupsPerIter;
+  uint32_t base = blockIdx.x * kSiluGroupsPerIter;
+  if (base >= total) return;
+  SiluFrag cur;
+  silu_load(cur, x, ldx, base, slot, sub, total, gpr, magic, I);
+  for (; base < total; base += step) {
+    SiluFrag nxt;
+    const uint32_t nb = base + step;  // < 2^25: no wrap
+    if (nb < total) silu_load(nxt, x, ldx, nb, slot, sub, total, gpr, magic, I);
+#pragma unroll
+    for (int k = 0; k < kSiluUnroll; ++k) {
+      const uint32_t g = base + k * 16u + slot;
+      const uint32_t gc[4] = {cur.gv[k].x, cur.gv[k].y, cur.gv[k].z, cur.gv[k].w};
+      const uint32_t uc[4] = {cur.uv[k].x, cur.uv[k].y, cur.uv[k].z, cur.uv[k].w};
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = silu_mul(bf16_lo(gc[j]), bf16_lo(uc[j]));
+        y[2 * j + 1] = silu_mul(bf16_hi(gc[j]), bf16_hi(uc[j]));
+      }
+      float sc;
+      const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
+      if (g < total) {
+        const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
+        const uint32_t col = g - row * gpr;
+        const int64_t rr = row0 + row;
+        *(uint2*)(q + rr * ldq + (int64_t)col * kGroup + sub * 8) = codes;
+        if (sub == 0) store_scale(s, fmt, lds, rr, col, sc);
+      }
+    }
+    cur = nxt;
+  }
 }
 
 }  // namespace
@@ -249,14 +362,37 @@ hipError_t launch_rms_norm_quant(const uint16_t* x, int64_t M, int64_t H, int64_
     const int64_t selt = (scale_format & 2) ? 1 : 4;
     void* sr = (char*)s + ((scale_format & 1) ? r0 : r0 * lds) * selt;
     hipError_t e;
-    if (H <= 512) e = launch_rms<1, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 1024) e = launch_rms<2, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 2048) e = launch_rms<4, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 4096) e = launch_rms<8, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 6144) e = launch_rms<12, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 8192) e = launch_rms<16, 1>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else if (H <= 16384) e = launch_rms<8, 4>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
-    else e = launch_rms<16, 4>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream);
+    // Exact fits (H a multiple of 512): one wave per row up to 4096 values,
+    // two waves up to 8192, four beyond, at most 8 vectors per lane (two
+    // rows in registers at 3 or more waves per SIMD).  Other H (multiples
+    // of 128): masked shapes that round the row up.
+#define FP8BLK_RMS(V, W, F) launch_rms<V, W, F>(xr, ldx, w, qr, ldq, sr, lds, rows, h, eps_norm, eps, u, scale_format, stream)
+    switch (H % 512 == 0 ? H / 512 : 0) {
+      case 1: e = FP8BLK_RMS(1, 1, true); break;
+      case 2: e = FP8BLK_RMS(2, 1, true); break;
+      case 3: e = FP8BLK_RMS(3, 1, true); break;
+      case 4: e = FP8BLK_RMS(4, 1, true); break;
+      case 5: e = FP8BLK_RMS(5, 1, true); break;
+      case 6: e = FP8BLK_RMS(6, 1, true); break;
+      case 7: e = FP8BLK_RMS(7, 1, true); break;
+      case 8: e = FP8BLK_RMS(8, 1, true); break;
+      case 10: e = FP8BLK_RMS(5, 2, true); break;
+      case 12: e = FP8BLK_RMS(6, 2, true); break;
+      case 14: e = FP8BLK_RMS(7, 2, true); break;
+      case 16: e = FP8BLK_RMS(8, 2, true); break;
+      case 20: e = FP8BLK_RMS(5, 4, true); break;
+      case 24: e = FP8BLK_RMS(6, 4, true); break;
+      case 28: e = FP8BLK_RMS(7, 4, true); break;
+      case 32: e = FP8BLK_RMS(8, 4, true); break;
+      case 64: e = FP8BLK_RMS(16, 4, true); break;
+      default:
+        if (H <= 1024) e = FP8BLK_RMS(2, 1, false);
+        else if (H <= 4096) e = FP8BLK_RMS(8, 1, false);
+        else if (H <= 8192) e = FP8BLK_RMS(8, 2, false);
+        else if (H <= 16384) e = FP8BLK_RMS(8, 4, false);
+        else e = FP8BLK_RMS(16, 4, false);
+    }
+#undef FP8BLK_RMS
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

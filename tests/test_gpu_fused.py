@@ -66,12 +66,15 @@ def _assert_near(q, s, rq, rs, what, max_flip=1e-4):
 
 # ----------------------------------------------------------------- RMSNorm
 
-# H covers every kernel shape: one wave per row with 1, 2, 4, 8, 12, 16
-# vectors per lane (partly masked for 384, 640, 5120), and four waves per
-# row (12288, 16384, 32768).  M covers 1, ragged multiples of the 4 rows a
-# workgroup holds, and several hundred rows.
-RMS_CASES = [(1, 128), (3, 384), (5, 640), (7, 2048), (17, 4096), (33, 5120), (2, 6144),
-             (9, 8192), (6, 12288), (4, 16384), (3, 32768), (301, 4096), (64, 2048)]
+# H covers every kernel shape: exact fits with one wave per row (1536 ..
+# 4096), two waves (5120 .. 8192) and four (12288 .. 32768), and the masked
+# shapes for H not a multiple of 512 (128, 384, 640, 4224, 9216, 20480).
+# M covers 1, ragged multiples of the rows a workgroup holds, and enough
+# rows that every resident workgroup walks several (301, 1001, 4096).
+RMS_CASES = [(1, 128), (3, 384), (5, 640), (2, 1536), (7, 2048), (3, 2560), (2, 3584), (17, 4096),
+             (4, 4224), (33, 5120), (2, 6144), (3, 7168), (9, 8192), (2, 9216), (6, 12288),
+             (2, 14336), (4, 16384), (2, 20480), (3, 32768), (301, 4096), (64, 2048), (1001, 5120),
+             (4096, 1024)]
 
 
 @pytest.mark.parametrize("M,H", RMS_CASES)

@@ -1,8 +1,11 @@
 """The quantizer kernel divides by the scale with a reciprocal and one FMA
-correction step instead of an IEEE divide.  This CPU test checks, for every
-pair of (bf16 value significand, scale significand) the activation path can
-produce, that the 3-operation sequence plus the sign copy gives exactly the
-IEEE single-precision quotient.  Scales come from bf16 amax values (one per
+correction step instead of an IEEE divide (residual taken as q0 s - x so
+that signed zeros come out right without a sign copy), and computes the
+scale amax / 448 the same way.  This CPU test checks, for every pair of
+(bf16 value significand, scale significand) the activation path can
+produce, for random fp32 values (the fused producers quantize fp32 values),
+and for every fp32 significand divided by 448, that the 3-operation
+sequence gives exactly the IEEE single-precision quotient.  Scales come from bf16 amax values (one per
 bf16 significand) and from eps; power-of-two (UE8M0) scales are exact
 trivially and are checked too.  Scaling x or s by powers of two scales every
 intermediate exactly, so significands at one exponent cover the normal range;
@@ -20,9 +23,56 @@ _libm.fmaf.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
 
 def _kernel_div(x: np.float32, s: np.float32, y: np.float32) -> np.float32:
     q0 = np.float32(x * y)
-    r = np.float32(_libm.fmaf(float(-q0), float(s), float(x)))
-    t = np.float32(_libm.fmaf(float(r), float(y), float(q0)))
-    return np.copysign(t, x)
+    r = np.float32(_libm.fmaf(float(q0), float(s), float(-x)))
+    return np.float32(_libm.fmaf(float(-r), float(y), float(q0)))
+
+
+def _kernel_div_vec(x: np.ndarray, s: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """The same three operations on arrays.  q0 s - x is exact in float64 (48-bit
+    product, difference within 53 bits) and, by the theorem, representable in
+    fp32 (asserted).  q0 - r y is exact only to float64, so the few results
+    whose float64 value sits within a few float64 ulps of an fp32 rounding
+    midpoint are recomputed with the C library's exact fmaf."""
+    x = x.astype(np.float32)
+    s = np.broadcast_to(s, x.shape).astype(np.float32)
+    y = np.broadcast_to(y, x.shape).astype(np.float32)
+    q0 = (x * y).astype(np.float32)
+    r64 = q0.astype(np.float64) * s.astype(np.float64) - x.astype(np.float64)
+    r = r64.astype(np.float32)
+    assert np.array_equal(r.astype(np.float64), r64), "residual not exact in fp32"
+    t64 = q0.astype(np.float64) - r.astype(np.float64) * y.astype(np.float64)
+    t = t64.astype(np.float32)
+    half = np.spacing(np.abs(t)).astype(np.float64) / 2
+    near = np.abs(np.abs(t64 - t.astype(np.float64)) - half) <= 4 * np.spacing(np.abs(t64))
+    for i in np.nonzero(near)[0]:
+        t[i] = _kernel_div(x[i], s[i], y[i])
+    return t
+
+
+def _exact_fma_vec(a, b, c):
+    """RN32(a b + c) for fp32 arrays: a b is exact in float64; where the
+    float64 sum could sit on an fp32 rounding midpoint the C library's exact
+    fmaf is used instead."""
+    t64 = a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)
+    t = t64.astype(np.float32)
+    half = np.spacing(np.abs(t)).astype(np.float64) / 2
+    near = np.abs(np.abs(t64 - t.astype(np.float64)) - half) <= 4 * np.spacing(np.abs(t64))
+    for i in np.nonzero(near)[0]:
+        t[i] = _libm.fmaf(float(a[i]), float(b[i]), float(c[i]))
+    return t
+
+
+def _kernel_div2_vec(x, s, y):
+    """The fp32-input division: two correction steps.  The first makes the
+    quotient faithful (within one ulp), the second rounds it correctly."""
+    x = x.astype(np.float32)
+    s = np.broadcast_to(s, x.shape).astype(np.float32)
+    y = np.broadcast_to(y, x.shape).astype(np.float32)
+    q0 = (x * y).astype(np.float32)
+    r0 = _exact_fma_vec(q0, s, -x)
+    q1 = _exact_fma_vec(-r0, y, q0)
+    r1 = _exact_fma_vec(q1, s, -x)
+    return _exact_fma_vec(-r1, y, q1)
 
 
 def _bf16_significands():
@@ -66,3 +116,58 @@ def test_signed_zero_and_tiny_values():
             if got.view(np.uint32) != ref.view(np.uint32):
                 assert abs(ref) < 2.0 ** -60 and abs(got) < 2.0 ** -60, (x, s, got, ref)
             assert np.signbit(got) == np.signbit(ref) == np.signbit(x)
+
+
+def test_scale_division_by_448_for_every_fp32_significand():
+    # every significand at one exponent (the quotient and residual scale
+    # exactly with the exponent of amax) plus both ends of the range in use
+    m = (np.arange(1 << 23, dtype=np.uint32) | np.uint32(0x3F800000)).view(np.float32)
+    y = np.float32(1) / np.float32(448)
+    assert float(y) == float.fromhex("0x1.24924ap-9")
+    for a in (m, m * np.float32(2.0 ** -100), m * np.float32(2.0 ** 127)):
+        got = _kernel_div_vec(a, np.float32(448), y)
+        ref = (a / np.float32(448)).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _random_fp32_groups(n, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = (g.standard_normal(n) * np.exp(g.uniform(-20, 20, n))).astype(np.float32)
+    amax = np.abs((g.standard_normal(n) * np.exp(g.uniform(-20, 20, n)))).astype(np.float32)
+    s = (np.maximum(amax, np.float32(1e-10)) / np.float32(448)).astype(np.float32)
+    x = np.clip(x, -amax, amax).astype(np.float32)  # |x| <= amax, as in a group
+    return x, s, (np.float32(1) / s).astype(np.float32)
+
+
+def test_one_step_division_is_not_enough_for_fp32_inputs():
+    # with 24-bit x, q0 = RN(x y) can be 1.5 ulp off and the residual then
+    # needs 25 bits: the single-step form is reserved for bf16 inputs
+    x, s, y = _random_fp32_groups(1 << 16, 96)
+    q0 = (x * y).astype(np.float32)
+    r64 = q0.astype(np.float64) * s.astype(np.float64) - x.astype(np.float64)
+    assert np.any(r64.astype(np.float32).astype(np.float64) != r64)
+
+
+def test_two_step_division_matches_ieee_for_random_fp32_inputs():
+    x, s, y = _random_fp32_groups(1 << 20, 97)
+    got = _kernel_div2_vec(x, s, y)
+    ref = (x / s).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the hardest significands: x just below a power of two over scales with
+    # significands near 2 (largest error of RN(1/s))
+    xs = (np.uint32(0x3FFFFFFF) - np.arange(4096, dtype=np.uint32)).view(np.float32)
+    for sb in (0x3FFFFFFF, 0x3FFFFF00, 0x3F800001, 0x3FB504F3):
+        s1 = np.uint32(sb).view(np.float32)
+        got = _kernel_div2_vec(xs, s1, np.float32(1) / s1)
+        assert np.array_equal(got.view(np.uint32), (xs / s1).astype(np.float32).view(np.uint32))
+
+
+def test_two_step_division_signed_zero_and_tiny():
+    for s in (np.float32(1.0), np.float32(3.0) / np.float32(448), np.float32(1e30)):
+        y = np.float32(1) / s
+        xs = np.array([0.0, -0.0, -2.0 ** -133, 2.0 ** -133, -1e-38, 1e-30, -3e-36], np.float32)
+        got = _kernel_div2_vec(xs, s, y)
+        ref = (xs / s).astype(np.float32)
+        assert np.array_equal(np.signbit(got), np.signbit(xs))
+        big = np.abs(ref) >= 2.0 ** -60
+        assert np.array_equal(got[big], ref[big])
