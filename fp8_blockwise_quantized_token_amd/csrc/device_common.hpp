@@ -61,17 +61,30 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float y) {
   return __builtin_fmaf(-r, y, q0);
 }
 
-// x / s, correctly rounded, for any fp32 x (24-bit significand): with 24
-// bits, q0 = RN(x y) can be up to 1.5 ulp off, and then the one-step form's
-// residual is not exact.  A first correction makes the quotient faithful
-// (within one ulp), a second rounds it correctly (Markstein's theorem needs
-// a faithful quotient).  Same signed-zero behaviour as div_by_scale.
-__device__ __forceinline__ float div_by_scale_f32(float x, float s, float y) {
-  const float q0 = x * y;
-  const float r0 = __builtin_fmaf(q0, s, -x);
-  const float q1 = __builtin_fmaf(-r0, y, q0);
-  const float r1 = __builtin_fmaf(q1, s, -x);
-  return __builtin_fmaf(-r1, y, q1);
+// Reciprocal pair for div_by_scale_f32: yn = RN(1/s), yd = the largest fp32
+// not above 1/s (yn or its predecessor), yl = RN((1 - s yd) / s) >= 0, so
+// that yd + yl is 1/s to about 2^-47.
+struct Recip {
+  float yn, yd, yl;
+};
+__device__ __forceinline__ Recip recip_of_scale(float s) {
+  Recip r;
+  r.yn = 1.0f / s;
+  const float e = __builtin_fmaf(-s, r.yn, 1.0f);  // exact: 1 - s yn
+  r.yd = e < 0.0f ? __uint_as_float(__float_as_uint(r.yn) - 1u) : r.yn;
+  r.yl = __builtin_fmaf(-s, r.yd, 1.0f) * r.yd;    // >= 0
+  return r;
+}
+
+// x / s, correctly rounded, for any fp32 x: q0 = RN(x yd + RN(x yl)) is
+// within half an ulp plus a hair of x/s (faithful), so the residual q0 s - x
+// is exact under an FMA and one Markstein correction with RN(1/s) rounds
+// correctly.  yl >= 0 keeps the sign of a zero x through the first FMA; the
+// residual form keeps it through the rest.  4 operations per value.
+__device__ __forceinline__ float div_by_scale_f32(float x, float s, const Recip& r) {
+  const float q0 = __builtin_fmaf(x, r.yd, x * r.yl);
+  const float res = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-res, r.yn, q0);
 }
 
 // scale = max(amax, eps) / 448, correctly rounded, with the optional

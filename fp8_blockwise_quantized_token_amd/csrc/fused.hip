@@ -11,7 +11,7 @@
 // lane layout: 16 lanes own one 128-group, 8 contiguous values per lane
 // loaded with one 16-byte load, the group amax reduced with DPP inside the
 // 16-lane row, the scale computed once per group, every value divided with
-// the 5-instruction correctly rounded division for fp32 values, two values
+// a 4-instruction correctly rounded division for fp32 values, two values
 // per fp8 convert.
 //
 // RMSNorm (the fp8 RMSNorm example of the Chinese Helion article, section
@@ -55,13 +55,14 @@ __device__ __forceinline__ void store_scale(void* s, int fmt, int64_t lds, int64
 
 // Group quantization of 8 fp32 values per lane, 16 lanes per group (one DPP
 // row): amax, scale, codes.  Returns the 8 codes; *sc_out gets the scale.
+// The values are results of fp32 arithmetic (canonical, finite), so their
+// magnitudes are compared as floats.
 __device__ __forceinline__ uint2 quant8(const float (&y)[8], float eps, bool ue8m0, float* sc_out) {
-  uint32_t am = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) am = max(am, __float_as_uint(y[j]) & 0x7FFFFFFFu);
-  am = row16_max_u32(am);
+  float m = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+  m = fmaxf(m, fmaxf(fmaxf(fabsf(y[4]), fabsf(y[5])), fmaxf(fabsf(y[6]), fabsf(y[7]))));
+  const uint32_t am = row16_max_u32(__float_as_uint(m));
   const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
-  const float rc = 1.0f / sc;
+  const Recip rc = recip_of_scale(sc);
   *sc_out = sc;
   const uint32_t lo = encode4(div_by_scale_f32(y[0], sc, rc), div_by_scale_f32(y[1], sc, rc),
                               div_by_scale_f32(y[2], sc, rc), div_by_scale_f32(y[3], sc, rc));
@@ -242,14 +243,24 @@ hipError_t launch_rms(const uint16_t* x, int64_t ldx, const float* w, uint8_t* q
 
 // ------------------------------------------------------------ SiLU and mul
 //
-// 16 lanes per group, kSiluUnroll groups per 16 lanes in flight; groups are
+// 16 lanes per group, kSiluUnroll groups per 16 lanes in flight (group k of
+// a 16-lane slot is base + k * slots + slot); groups are
 // numbered row-major over (row, group column) and split into chunks of
 // fewer than 2^24 groups so that row = (g * ceil(2^40 / gpr)) >> 40 is exact.
 // Grid-stride over the groups, the next iteration's loads issued before the
 // current groups are computed.
-constexpr int kSiluThreads = 256;
+//
+// Two ways to the sigmoid (TAB):
+//   - table: s(g) = 1 / (1 + e^-g) correctly rounded to fp32 for every bf16
+//     g, copied once per workgroup into LDS (8196 floats; see
+//     sigmoid_table.inc) and looked up by the bits of g: 6 integer/LDS
+//     operations per value; y = RN(RN(g u) s) with g u exact, within an ulp.
+//     Used when the problem is large enough to amortize the table copy.
+//   - arithmetic: (g u) / (1 + e^-g) with the hardware exp2 and a corrected
+//     division (about 1.5 ulp); no set-up, for small problems.
 constexpr int kSiluUnroll = 2;
-constexpr uint32_t kSiluGroupsPerIter = (kSiluThreads / 16) * kSiluUnroll;
+
+#include "sigmoid_table.inc"
 
 constexpr float kLog2eHi = 0x1.715476p+0f;   // log2(e) rounded to fp32
 constexpr float kLog2eLo = 0x1.4ae0c0p-26f;  // log2(e) - kLog2eHi
@@ -277,7 +288,7 @@ __device__ __forceinline__ float exp_capped(float n) {
 // of g u.
 __device__ __forceinline__ float silu_mul(float g, float u) {
   const float gu = g * u;
-  const float e = exp_capped(fminf(-g, 80.0f));
+  const float e = exp_capped(__builtin_amdgcn_fmed3f(-g, -1.0e30f, 80.0f));
   const float a = fmaxf(1.0f, e), b = fminf(1.0f, e);
   const float d = a + b;
   const float t = b - (d - a);
@@ -288,61 +299,109 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __builtin_copysignf(__builtin_fmaf(r2, rd, q), gu);
 }
 
+// Table lookup of s(g) for the bf16 bit pattern h (low 16 bits): the
+// magnitude bits clamped to the table's span, the sign selecting the half.
+__device__ __forceinline__ float sigmoid_lookup(uint32_t h, const float* tab) {
+  const int i = min(max((int)(h & 0x7FFFu) - kSigmoidBase, 0), kSigmoidSpan - 1);
+  return tab[i + (int)((h >> 15) & 1u) * kSigmoidSpan];
+}
+
+// One iteration's inputs for kSiluUnroll groups per 16 lanes, with each
+// group's row, column and offset in q (32-bit offsets: a launch covers
+// fewer than 2^31 elements of x and of q).
 struct SiluFrag {
   u32x4 gv[kSiluUnroll], uv[kSiluUnroll];
+  uint32_t qo[kSiluUnroll];
+  uint32_t row[kSiluUnroll], col[kSiluUnroll];
 };
 
-__device__ __forceinline__ void silu_load(SiluFrag& f, const uint16_t* __restrict__ x, int64_t ldx,
-                                          uint32_t base, uint32_t slot, uint32_t sub, uint32_t total,
-                                          uint32_t gpr, uint64_t magic, int I) {
+// Group k of a lane is base + k * NS + slot (NS = 16-lane slots per
+// workgroup), so one iteration covers NS * kSiluUnroll consecutive groups.
+template <uint32_t NS>
+__device__ __forceinline__ void silu_load(SiluFrag& f, const uint16_t* __restrict__ x, uint32_t ldx,
+                                          uint32_t ldq, uint32_t base, uint32_t slot, uint32_t sub,
+                                          uint32_t total, uint32_t gpr, uint64_t magic, uint32_t I) {
 #pragma unroll
   for (int k = 0; k < kSiluUnroll; ++k) {
-    const uint32_t g = base + k * 16u + slot;
+    // groups past the end load the last group again (in bounds, unused:
+    // their stores are skipped), which keeps the loads unpredicated
+    const uint32_t g = min(base + k * NS + slot, total - 1u);
     const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
     const uint32_t col = g - row * gpr;
-    const uint16_t* p = x + (int64_t)row * ldx + (int64_t)col * kGroup + sub * 8;
-    f.gv[k] = g < total ? load_nt16(p) : u32x4{0u, 0u, 0u, 0u};
-    f.uv[k] = g < total ? load_nt16(p + I) : u32x4{0u, 0u, 0u, 0u};
+    f.row[k] = row;
+    f.col[k] = col;
+    const uint32_t xo = row * ldx + col * kGroup + sub * 8;  // elements
+    f.qo[k] = row * ldq + col * kGroup + sub * 8;
+    f.gv[k] = load_nt16((const char*)x + 2u * xo);
+    f.uv[k] = load_nt16((const char*)x + 2u * (xo + I));
   }
 }
 
-__global__ __launch_bounds__(kSiluThreads) void k_silu_mul_quant(
-    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    void* __restrict__ s, int64_t lds, int64_t row0, uint32_t total, uint32_t gpr, uint64_t magic,
-    int I, float eps, int ue8m0, int fmt) {
-  const uint32_t sub = threadIdx.x & 15u;
-  const uint32_t slot = threadIdx.x >> 4;
-  const uint32_t step = gridDim.x * kSiluGroupsPerIter;
-  uint32_t base = blockIdx.x * kSiluGroupsPerIter;
-  if (base >= total) return;
-  SiluFrag cur;
-  silu_load(cur, x, ldx, base, slot, sub, total, gpr, magic, I);
-  for (; base < total; base += step) {
-    SiluFrag nxt;
-    const uint32_t nb = base + step;  // < 2^25: no wrap
-    if (nb < total) silu_load(nxt, x, ldx, nb, slot, sub, total, gpr, magic, I);
+template <bool TAB, uint32_t NS>
+__device__ __forceinline__ void silu_compute_store(const SiluFrag& f, uint32_t base, uint32_t slot,
+                                                   uint32_t sub, uint32_t total, const float* tab,
+                                                   uint8_t* __restrict__ q, void* __restrict__ s,
+                                                   int64_t lds, int64_t row0, float eps, int ue8m0,
+                                                   int fmt) {
 #pragma unroll
-    for (int k = 0; k < kSiluUnroll; ++k) {
-      const uint32_t g = base + k * 16u + slot;
-      const uint32_t gc[4] = {cur.gv[k].x, cur.gv[k].y, cur.gv[k].z, cur.gv[k].w};
-      const uint32_t uc[4] = {cur.uv[k].x, cur.uv[k].y, cur.uv[k].z, cur.uv[k].w};
-      float y[8];
+  for (int k = 0; k < kSiluUnroll; ++k) {
+    const uint32_t g = base + k * NS + slot;
+    const uint32_t gc[4] = {f.gv[k].x, f.gv[k].y, f.gv[k].z, f.gv[k].w};
+    const uint32_t uc[4] = {f.uv[k].x, f.uv[k].y, f.uv[k].z, f.uv[k].w};
+    float y[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      if (TAB) {
+        y[2 * j] = (bf16_lo(gc[j]) * bf16_lo(uc[j])) * sigmoid_lookup(gc[j], tab);
+        y[2 * j + 1] = (bf16_hi(gc[j]) * bf16_hi(uc[j])) * sigmoid_lookup(gc[j] >> 16, tab);
+      } else {
         y[2 * j] = silu_mul(bf16_lo(gc[j]), bf16_lo(uc[j]));
         y[2 * j + 1] = silu_mul(bf16_hi(gc[j]), bf16_hi(uc[j]));
       }
-      float sc;
-      const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
-      if (g < total) {
-        const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
-        const uint32_t col = g - row * gpr;
-        const int64_t rr = row0 + row;
-        *(uint2*)(q + rr * ldq + (int64_t)col * kGroup + sub * 8) = codes;
-        if (sub == 0) store_scale(s, fmt, lds, rr, col, sc);
-      }
     }
-    cur = nxt;
+    float sc;
+    const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
+    if (g < total) {
+      *(uint2*)(q + f.qo[k]) = codes;
+      if (sub == 0) store_scale(s, fmt, lds, row0 + f.row[k], f.col[k], sc);
+    }
+  }
+}
+
+// x and q point at the launch's first row; row0 is that row's index (for
+// the scales).
+template <bool TAB, int NT>
+__global__ __launch_bounds__(NT) void k_silu_mul_quant(
+    const uint16_t* __restrict__ x, uint32_t ldx, uint8_t* __restrict__ q, uint32_t ldq,
+    void* __restrict__ s, int64_t lds, int64_t row0, uint32_t total, uint32_t gpr, uint64_t magic,
+    uint32_t I, float eps, int ue8m0, int fmt) {
+  constexpr uint32_t kSlots = NT / 16;
+  constexpr uint32_t kPerIter = kSlots * kSiluUnroll;
+  __shared__ float tab[TAB ? 2 * kSigmoidSpan : 1];
+  const uint32_t sub = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;
+  const uint32_t step = gridDim.x * kPerIter;
+  uint32_t base = blockIdx.x * kPerIter;
+  if (base >= total) return;  // uniform over the workgroup
+  SiluFrag fa, fb;
+  silu_load<kSlots>(fa, x, ldx, ldq, base, slot, sub, total, gpr, magic, I);
+  if (TAB) {
+    for (int i = threadIdx.x; i < 2 * kSigmoidSpan; i += NT) tab[i] = kSigmoidTable[i];
+    __syncthreads();
+  }
+  // two fragments used in turn: the loads of one are in flight while the
+  // other is computed (total + step < 2^26: no wrap)
+  for (;;) {
+    uint32_t nb = base + step;
+    if (nb < total) silu_load<kSlots>(fb, x, ldx, ldq, nb, slot, sub, total, gpr, magic, I);
+    silu_compute_store<TAB, kSlots>(fa, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
+    base = nb;
+    if (base >= total) break;
+    nb = base + step;
+    if (nb < total) silu_load<kSlots>(fa, x, ldx, ldq, nb, slot, sub, total, gpr, magic, I);
+    silu_compute_store<TAB, kSlots>(fb, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
+    base = nb;
+    if (base >= total) break;
   }
 }
 
@@ -402,18 +461,37 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, int64_t M, int64_t I, int64_
                                  int64_t ldq, void* s, int64_t lds, float eps, bool ue8m0,
                                  int scale_format, hipStream_t stream) {
   const int64_t gpr = I / kGroup;
+  // chunks of rows: fewer than 2^24 groups (exact row division) and fewer
+  // than 2^31 elements of x and of q (32-bit offsets)
+  const int64_t pitch = ldx > ldq ? ldx : ldq;
   int64_t rows_per_chunk = (int64_t(1) << 24) / gpr;
+  const int64_t by_offset = ((int64_t(1) << 31) - 1) / pitch;
+  if (rows_per_chunk > by_offset) rows_per_chunk = by_offset;
   if (rows_per_chunk < 1) rows_per_chunk = 1;
   const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)gpr - 1) / (uint64_t)gpr;
-  const int max_blocks = cu_count() * 8;
+  const int cus = cu_count();
   for (int64_t r0 = 0; r0 < M; r0 += rows_per_chunk) {
     const int64_t rows = (M - r0) < rows_per_chunk ? (M - r0) : rows_per_chunk;
     const uint32_t total = (uint32_t)(rows * gpr);
-    int64_t blocks = (total + kSiluGroupsPerIter - 1) / kSiluGroupsPerIter;
+    // the LDS table pays off once every resident workgroup has several
+    // iterations to run (4 workgroups of 512 threads per CU)
+    const bool tab = total >= (uint32_t)cus * 4 * (512 / 16) * kSiluUnroll * 2;
+    const int nt = tab ? 512 : 256;
+    const uint32_t per_iter = (uint32_t)(nt / 16) * kSiluUnroll;
+    int64_t blocks = (total + per_iter - 1) / per_iter;
+    const int64_t max_blocks = (int64_t)cus * (tab ? 4 : 8);
     if (blocks > max_blocks) blocks = max_blocks;
-    hipLaunchKernelGGL(k_silu_mul_quant, dim3((unsigned)blocks), dim3(kSiluThreads), 0, stream,
-                       x + r0 * ldx, ldx, q, ldq, s, lds, r0, total, (uint32_t)gpr, magic, (int)I, eps,
-                       ue8m0 ? 1 : 0, scale_format);
+    const int u = ue8m0 ? 1 : 0;
+    const uint16_t* xr = x + r0 * ldx;
+    uint8_t* qr = q + r0 * ldq;
+    if (tab)
+      hipLaunchKernelGGL((k_silu_mul_quant<true, 512>), dim3((unsigned)blocks), dim3(512), 0, stream, xr,
+                         (uint32_t)ldx, qr, (uint32_t)ldq, s, lds, r0, total, (uint32_t)gpr, magic,
+                         (uint32_t)I, eps, u, scale_format);
+    else
+      hipLaunchKernelGGL((k_silu_mul_quant<false, 256>), dim3((unsigned)blocks), dim3(256), 0, stream, xr,
+                         (uint32_t)ldx, qr, (uint32_t)ldq, s, lds, r0, total, (uint32_t)gpr, magic,
+                         (uint32_t)I, eps, u, scale_format);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

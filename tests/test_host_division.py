@@ -1,7 +1,9 @@
 """The quantizer kernel divides by the scale with a reciprocal and one FMA
 correction step instead of an IEEE divide (residual taken as q0 s - x so
 that signed zeros come out right without a sign copy), and computes the
-scale amax / 448 the same way.  This CPU test checks, for every pair of
+scale amax / 448 the same way.  For fp32 inputs (the fused producers) the
+first quotient comes from a two-term reciprocal (yd + yl), which makes it
+faithful, before the correction.  This CPU test checks, for every pair of
 (bf16 value significand, scale significand) the activation path can
 produce, for random fp32 values (the fused producers quantize fp32 values),
 and for every fp32 significand divided by 448, that the 3-operation
@@ -62,17 +64,26 @@ def _exact_fma_vec(a, b, c):
     return t
 
 
-def _kernel_div2_vec(x, s, y):
-    """The fp32-input division: two correction steps.  The first makes the
-    quotient faithful (within one ulp), the second rounds it correctly."""
+def _recip_pair(s):
+    """yn = RN(1/s); yd = yn, or its predecessor when s yn > 1; yl = RN(RN(1 - s yd) yd)."""
+    s = s.astype(np.float32)
+    yn = (np.float32(1) / s).astype(np.float32)
+    e = _exact_fma_vec(-s, yn, np.ones_like(s))
+    yd = np.where(e < 0, (yn.view(np.uint32) - np.uint32(1)).view(np.float32), yn).astype(np.float32)
+    yl = (_exact_fma_vec(-s, yd, np.ones_like(s)) * yd).astype(np.float32)
+    assert np.all(yl >= 0)
+    return yn, yd, yl
+
+
+def _kernel_div_f32_vec(x, s):
+    """The fp32-input division: q0 = RN(x yd + RN(x yl)) (faithful), then one
+    Markstein correction with yn = RN(1/s)."""
     x = x.astype(np.float32)
     s = np.broadcast_to(s, x.shape).astype(np.float32)
-    y = np.broadcast_to(y, x.shape).astype(np.float32)
-    q0 = (x * y).astype(np.float32)
-    r0 = _exact_fma_vec(q0, s, -x)
-    q1 = _exact_fma_vec(-r0, y, q0)
-    r1 = _exact_fma_vec(q1, s, -x)
-    return _exact_fma_vec(-r1, y, q1)
+    yn, yd, yl = _recip_pair(s)
+    q0 = _exact_fma_vec(x, yd, (x * yl).astype(np.float32))
+    r = _exact_fma_vec(q0, s, -x)
+    return _exact_fma_vec(-r, yn, q0)
 
 
 def _bf16_significands():
@@ -148,9 +159,9 @@ def test_one_step_division_is_not_enough_for_fp32_inputs():
     assert np.any(r64.astype(np.float32).astype(np.float64) != r64)
 
 
-def test_two_step_division_matches_ieee_for_random_fp32_inputs():
+def test_fp32_division_matches_ieee_for_random_fp32_inputs():
     x, s, y = _random_fp32_groups(1 << 20, 97)
-    got = _kernel_div2_vec(x, s, y)
+    got = _kernel_div_f32_vec(x, s)
     ref = (x / s).astype(np.float32)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     # the hardest significands: x just below a power of two over scales with
@@ -158,15 +169,16 @@ def test_two_step_division_matches_ieee_for_random_fp32_inputs():
     xs = (np.uint32(0x3FFFFFFF) - np.arange(4096, dtype=np.uint32)).view(np.float32)
     for sb in (0x3FFFFFFF, 0x3FFFFF00, 0x3F800001, 0x3FB504F3):
         s1 = np.uint32(sb).view(np.float32)
-        got = _kernel_div2_vec(xs, s1, np.float32(1) / s1)
+        got = _kernel_div_f32_vec(xs, s1)
         assert np.array_equal(got.view(np.uint32), (xs / s1).astype(np.float32).view(np.uint32))
 
 
-def test_two_step_division_signed_zero_and_tiny():
-    for s in (np.float32(1.0), np.float32(3.0) / np.float32(448), np.float32(1e30)):
-        y = np.float32(1) / s
+def test_fp32_division_signed_zero_and_tiny():
+    # scales whose reciprocal pair has yl > 0, yl = 0 (power of two) and yd < yn
+    for s in (np.float32(1.0), np.float32(3.0) / np.float32(448), np.float32(1e30), np.float32(0.3),
+              np.float32(0.7), np.float32(1.1)):
         xs = np.array([0.0, -0.0, -2.0 ** -133, 2.0 ** -133, -1e-38, 1e-30, -3e-36], np.float32)
-        got = _kernel_div2_vec(xs, s, y)
+        got = _kernel_div_f32_vec(xs, s)
         ref = (xs / s).astype(np.float32)
         assert np.array_equal(np.signbit(got), np.signbit(xs))
         big = np.abs(ref) >= 2.0 ** -60
