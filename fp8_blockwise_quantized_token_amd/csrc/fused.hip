@@ -109,24 +109,39 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // resident workgroups), the next rows' loads issued before the current rows
 // are reduced and quantized (two register buffers used in turn), so HBM
 // reads overlap the arithmetic.  The walk is uniform over the workgroup
-// (its barriers); waves whose row is past M only skip their memory traffic.
+// (its barriers); waves whose row is past M compute on a copy of the last
+// row and store nothing.
+// Loads one row's vectors.  Loads are never predicated (so the compiler can
+// count them and wait for exactly the ones it needs): a row past M reads the
+// last row instead, and in masked shapes a vector past H reads the row's
+// last vector and is then zeroed.
 template <int VPL, int WPR, bool FULL>
-__device__ __forceinline__ void rms_load_row(u32x4 (&v)[VPL], const uint16_t* xr, bool active, int wv,
-                                             int lane, int ngroups) {
+__device__ __forceinline__ void rms_load_row(u32x4 (&v)[VPL], const uint16_t* x, int64_t ldx, int64_t row,
+                                             int64_t M, int wv, int lane, int H) {
+  const uint16_t* xr = x + (row < M ? row : M - 1) * ldx;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = ((i * WPR + wv) * 64 + lane) * 8;
-    const bool ok = active && (FULL || (e >> 7) < ngroups);
-    v[i] = ok ? load_nt16(xr + e) : u32x4{0u, 0u, 0u, 0u};
+    if (FULL) {
+      v[i] = load_nt16(xr + e);
+    } else {
+      const u32x4 t = load_nt16(xr + (e < H ? e : H - 8));
+      v[i] = e < H ? t : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
+// WL: the weight is staged once per workgroup in LDS (rows up to 8192
+// values), so the row loop issues no global loads besides the rows' own.
 template <int VPL, int WPR, bool FULL>
 __global__ __launch_bounds__(256) void k_rms_norm_quant(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ w, uint8_t* __restrict__ q,
     int64_t ldq, void* __restrict__ s, int64_t lds, int64_t M, int H, float eps_norm, float eps,
     int ue8m0, int fmt) {
+  constexpr int kCover = VPL * WPR * 512;
+  constexpr bool WL = kCover <= 8192;
   __shared__ double red[2][4];
+  __shared__ float4 wl[WL ? kCover / 4 : 1];
   constexpr int kRowsPerBlock = 4 / WPR;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -137,8 +152,14 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
   int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
   if (base >= M) return;  // uniform over the workgroup
 
+  u32x4 va[VPL], vb[VPL];
+  rms_load_row<VPL, WPR, FULL>(va, x, ldx, base + slot, M, wv, lane, H);
+  if (WL) {
+    for (int i = threadIdx.x; i < H / 4; i += 256) wl[i] = ((const float4*)w)[i];
+    __syncthreads();
+  }
+
   auto process = [&](const u32x4(&v)[VPL], int64_t row, int it) __attribute__((always_inline)) {
-    const bool active = row < M;
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
       const double* rr = &red[it & 1][slot * WPR];
       ss = WPR == 2 ? rr[0] + rr[1] : (rr[0] + rr[1]) + (rr[2] + rr[3]);
     }
-    if (!active) return;
+    if (row >= M) return;
     const float r = (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)eps_norm));
     uint8_t* qr = q + row * ldq;
 #pragma unroll
@@ -167,8 +188,14 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
       const int e = ((i * WPR + wv) * 64 + lane) * 8;
       const int g = e >> 7;
       if (!FULL && g >= ngroups) continue;  // the 16 lanes of a group agree
-      const float4 w0 = *(const float4*)(w + e);
-      const float4 w1 = *(const float4*)(w + e + 4);
+      float4 w0, w1;
+      if (WL) {
+        w0 = wl[e / 4];
+        w1 = wl[e / 4 + 1];
+      } else {
+        w0 = *(const float4*)(w + e);
+        w1 = *(const float4*)(w + e + 4);
+      }
       const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       float y[8];
@@ -184,16 +211,14 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
     }
   };
 
-  u32x4 va[VPL], vb[VPL];
-  rms_load_row<VPL, WPR, FULL>(va, x + (base + slot) * ldx, base + slot < M, wv, lane, ngroups);
   for (int it = 0;; it += 2) {
     int64_t nbase = base + rstep;
-    rms_load_row<VPL, WPR, FULL>(vb, x + (nbase + slot) * ldx, nbase + slot < M, wv, lane, ngroups);
+    rms_load_row<VPL, WPR, FULL>(vb, x, ldx, nbase + slot, M, wv, lane, H);
     process(va, base + slot, it);
     base = nbase;
     if (base >= M) break;
     nbase = base + rstep;
-    rms_load_row<VPL, WPR, FULL>(va, x + (nbase + slot) * ldx, nbase + slot < M, wv, lane, ngroups);
+    rms_load_row<VPL, WPR, FULL>(va, x, ldx, nbase + slot, M, wv, lane, H);
     process(vb, base + slot, it + 1);
     base = nbase;
     if (base >= M) break;
