@@ -76,9 +76,18 @@ def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False) -
 
 
 def kernel_sources(symbol: str):
+    """The source files a kernel is built from (their hash keys the traffic summary)."""
     if symbol.startswith("k_gemm_lds"):
         return ("gemm_standard.hip", "device_common.hpp")
+    if symbol.startswith(("k_group_quant", "k_row_quant")):
+        return ("quant.hip", "device_common.hpp")
+    if symbol.startswith(("k_rms_norm_quant", "k_silu_mul_quant")):
+        return ("fused.hip", "device_common.hpp", "sigmoid_table.inc")
     return ("gemm.hip", "device_common.hpp")
+
+
+PRODUCER_SYMBOLS = {"rms_norm_per_block_quant": "k_rms_norm_quant<8, 1, true>",  # H = 4096
+                    "silu_and_mul_per_block_quant": "k_silu_mul_quant<true, 512>"}  # table path, M = 8192
 
 
 def source_hash(*names: str) -> str:
@@ -228,8 +237,11 @@ def bench_producers(args) -> int:
            "dtype": "bf16-in/fp32-compute/e4m3-out", "data": "synthetic (seeded)",
            "config": {"workload": "producers_qwen3_8b", "H": PRODUCER_H, "I": PRODUCER_I,
                       "m_values": list(PRODUCER_M), "graph_replay": True, "launches_per_graph": reps},
-           "roofline": [{"bound": "hbm", "kernel": r["op"], "achieved": r["gbps"], "peak": PEAK_HBM_GBPS,
-                         "unit": "GB/s", "frac": r["hbm_frac"], "traffic": None} for r in big],
+           "roofline": [{"bound": "hbm", "op": r["op"], "kernel": PRODUCER_SYMBOLS[r["op"]],
+                         "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": r["hbm_frac"], "avg_launch_us": r["us"],
+                         "algorithmic_bytes_per_launch": producer_bytes(r["op"], r["M"]),
+                         "traffic": traffic_from_profiles(PRODUCER_SYMBOLS[r["op"]])} for r in big],
            "cases": rows}
     if not args.no_cpu_baseline:
         t_cpu = b_cpu = 0.0

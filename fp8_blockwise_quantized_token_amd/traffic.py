@@ -11,7 +11,8 @@ Two steps, each under its own rocprofv3 counter pass:
 
 ``run`` launches every case of the workload once through fp8_linear (and
 once through fp8_block_gemm on pre-quantized input, so the Standard GEMM
-kernel is seen alone) plus a plain device-to-device copy of a known size.
+kernel is seen alone), the two fused producers at the producer benchmark's
+largest size, plus a plain device-to-device copy of a known size.
 ``summarize`` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per
 kernel, scales each by what the same counter reads for the copy (bytes
 expected / bytes counted), and records the result keyed by the kernel name
@@ -23,7 +24,6 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
-import hashlib
 import json
 import os
 import sys
@@ -34,26 +34,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 COPY_BYTES = 1 << 30
-PREFIX = "void fp8blk::(anonymous namespace)::"
+PREFIX = "fp8blk::(anonymous namespace)::"
 
 
-def source_hash(*names: str) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(HERE, "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def kernel_sources(symbol: str):
-    if symbol.startswith("k_gemm_lds"):
-        return ("gemm_standard.hip", "device_common.hpp")
-    if symbol.startswith("k_group_quant"):
-        return ("quant.hip", "device_common.hpp")
-    return ("gemm.hip", "device_common.hpp")
+def _bench():
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    return bench
 
 
 def short_name(name: str) -> str:
+    if name.startswith("void "):
+        name = name[len("void "):]
     if name.startswith(PREFIX):
         name = name[len(PREFIX):]
     depth = 0
@@ -99,6 +92,19 @@ def run(workload: str) -> None:
             qa, sa = fb.quantize_activations(x, ue8m0=c.ue8m0)
             fb.block_gemm(qa, sa, qw, sw, cfg)
         torch.cuda.synchronize()
+    # the fused producers at the producer benchmark's largest size
+    bench = _bench()
+    M, H, I = max(bench.PRODUCER_M), bench.PRODUCER_H, bench.PRODUCER_I
+    case = synth.Case("prefill_8b", "producer", M, 128, H, "normal_outlier", False, 7)
+    x = torch.from_numpy(synth.activations_bf16(case).view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(synth.norm_weight_f32(H)).to(dev)
+    print(f"[traffic] rms_norm_per_block_quant M={M} H={H}", flush=True)
+    fb.rms_norm_quant(x, w)
+    case = synth.Case("prefill_8b", "producer", M, 128, 2 * I, "normal_outlier", False, 7)
+    x = torch.from_numpy(synth.activations_bf16(case).view(np.int16)).to(dev).view(torch.bfloat16)
+    print(f"[traffic] silu_and_mul_per_block_quant M={M} I={I}", flush=True)
+    fb.silu_and_mul_quant(x)
+    torch.cuda.synchronize()
 
 
 def _read_counter(d: str, counter: str) -> dict:
@@ -131,6 +137,7 @@ def summarize(dir_f: str, dir_w: str, out_path: str) -> None:
     expected_kib = COPY_BYTES / 1024
     f_fac = expected_kib / copy_f
     w_fac = expected_kib / copy_w
+    bench = _bench()
     kernels = {}
     for name in sorted(set(fetch) & set(write)):
         if not name.startswith("k_"):
@@ -139,7 +146,7 @@ def summarize(dir_f: str, dir_w: str, out_path: str) -> None:
         wb_ = sum(write[name]) / len(write[name]) * w_fac * 1024
         kernels[name] = {"fetch_bytes": round(fb_), "write_bytes": round(wb_),
                          "bytes_per_launch": round(fb_ + wb_), "dispatches": len(fetch[name]),
-                         "source_hash": source_hash(*kernel_sources(name))}
+                         "source_hash": bench.source_hash(*bench.kernel_sources(name))}
     data = {"counters": ["FETCH_SIZE", "WRITE_SIZE"], "unit": "bytes per dispatch (average)",
             "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": copy,
                             "fetch_kib_read": copy_f, "write_kib_read": copy_w,
