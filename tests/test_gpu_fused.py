@@ -243,3 +243,25 @@ def test_silu_and_mul_quant_table_path_all_gate_ranges():
         q, s = _gpu_silu(x, ue8m0)
         rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
         _assert_near(q, s, rq, rs, ("table path", ue8m0))
+
+
+def test_silu_and_mul_quant_row_chunks_with_a_wide_pitch():
+    # a row pitch of 2^27 elements limits one launch to 15 rows (32-bit
+    # offsets), so 40 rows take three launches; only the first 2I columns of
+    # each row are read
+    import torch
+    M, I = 40, 256
+    pitch = 1 << 27
+    x = _x(M, 2 * I, 17)
+    big = torch.empty((M, pitch), dtype=torch.bfloat16, device=dev())
+    big[:, :2 * I] = to_dev_bf16(x)
+    xd = big[:, :2 * I]
+    assert xd.stride(0) == pitch
+    for ue8m0 in (False, True):
+        say("silu wide pitch, chunked rows", M, I, pitch, ue8m0)
+        q, s = fb.silu_and_mul_quant(xd, ue8m0=ue8m0)
+        q, s = host(q), host(s)
+        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
+        _assert_near(q, s, rq, rs, ("wide pitch", ue8m0), max_flip=1.0 / q.size)
+    del big
+    torch.cuda.empty_cache()
