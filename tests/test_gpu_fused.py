@@ -67,15 +67,17 @@ def _assert_near(q, s, rq, rs, what, max_flip=1e-4):
 
 # ----------------------------------------------------------------- RMSNorm
 
-# H covers every kernel shape: exact fits with one wave per row (1536 ..
-# 4096), two waves (5120 .. 8192) and four (12288 .. 32768), and the masked
-# shapes for H not a multiple of 512 (128, 384, 640, 4224, 9216, 20480).
-# M covers 1, ragged multiples of the rows a workgroup holds, and enough
-# rows that every resident workgroup walks several (301, 1001, 4096).
+# (M, H) cover every kernel shape.  Up to 1024 rows (decode): four waves
+# per row for H a multiple of 2048 (2048 .. 16384), two for 5120 and 7168,
+# one otherwise (1536, 2560, 3584); beyond 1024 rows: one wave per row up to
+# 4096, two up to 8192, four beyond.  Masked shapes for H not a multiple of
+# 512 (128, 384, 640, 4224, 9216, 20480).  M covers 1, ragged multiples of
+# the rows a workgroup holds, and enough rows that every resident workgroup
+# walks several.
 RMS_CASES = [(1, 128), (3, 384), (5, 640), (2, 1536), (7, 2048), (3, 2560), (2, 3584), (17, 4096),
-             (4, 4224), (33, 5120), (2, 6144), (3, 7168), (9, 8192), (2, 9216), (6, 12288),
+             (4, 4224), (33, 5120), (2, 6144), (3, 7168), (9, 8192), (2, 9216), (3, 10240), (6, 12288),
              (2, 14336), (4, 16384), (2, 20480), (3, 32768), (301, 4096), (64, 2048), (1001, 5120),
-             (4096, 1024)]
+             (4096, 1024), (2048, 4096), (1100, 8192), (1050, 6144), (1030, 16384), (1025, 7168)]
 
 
 @pytest.mark.parametrize("M,H", RMS_CASES)
