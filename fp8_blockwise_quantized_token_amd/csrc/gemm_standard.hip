@@ -23,7 +23,11 @@
 //   * One v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile and K block gives the
 //     complete block partial P_kb; it is folded into the fp32 accumulator
 //     with one FMA by sa[m][kb] * sw[nb][kb] (a wave's N range lies inside one
-//     128-row weight block, so sw is a scalar per wave and K block).
+//     128-row weight block, so sw is a scalar per wave and K block).  The
+//     matrix core computes the tile transposed (weight fragment as its A
+//     operand, activation fragment as its B): a lane then holds one row m
+//     and four consecutive columns n, so the rescale needs one activation
+//     scale per lane and tile row, and the output leaves in 8-byte stores.
 //   * Tile order: blocks are remapped so that each XCD (blocks are dealt
 //     round-robin to the 8 XCDs) owns a contiguous range of tiles, and tiles
 //     are walked in column groups of GROUP_M tile-rows, so the workgroups
@@ -103,10 +107,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 //
 // P2 (power-of-two scales, the UE8M0 mode): every sa and sw is 2^e, so the
 // K-block scaling is exact in the matrix core itself:
-// v_mfma_scale_f32_16x16x128_f8f6f4 takes an E8M0 exponent per A row (lane
-// l & 15; the same for the lane's four 32-wide K sub-blocks) and per B
-// column, multiplies the block product by 2^(ea + eb - 254) and accumulates
-// into the fp32 tile directly.  No VALU rescale and no product registers.
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes an E8M0 exponent per row of its A
+// operand (here the weight rows: one exponent for the wave's 128-row weight
+// block) and per column of its B operand (here the activation rows: lane
+// l & 15 passes sa's exponent for its row; the same for the lane's four
+// 32-wide K sub-blocks), multiplies the block product by 2^(ea + eb - 254)
+// and accumulates into the fp32 tile directly.  No VALU rescale and no
+// product registers.
 template <int BM, int BN, int WM, int WN, bool SPLIT, int NS, int SM>
 __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams p) {
   using S = Shape<BM, BN, WM, WN>;
@@ -247,11 +254,11 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   static_assert(S::TM % 2 == 0, "row pipeline assumes an even number of tile rows");
   const int arow = wave_m * WM + frow;
   const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
-  const int srow = wave_m * WM + orow;                                 // + 16 per tile row
+  const int srow = wave_m * WM + frow;                                 // + 16 per tile row
   v8i bf[S::TN];
   v8i af[2];
-  v4f scl;      // scales of the row read last
-  v4f gq[2];    // factors sa * sw of the rows in flight
+  float scl;    // activation scale of this lane's row in the tile row read last
+  float gq[2];  // factors sa * sw of the tile rows in flight
   v4f P[2][S::TN];
   float swv;
   uint32_t ea[S::TM];  // P2: E8M0 exponents of sa for row frow of each tile row
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
       for (int i = 0; i < S::TM; ++i) ea[i] = __float_as_uint(ls[erow + i * 16]) >> 23;
     } else if constexpr (!CH) {
-      scl = *(const v4f*)(ls + srow);
+      scl = ls[srow];
     }
   };
 
@@ -290,10 +297,10 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
           if constexpr (P2)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
-                                                                         (int)ea[i], 0, (int)eb);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
+                                                                         (int)eb, 0, (int)ea[i]);
           else  // unscaled accumulate (zero scale operands select the plain instruction)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[cur], bf[j], acc[i][j], 0, 0, 0,
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
                                                                          0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -313,15 +320,15 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       if (i + 1 < S::TM) {
         af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                            *(const u32x4*)(la + a_hi + (i + 1) * 2048));
-        scl = *(const v4f*)(ls + srow + (i + 1) * 16);
+        scl = ls[srow + (i + 1) * 16];
       }
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
-        P[cur][j] = mfma16x16x128(af[cur], bf[j]);
+        P[cur][j] = mfma16x16x128(bf[j], af[cur]);
         if (i > 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[i - 1][j][q] = __builtin_fmaf(P[prv][j][q], gq[prv][q], acc[i - 1][j][q]);
+            acc[i - 1][j][q] = __builtin_fmaf(P[prv][j][q], gq[prv], acc[i - 1][j][q]);
         }
       }
       if (i > 0) {
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     for (int j = 0; j < S::TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        acc[last][j][q] = __builtin_fmaf(P[lc][j][q], gq[lc][q], acc[last][j][q]);
+        acc[last][j][q] = __builtin_fmaf(P[lc][j][q], gq[lc], acc[last][j][q]);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -382,27 +389,36 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   });
   wait_vmcnt<0>();
 
-  // ---- epilogue: lane holds rows orow..orow+3 and column frow of each tile ----
-  float swc[S::TN];  // CH: per-channel weight scales of this lane's columns
+  // ---- epilogue: lane holds row frow and columns orow..orow+3 of each tile
+  // (the products are computed as W A^T, so a lane's four values are
+  // consecutive in n): one 8-byte bf16 store, or one 16-byte fp32 store of
+  // split-K partials, per tile ----
+  v4f swc[S::TN];  // CH: per-channel weight scales of this lane's columns
   if constexpr (CH) {
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j) swc[j] = g.sw[n0 + wave_n * WN + j * 16 + frow];
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) swc[j][q] = g.sw[n0 + wave_n * WN + j * 16 + orow + q];
   }
 #pragma unroll
   for (int i = 0; i < S::TM; ++i) {
+    const int64_t m = m0 + wave_m * WM + i * 16 + frow;
+    if (m >= g.M) continue;
+    const float sam = CH ? g.sa[m] : 1.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t m = m0 + wave_m * WM + i * 16 + orow + q;
-      if (m >= g.M) continue;
-      const float sam = CH ? g.sa[m] : 1.0f;
+    for (int j = 0; j < S::TN; ++j) {
+      const int64_t n = n0 + wave_n * WN + j * 16 + orow;
+      v4f v = acc[i][j];
+      if constexpr (CH) {
 #pragma unroll
-      for (int j = 0; j < S::TN; ++j) {
-        const int64_t n = n0 + wave_n * WN + j * 16 + frow;
-        const float v = CH ? acc[i][j][q] * sam * swc[j] : acc[i][j][q];
-        if (SPLIT)
-          g.ws[((int64_t)split * g.M + m) * g.N + n] = v;
-        else
-          g.y[m * g.ldy + n] = (uint16_t)f32_to_bf16_bits(v);
+        for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
+      }
+      if (SPLIT) {
+        *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
+      } else {
+        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
       }
     }
   }
