@@ -148,15 +148,16 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
     float swv[UNR];
   };
   const int kblast = kb1 - 1;
+  // The activation bytes and the scales of a batch are requested before its
+  // weight fragments: loads complete in order, so the activation operand
+  // (and the fused quantizer's work on it) is ready while the weights are
+  // still streaming in.
   auto load = [&](Batch& b, int kb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int k = kb + u;
       const int kc = max(min(k, kblast), 0);
       const int64_t ko = (int64_t)kc * 128;
-#pragma unroll
-      for (int r = 0; r < RN; ++r)
-        b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
       const float swv = CH ? 0.f : (k <= kblast ? swsrc[kc] : 0.f);
       if (FUSED) b.swv[u] = swv;
       if (LEAN) {
@@ -200,6 +201,13 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
           b.gsc[u][t] = 0.f;
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t ko = (int64_t)max(min(kb + u, kblast), 0) * 128;
+#pragma unroll
+      for (int r = 0; r < RN; ++r)
+        b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
     }
   };
   // fused: quantize one lane's 32 values of group (token, kb) -> operand, scale
