@@ -267,3 +267,43 @@ def test_silu_and_mul_quant_row_chunks_with_a_wide_pitch():
         _assert_near(q, s, rq, rs, ("wide pitch", ue8m0), max_flip=1.0 / q.size)
     del big
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- producers feeding the GEMM
+
+
+@pytest.mark.parametrize("M", [1, 24, 300])
+def test_producers_feed_the_block_gemm(M):
+    """The MLP of a Qwen3-8B layer on the hot path: RMSNorm + group quant ->
+    gate_up GEMM -> SiLU-and-mul + group quant -> down GEMM, every step in
+    the library, against the oracle's chain of the same steps (each GEMM
+    output rounded to bf16 as the library's is).  The codes feeding each
+    GEMM are compared first (RMSNorm: bit-exact; SiLU-and-mul: to its
+    tolerance), then the final output to the GEMM tolerance, on the oracle's
+    own inputs to each GEMM so that no difference carries over."""
+    import torch
+    from gpu_common import assert_close, oracle_weight, sample_rows
+    H, I = 4096, 12288
+    x = _x(M, H, 23)
+    w_norm = synth.norm_weight_f32(H)
+    # gate_up weight [2I, H], down weight [H, I], quantized by the oracle
+    qgu, sgu = oracle_weight(2 * I, H, False)
+    qdn, sdn = oracle_weight(H, I, False)
+    say("mlp chain", M)
+    # library chain
+    qa, sa = fb.rms_norm_quant(to_dev_bf16(x), to_dev(w_norm))
+    h = fb.block_gemm(qa, sa, to_dev(qgu), to_dev(sgu))
+    qh, shh = fb.silu_and_mul_quant(h)
+    y = fb.block_gemm(qh, shh, to_dev(qdn), to_dev(sdn))
+    # oracle chain
+    rqa, rsa = oracle.rms_norm_per_block_quant(x, w_norm)
+    _assert_exact(host(qa), host(sa), rqa, rsa, ("mlp rmsnorm", M))
+    rows = sample_rows(M, 8, key=M)
+    h_ref = oracle.block_gemm(rqa, rsa, qgu, sgu, rows=rows)
+    assert_close(host(h)[rows].astype(np.float64), h_ref, "gate_up")
+    # the library's own bf16 h (within tolerance of the oracle) feeds both sides
+    hb = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    rqh, rsh = oracle.silu_and_mul_per_block_quant(hb)
+    _assert_near(host(qh), host(shh), rqh, rsh, ("mlp silu", M), max_flip=max(1e-4, 2.0 / rqh.size))
+    y_ref = oracle.block_gemm(host(qh), host(shh), qdn, sdn, rows=rows)
+    assert_close(host(y)[rows].astype(np.float64), y_ref, "down")
