@@ -17,23 +17,21 @@
 // RMSNorm (the fp8 RMSNorm example of the Chinese Helion article, section
 // "自己写一个 Helion kernel 并接入 vLLM": variance = mean of squares,
 // rms = sqrt(variance + eps), y = x / rms * weight):
-//   - one wave per row: the row is read once and held in registers, so the
-//     normalization pass costs no second HBM read;
+//   - a row is spread over one, two or four waves and held in registers, so
+//     the normalization pass costs no second HBM read;
 //   - the sum of squares is accumulated in fp64 (every square of a bf16
 //     value is exact there), then 1/sqrt(variance + eps) in fp64 with
 //     correctly rounded sqrt and division, rounded once to fp32;
 //   - y = (x * (1/rms)) * weight in fp32, quantized straight from fp32
 //     (no bf16 rounding in between).
-//   Rows longer than 4096 are split over the four waves of the workgroup,
-//   whose partial sums meet in LDS.  Rows are walked grid-stride and the
-//   next row is loaded while the current one is reduced and quantized.
+//   Rows are walked grid-stride and the next row is loaded while the
+//   current one is reduced and quantized.
 //
 // SiLU-and-mul: x row = [gate (I values) | up (I values)]; y = silu(g) * u
-// = (g u) / (1 + exp(-g)) in fp32 with the hardware exp2 plus a two-FMA
-// argument correction (about an ulp) and one corrected reciprocal division,
-// quantized from fp32.  The arithmetic is trimmed to the few instructions
-// that keep y within about 1.5 ulp: at 5 bytes per element the kernel needs
-// about 30 VALU cycles per element or less to stay on the HBM roofline.
+// in fp32, quantized from fp32.  At 5 bytes per element the kernel must stay
+// near 30 VALU cycles per element to remain on the HBM roofline, so large
+// problems take the logistic function from a correctly rounded table (LDS)
+// and small ones compute it with a trimmed exp2 and a corrected division.
 #include "device_common.hpp"
 #include "launch.hpp"
 
