@@ -67,8 +67,9 @@ def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False) -
     b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
+        wn = 32 if cfg.kwaves == 2 else 64
         sm = 2 if channel else cfg.scale_mode
-        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, 64, {b(cfg.split_k > 1)}, {cfg.stages or 2}, {sm}>"
+        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, {wn}, {b(cfg.split_k > 1)}, {cfg.stages or 2}, {sm}>"
     fq = 0
     if fused:  # the fused quantizer variant the launcher picks for this M
         fq = 16 if cfg.tile_m > 16 or M > 8 else (1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8)

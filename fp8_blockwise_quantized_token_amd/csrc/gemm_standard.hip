@@ -451,10 +451,19 @@ hipError_t run(const GemmArgs& g, int split_k, int sm, hipStream_t stream) {
 
 }  // namespace
 
-// (tile_m, tile_n, LDS stages) combinations that are compiled; stages 0
-// means the default, 2.
-bool standard_tile_supported(int tile_m, int tile_n, int stages) {
+// (tile_m, tile_n, LDS stages, kwaves) combinations that are compiled;
+// stages 0 means the default, 2.  kwaves 2 doubles the waves of the 64x128
+// and 128x128 tiles (each wave 32 columns wide instead of 64): two waves per
+// SIMD hide each other's latencies when the grid holds only one workgroup
+// per CU (M of a few hundred to a few thousand).
+bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves) {
   const int ns = stages == 0 ? 2 : stages;
+  if (kwaves == 2) {
+    if (tile_m == 64 && tile_n == 128) return ns >= 2 && ns <= 4;
+    if (tile_m == 128 && tile_n == 128) return ns == 2 || ns == 3;
+    return false;
+  }
+  if (kwaves != 1) return false;
   if (tile_m == 64 && tile_n == 128) return ns >= 2 && ns <= 4;
   if (tile_m == 128 && tile_n == 128) return ns == 2 || ns == 3;
   if (tile_m == 256 && tile_n == 128) return ns == 2 || ns == 3;
@@ -463,23 +472,31 @@ bool standard_tile_supported(int tile_m, int tile_n, int stages) {
   return false;
 }
 
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages, int kwaves,
                                 int scale_mode, hipStream_t stream) {
-  const int pow2 = scale_mode;  // 0 block fp32, 1 block power-of-two, 2 per-token / per-channel
+  const int sm = scale_mode;  // 0 block fp32, 1 block power-of-two, 2 per-token / per-channel
   const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
-  if (tile_m == 64 && tile_n == 128)
-    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, pow2, stream)
-      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, pow2, stream)
-                : run<64, 128, 32, 64, 2>(g, split_k, pow2, stream);
-  else if (tile_m == 128 && tile_n == 128)
-    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, pow2, stream) : run<128, 128, 64, 64, 2>(g, split_k, pow2, stream);
-  else if (tile_m == 256 && tile_n == 128)
-    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, pow2, stream) : run<256, 128, 64, 64, 2>(g, split_k, pow2, stream);
-  else if (tile_m == 128 && tile_n == 256)
-    e = run<128, 256, 64, 64, 2>(g, split_k, pow2, stream);
-  else if (tile_m == 256 && tile_n == 256)
-    e = run<256, 256, 128, 64, 2>(g, split_k, pow2, stream);
+  if (kwaves == 2) {
+    if (tile_m == 64 && tile_n == 128)
+      e = ns == 4 ? run<64, 128, 32, 32, 4>(g, split_k, sm, stream)
+        : ns == 3 ? run<64, 128, 32, 32, 3>(g, split_k, sm, stream)
+                  : run<64, 128, 32, 32, 2>(g, split_k, sm, stream);
+    else if (tile_m == 128 && tile_n == 128)
+      e = ns == 3 ? run<128, 128, 64, 32, 3>(g, split_k, sm, stream) : run<128, 128, 64, 32, 2>(g, split_k, sm, stream);
+  } else if (tile_m == 64 && tile_n == 128) {
+    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, sm, stream)
+      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, sm, stream)
+                : run<64, 128, 32, 64, 2>(g, split_k, sm, stream);
+  } else if (tile_m == 128 && tile_n == 128) {
+    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, sm, stream) : run<128, 128, 64, 64, 2>(g, split_k, sm, stream);
+  } else if (tile_m == 256 && tile_n == 128) {
+    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, sm, stream) : run<256, 128, 64, 64, 2>(g, split_k, sm, stream);
+  } else if (tile_m == 128 && tile_n == 256) {
+    e = run<128, 256, 64, 64, 2>(g, split_k, sm, stream);
+  } else if (tile_m == 256 && tile_n == 256) {
+    e = run<256, 256, 128, 64, 2>(g, split_k, sm, stream);
+  }
   if (e != hipSuccess || split_k == 1) return e;
   return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
 }

@@ -55,14 +55,16 @@ struct GemmArgs {
   int ue8m0;
 };
 
-// Standard variant: (tile_m, tile_n, LDS stages) among the compiled ones.
+// Standard variant: (tile_m, tile_n, LDS stages, wave layout) among the
+// compiled ones; kwaves 1 = the tile's default waves, 2 = twice as many
+// waves, each half as wide in N (64x128 and 128x128 tiles).
 // scale_mode: kScalesBlock (sa [M][K/128], sw [N/128][K/128], any fp32),
 // kScalesBlockPow2 (same layout, every scale a power of two, applied by the
 // matrix core), kScalesChannel (sa [M], sw [N]: per token / per channel).
 constexpr int kScalesBlock = 0, kScalesBlockPow2 = 1, kScalesChannel = 2;
-bool standard_tile_supported(int tile_m, int tile_n, int stages);
+bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves);
 hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                int scale_mode, hipStream_t stream);
+                                int kwaves, int scale_mode, hipStream_t stream);
 
 // Swap-AB variant.
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);

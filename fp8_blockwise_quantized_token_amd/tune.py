@@ -62,13 +62,16 @@ def candidates(M: int, N: int, K: int):
         if N % tn or (tm >= 128 and M <= 32):
             continue
         tiles = -(-M // tm) * (N // tn)
-        for sk in (1, 2, 4, 8):
+        for sk in (1, 2, 3, 4, 6, 8):
             if sk > 1 and (tiles >= 512 or sk * 2 > kb):
                 continue
             for ns in stages[(tm, tn)]:
                 if ns > 2 and (tiles * sk >= 2048 or kb // sk < ns):
                     continue  # deep pipelines are for few, short K loops
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, 0 if ns == 2 else ns))
+                # twice the waves for grids of about one workgroup per CU
+                if (tm, tn) in ((64, 128), (128, 128)) and tiles * sk <= 1024:
+                    out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 2, 0 if ns == 2 else ns))
     return out
 
 

@@ -94,7 +94,10 @@ extern "C" {
  *             pipeline depth (K blocks staged ahead): 0 (default, = 2) or
  *             2..4 where compiled (64x128: 2-4; 128x128, 256x128: 2-3;
  *             others: 2).  Deeper pipelines hide memory latency in
- *             decode-sized problems.
+ *             decode-sized problems.  kwaves 1 (or 0): the tile's default
+ *             waves; 2: twice the waves, each half as wide (64x128 with
+ *             stages 2-4, 128x128 with stages 2-3), for grids of about one
+ *             workgroup per CU.
  *   SWAPAB:   tile_m (tokens per workgroup) in {16, 32, 64} and >= M,
  *             tile_n (weight rows per workgroup) in {16, 32, 64},
  *             kwaves (waves sharing one tile, each on its own K range,

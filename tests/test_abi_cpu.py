@@ -139,6 +139,11 @@ def test_gemm_argument_errors():
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, stages=4)) == CFG
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 64, 128, stages=5)) == CFG
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 64, 128, stages=1)) == CFG
+    # twice the waves: 64x128 and 128x128 only, at most 4 / 3 stages; kwaves 1 or 2
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 256, 256, kwaves=2)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, kwaves=2, stages=4)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, kwaves=3)) == CFG
+    assert _gemm(M=0, a=None, sa=None, w=None, sw=None, y=None, cfg=fb.make_config(fb.STANDARD, 64, 128, kwaves=2, stages=4)) == OK
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, stages=2)) == CFG
     # split-K needs a workspace of split * M * N * 4 bytes
     sk = fb.make_config(fb.STANDARD, 128, 128, split_k=2)

@@ -79,6 +79,10 @@ def _configs(M, N, K):
         for sk in (1, 3):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, ns))
+    for tm, ns in ((64, 4), (128, 0)):  # twice the waves
+        for sk in (1, 3):
+            if sk <= kb:
+                out.append(fb.make_config(fb.STANDARD, tm, 128, sk, 2, ns))
     for tm in (16, 32, 64):
         if M > tm:
             continue

@@ -36,6 +36,11 @@ def _configs(M, N, K):
         for sk in (1, 3):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, ns))
+    # twice the waves (each 32 columns wide)
+    for tm, tn, ns in ((64, 128, 0), (64, 128, 3), (64, 128, 4), (128, 128, 0), (128, 128, 3)):
+        for sk in (1, 2):
+            if sk <= kb:
+                out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 2, ns))
     for tm in (16, 32, 64):
         if M > tm:
             continue
