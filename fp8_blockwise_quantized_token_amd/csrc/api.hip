@@ -15,6 +15,7 @@ namespace {
 constexpr int64_t kG = FP8BLK_GROUP;
 constexpr int64_t kMaxDim = int64_t(1) << 31;  // every extent fits int32 index math
 constexpr int64_t kMaxK = int64_t(1) << 22;    // the strided quantizer's row division
+constexpr int64_t kMaxPitch = int64_t(1) << 24;  // GEMM operand row pitch in bytes: a tile spans < 2^32 bytes
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -202,6 +203,8 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   st = check_config(c, M, N, K);
   if (st != FP8BLK_OK) return st;
   if (lda < K || ldw < K || ldy < N || ldsa < K / kG || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (lda >= kMaxPitch || ldw >= kMaxPitch || ldsa * 4 >= kMaxPitch || ldsw * 4 >= kMaxPitch)
+    return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;
   if (!a || !sa || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned4(sa) || !aligned4(sw) ||
@@ -269,6 +272,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   st = check_config(c, M, N, K);
   if (st != FP8BLK_OK) return st;
   if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (ldw >= kMaxPitch || ldsw * 4 >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;
   if (!x || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned4(sw) || (ldx * 2) % 16 != 0 ||
@@ -360,6 +364,7 @@ int fp8_scaled_mm(const uint8_t* a, const float* sa, int64_t lda, const uint8_t*
   if (st != FP8BLK_OK) return st;
   if (c.scale_mode != FP8BLK_SCALES_FP32) return FP8BLK_ERR_BAD_CONFIG;  // the scale layout is fixed here
   if (lda < K || ldw < K || ldy < N) return FP8BLK_ERR_BAD_STRIDE;
+  if (lda >= kMaxPitch || ldw >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;
   if (!a || !sa || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned4(sa) || !aligned4(sw) ||

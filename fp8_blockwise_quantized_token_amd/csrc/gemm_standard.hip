@@ -56,6 +56,8 @@ struct StdParams {
 };
 
 constexpr int kGroupM = 8;
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit untyped data).
+constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kXcds = 8;
 
 template <int BM, int BN, int WM, int WN>
@@ -213,21 +215,29 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const uint32_t sc_off = sa_wave ? sa_off : sw_off;
   const int sc_dst = sa_wave ? wave * 64 : BM;
 
+  // Buffer resources over the tile bases (raw, byte-addressed; offsets are
+  // below 2^32 as above).  The buffer form of the direct-to-LDS load keeps
+  // LDS-read waits exact: the compiler treats the global form as a flat
+  // access that may also count on the LDS counter, and then waits for every
+  // outstanding LDS read wherever it needs one.
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, -1, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, -1, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)sc_base, (short)0, -1, kRsrcWord3);
+
   auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
-    const uint8_t* ab = a_base + (int64_t)kb * 128;
-    const uint8_t* bb = b_base + (int64_t)kb * 128;
+    const int kbyte = kb * 128;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[i]),
-                                       (lds_void*)(la + (wave + i * S::WAVES) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(la + (wave + i * S::WAVES) * 1024), 16,
+                                               (int)a_off[i], kbyte, 0, 0);
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bb + b_off[i]),
-                                       (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16,
+                                               (int)b_off[i], kbyte, 0, 0);
     // one 4-byte scale load per wave: waves < SA_INSTR load activation
     // scales, the others the weight scales (the same values, harmless)
     if constexpr (!CH)
-      __builtin_amdgcn_global_load_lds((const void*)(sc_base + kb + sc_off), (lds_void*)(ls + sc_dst), 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(ls + sc_dst), 4, (int)(sc_off * 4u), kb * 4, 0, 0);
   };
 
   v4f acc[S::TM][S::TN];
@@ -261,23 +271,25 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   float gq[2];  // factors sa * sw of the tile rows in flight
   v4f P[2][S::TN];
   float swv;
-  uint32_t ea[S::TM];  // P2: E8M0 exponents of sa for row frow of each tile row
-  const int erow = wave_m * WM + frow;
+  float ear;  // P2: sa of row frow of the tile row read last (its exponent bits are the E8M0 scale)
 
+  // LDS reads complete in issue order, so the reads are issued in the order
+  // of use (pinned by scheduling barriers): the first MFMA waits only for
+  // the first A and B fragments, not for the whole burst.
   auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
-    swv = ls[sw_slot];
+    af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < S::TN; ++j) {
       const int r = wave_n * WN + j * 16 + frow;
       bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
-    if constexpr (P2) {
-#pragma unroll
-      for (int i = 0; i < S::TM; ++i) ea[i] = __float_as_uint(ls[erow + i * 16]) >> 23;
-    } else if constexpr (!CH) {
+    swv = ls[sw_slot];
+    if constexpr (P2)
+      ear = ls[srow];
+    else if constexpr (!CH)
       scl = ls[srow];
-    }
   };
 
   // One K block from the stage (la, ls) whose first fragments are already in
@@ -291,36 +303,41 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
       for (int i = 0; i < S::TM; ++i) {
         const int cur = i & 1, prv = cur ^ 1;
-        if (i + 1 < S::TM)
+        const uint32_t eac = __float_as_uint(ear) >> 23;
+        if (i + 1 < S::TM) {
           af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                              *(const u32x4*)(la + a_hi + (i + 1) * 2048));
+          if constexpr (P2) ear = ls[srow + (i + 1) * 16];
+        }
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
           if constexpr (P2)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
-                                                                         (int)eb, 0, (int)ea[i]);
+                                                                         (int)eb, 0, (int)eac);
           else  // unscaled accumulate (zero scale operands select the plain instruction)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
                                                                          0, 0, 0);
         }
+        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);  // next row's reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_vmcnt<(NS - 2) * PER>();
       __syncthreads();
-      issue(ra, rb, rs, kb_refill);
       read_first(na, nb, ns);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ra, rb, rs, kb_refill);
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
+    float scn = 0.f;  // activation scale of row i+1 (read during row i)
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
-      gq[cur] = scl * swv;                 // row i's scales were read one step ago
-      __builtin_amdgcn_sched_barrier(0);  // ...and are consumed before row i+1's are read
       if (i + 1 < S::TM) {
         af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                            *(const u32x4*)(la + a_hi + (i + 1) * 2048));
-        scl = ls[srow + (i + 1) * 16];
+        scn = ls[srow + (i + 1) * 16];
       }
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
@@ -340,14 +357,17 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      gq[cur] = scl * swv;  // row i's factor, folded during row i+1
+      scl = scn;
     }
     // this wave's loads into the next stage have landed (the NS-2 younger
     // stages may still be in flight); after the barrier every wave's have,
     // and nobody reads the stage just consumed any more
     wait_vmcnt<(NS - 2) * PER>();
     __syncthreads();
-    issue(ra, rb, rs, kb_refill);
     read_first(na, nb, ns);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(ra, rb, rs, kb_refill);
     constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)

@@ -34,6 +34,9 @@
  *     FP8BLK_ERR_HIP.  M == 0 (or n == 0) is a no-op returning FP8BLK_OK.
  *   - Required alignment: every base pointer 16 bytes, every fp8/bf16 row
  *     pitch a multiple of 16 bytes; scale pointers 4 bytes.
+ *   - GEMM operand row pitches (A, W and their scale arrays, in bytes) are
+ *     below 2^24, so that a 256-row tile spans less than 2^32 bytes
+ *     (FP8BLK_ERR_BAD_STRIDE otherwise).
  *   - Inputs must be finite; NaN/Inf inputs give unspecified (but memory-safe)
  *     results.
  */

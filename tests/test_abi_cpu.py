@@ -114,6 +114,11 @@ def test_gemm_argument_errors():
     assert _gemm(ldy=128, cfg=std) == STRIDE
     assert _gemm(ldsa=1, cfg=std) == STRIDE
     assert _gemm(ldsw=1, cfg=std) == STRIDE
+    # operand row pitches below 2^24 bytes (a 256-row tile spans < 2^32 bytes)
+    big = 1 << 24
+    assert _gemm(lda=big, cfg=std) == STRIDE and _gemm(lda=big - 16, M=0, cfg=std) == OK
+    assert _gemm(ldw=big, cfg=std) == STRIDE and _gemm(ldw=big, cfg=None) == STRIDE
+    assert _gemm(ldsa=big // 4, cfg=std) == STRIDE and _gemm(ldsw=big // 4, cfg=std) == STRIDE
     assert _gemm(a=A + 1, cfg=std) == MISAL
     assert _gemm(w=C + 8, cfg=std) == MISAL
     assert _gemm(y=E + 2, cfg=std) == MISAL
@@ -220,6 +225,7 @@ def test_linear_argument_errors():
     assert _lin(ldw=128, cfg=sw1) == STRIDE
     assert _lin(ldy=128, cfg=sw1) == STRIDE
     assert _lin(ldsw=1, cfg=sw1) == STRIDE
+    assert _lin(ldw=1 << 24, cfg=sw1) == STRIDE and _lin(ldsw=1 << 22, cfg=sw1) == STRIDE
     assert _lin(x=A + 2, cfg=sw1) == MISAL
     assert _lin(ldx=260, cfg=sw1) == MISAL
     assert _lin(M=40, cfg=sw1) == CFG  # Swap-AB tile_m < M
@@ -270,6 +276,7 @@ def test_dynamic_entry_argument_errors():
     assert sm(a=None, cfg=std) == NULL and sm(sa=None, cfg=std) == NULL and sm(sw=None, cfg=std) == NULL
     assert sm(K=200, cfg=std) == SHAPE and sm(N=200, cfg=std) == SHAPE
     assert sm(lda=128, cfg=std) == STRIDE and sm(ldy=128, cfg=std) == STRIDE
+    assert sm(lda=1 << 24, cfg=std) == STRIDE and sm(ldw=1 << 24, cfg=std) == STRIDE
     assert sm(sa=B + 2, cfg=std) == MISAL and sm(a=A + 1, cfg=std) == MISAL
     assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=fb.SCALES_POW2)) == CFG
     assert sm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=2)) == WS
