@@ -35,6 +35,7 @@ FLAG_UE8M0 = 1
 STANDARD = 0
 SWAPAB = 1
 DEFAULT_EPS = 1e-10
+MIN_EPS = 2.0 ** -80  # smallest eps the library accepts (FP8BLK_MIN_EPS)
 
 _STATUS = {0: "ok", -1: "null pointer", -2: "unsupported shape", -3: "misaligned",
            -4: "leading dimension too small", -5: "workspace too small",

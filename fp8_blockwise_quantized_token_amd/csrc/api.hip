@@ -98,7 +98,7 @@ int check_group_scales(uint32_t flags, int64_t M, int64_t K, int64_t lds, int* f
 }
 
 int check_quant_args(float eps, uint32_t flags) {
-  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps >= FP8BLK_MIN_EPS) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
   if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
   return FP8BLK_OK;
 }
@@ -127,7 +127,7 @@ int fp8_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_
                     void* s, int64_t lds, int32_t group, float eps, uint32_t flags, void* stream) {
   if (group != kG) return FP8BLK_ERR_BAD_SHAPE;
   if (M < 0 || K <= 0 || K % kG != 0 || K > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
-  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps >= FP8BLK_MIN_EPS) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
   int fmt = 0;
   const int st = check_group_scales(flags, M, K, lds, &fmt);
   if (st != FP8BLK_OK) return st;
@@ -145,7 +145,7 @@ int fp8_weight_block_quant(const float* w, int64_t N, int64_t K, int64_t ldw, ui
                            void* stream) {
   if (N < 0 || K < 0 || N % kG != 0 || K % kG != 0 || N >= kMaxDim || K >= kMaxDim)
     return FP8BLK_ERR_BAD_SHAPE;
-  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps >= FP8BLK_MIN_EPS) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
   if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
   if (ldw < K || ldq < K || lds < K / kG) return FP8BLK_ERR_BAD_STRIDE;
   if (N == 0 || K == 0) return FP8BLK_OK;
@@ -399,7 +399,7 @@ int fp8_rms_norm_per_block_quant(const uint16_t* x, int64_t M, int64_t H, int64_
                                  float eps_norm, uint8_t* q, int64_t ldq, void* s, int64_t lds, float eps,
                                  uint32_t flags, void* stream) {
   if (M < 0 || H <= 0 || H % kG != 0 || H > fp8blk::kRmsMaxH || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
-  if (!(eps > 0.0f) || !isfinite(eps) || !(eps_norm >= 0.0f) || !isfinite(eps_norm))
+  if (!(eps >= FP8BLK_MIN_EPS) || !isfinite(eps) || !(eps_norm >= 0.0f) || !isfinite(eps_norm))
     return FP8BLK_ERR_BAD_SHAPE;
   int fmt = 0;
   const int st = check_group_scales(flags, M, H, lds, &fmt);
@@ -418,7 +418,7 @@ int fp8_silu_and_mul_per_block_quant(const uint16_t* x, int64_t M, int64_t I, in
                                      int64_t ldq, void* s, int64_t lds, float eps, uint32_t flags,
                                      void* stream) {
   if (M < 0 || I <= 0 || I % kG != 0 || I > kMaxK || M >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
-  if (!(eps > 0.0f) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
+  if (!(eps >= FP8BLK_MIN_EPS) || !isfinite(eps)) return FP8BLK_ERR_BAD_SHAPE;
   int fmt = 0;
   const int st = check_group_scales(flags, M, I, lds, &fmt);
   if (st != FP8BLK_OK) return st;

@@ -92,14 +92,15 @@ __device__ __forceinline__ float div_by_scale_f32(float x, float s, const Recip&
 // the one-step corrected product with RN(1/448) (3 operations instead of
 // an IEEE divide): for the divisor 448 its residual is exact and its result
 // equals IEEE division for every fp32 significand (checked exhaustively by
-// the test-suite; exponents scale every step exactly).  Below 2^-100, where
-// the residual could lose bits to underflow, the IEEE divide is used.
+// the test-suite; exponents scale every step exactly) from 2^-100 up.  The
+// entry points accept eps >= 2^-80 only, so max(amax, eps) is always in
+// that range.  No branch: the work of several groups schedules together.
 __device__ __forceinline__ float scale_from_amax(float amax, float eps, bool ue8m0) {
   const float a = amax > eps ? amax : eps;
-  float s = a >= 0x1p-100f ? div_by_scale(a, kE4M3Max, kInv448) : a / kE4M3Max;
+  float s = div_by_scale(a, kE4M3Max, kInv448);
   if (ue8m0) {
     uint32_t b = __float_as_uint(s);
-    if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+    b = (b & 0x007FFFFFu) ? (b & 0x7F800000u) + 0x00800000u : b;
     s = __uint_as_float(b);
   }
   return s;

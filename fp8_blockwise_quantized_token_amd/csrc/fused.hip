@@ -69,6 +69,33 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float eps, bool ue8
   return make_uint2(lo, hi);
 }
 
+// Maximum over the 8 lanes of each half DPP row (lanes 8k .. 8k+7).
+__device__ __forceinline__ uint32_t row8_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  return v;
+}
+
+// quant8 for 16 values per lane and 8 lanes per group: the per-group work
+// (amax reduction, scale, reciprocal) is shared by twice as many values.
+__device__ __forceinline__ u32x4 quant16(const float (&y)[16], float eps, bool ue8m0, float* sc_out) {
+  float m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    m[k] = fmaxf(fmaxf(fabsf(y[4 * k]), fabsf(y[4 * k + 1])), fmaxf(fabsf(y[4 * k + 2]), fabsf(y[4 * k + 3])));
+  const uint32_t am = row8_max_u32(__float_as_uint(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))));
+  const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
+  const Recip rc = recip_of_scale(sc);
+  *sc_out = sc;
+  u32x4 c;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    c[k] = encode4(div_by_scale_f32(y[4 * k], sc, rc), div_by_scale_f32(y[4 * k + 1], sc, rc),
+                   div_by_scale_f32(y[4 * k + 2], sc, rc), div_by_scale_f32(y[4 * k + 3], sc, rc));
+  return c;
+}
+
 // 64-bit DPP move of a double (each 32-bit half moved with the same control).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
@@ -99,11 +126,11 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // ---------------------------------------------------------------- RMSNorm
 //
 // WPR waves per row (1, 2 or 4; 4 / WPR rows per workgroup), VPL vectors of
-// 8 values per lane: vector i of wave w (of its row), lane l covers elements
-// 8 * ((i * WPR + w) * 64 + l) .. +8, so each vector instruction of a wave
-// reads 4 whole groups (1 KiB).  A row covers WPR * 512 * VPL elements;
-// FULL when that is exactly H, else groups past H are masked (per 16
-// lanes).  Workgroups walk their row slots grid-stride (one round of
+// 8 values per lane (placement in rms_elem: with an even VPL a lane holds 16
+// consecutive values of one group, so a group's amax, scale and reciprocal
+// are shared by 16 values per lane instead of 8).  A row covers
+// WPR * 512 * VPL elements; FULL when that is exactly H, else groups past H
+// are masked (the lanes of a group agree).  Workgroups walk their row slots grid-stride (one round of
 // resident workgroups), the next rows' loads issued before the current rows
 // are reduced and quantized (two register buffers used in turn), so HBM
 // reads overlap the arithmetic.  The walk is uniform over the workgroup
@@ -113,13 +140,26 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // count them and wait for exactly the ones it needs): a row past M reads the
 // last row instead, and in masked shapes a vector past H reads the row's
 // last vector and is then zeroed.
+// First element of vector i of wave wv (of its row), lane `lane`.  Even VPL:
+// vectors go in pairs and lane l of pair p holds the 16 consecutive values
+// 16 * ((p * WPR + wv) * 64 + l) .. +16 (8 lanes per group; the two loads of
+// a pair read 16-byte pieces 32 bytes apart, together a contiguous 2 KiB).
+// Odd VPL: lane l of vector i holds 8 values, 16 lanes per group.
+template <int VPL, int WPR>
+__device__ __forceinline__ int rms_elem(int i, int wv, int lane) {
+  if constexpr (VPL % 2 == 0)
+    return 16 * (((i >> 1) * WPR + wv) * 64 + lane) + 8 * (i & 1);
+  else
+    return 8 * ((i * WPR + wv) * 64 + lane);
+}
+
 template <int VPL, int WPR, bool FULL>
 __device__ __forceinline__ void rms_load_row(u32x4 (&v)[VPL], const uint16_t* x, int64_t ldx, int64_t row,
                                              int64_t M, int wv, int lane, int H) {
   const uint16_t* xr = x + (row < M ? row : M - 1) * ldx;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int e = ((i * WPR + wv) * 64 + lane) * 8;
+    const int e = rms_elem<VPL, WPR>(i, wv, lane);
     if (FULL) {
       v[i] = load_nt16(xr + e);
     } else {
@@ -138,6 +178,9 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
     int ue8m0, int fmt) {
   constexpr int kCover = VPL * WPR * 512;
   constexpr bool WL = kCover <= 8192;
+  constexpr int VPU = VPL % 2 == 0 ? 2 : 1;  // vectors per group share of a lane
+  constexpr int NU = VPL / VPU;              // group shares per lane and row
+  constexpr int LPG = 16 / VPU;              // lanes per group
   __shared__ double red[2][4];
   __shared__ float4 wl[WL ? kCover / 4 : 1];
   constexpr int kRowsPerBlock = 4 / WPR;
@@ -181,31 +224,48 @@ __global__ __launch_bounds__(256) void k_rms_norm_quant(
     if (row >= M) return;
     const float r = (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)eps_norm));
     uint8_t* qr = q + row * ldq;
+    auto weight4 = [&](int e) __attribute__((always_inline)) -> float4 {
+      return WL ? wl[e / 4] : *(const float4*)(w + e);
+    };
+    // scales are kept and stored together after the row (one masked region)
+    float scs[NU];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = ((i * WPR + wv) * 64 + lane) * 8;
-      const int g = e >> 7;
-      if (!FULL && g >= ngroups) continue;  // the 16 lanes of a group agree
-      float4 w0, w1;
-      if (WL) {
-        w0 = wl[e / 4];
-        w1 = wl[e / 4 + 1];
+    for (int u = 0; u < NU; ++u) {
+      const int e = rms_elem<VPL, WPR>(u * VPU, wv, lane);
+      scs[u] = 0.f;
+      if (!FULL && (e >> 7) >= ngroups) continue;  // the lanes of a group agree
+      if constexpr (VPU == 2) {
+        const float4 w0 = weight4(e), w1 = weight4(e + 4), w2 = weight4(e + 8), w3 = weight4(e + 12);
+        const float wj[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
+                              w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
+        const uint32_t c[8] = {v[2 * u].x, v[2 * u].y, v[2 * u].z, v[2 * u].w,
+                               v[2 * u + 1].x, v[2 * u + 1].y, v[2 * u + 1].z, v[2 * u + 1].w};
+        float y[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          y[2 * k] = (bf16_lo(c[k]) * r) * wj[2 * k];
+          y[2 * k + 1] = (bf16_hi(c[k]) * r) * wj[2 * k + 1];
+        }
+        *(u32x4*)(qr + e) = quant16(y, eps, ue8m0 != 0, &scs[u]);
       } else {
-        w0 = *(const float4*)(w + e);
-        w1 = *(const float4*)(w + e + 4);
-      }
-      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      float y[8];
+        const float4 w0 = weight4(e), w1 = weight4(e + 4);
+        const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const uint32_t c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        float y[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        y[2 * k] = (bf16_lo(c[k]) * r) * wj[2 * k];
-        y[2 * k + 1] = (bf16_hi(c[k]) * r) * wj[2 * k + 1];
+        for (int k = 0; k < 4; ++k) {
+          y[2 * k] = (bf16_lo(c[k]) * r) * wj[2 * k];
+          y[2 * k + 1] = (bf16_hi(c[k]) * r) * wj[2 * k + 1];
+        }
+        *(uint2*)(qr + e) = quant8(y, eps, ue8m0 != 0, &scs[u]);
       }
-      float sc;
-      const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
-      *(uint2*)(qr + e) = codes;
-      if ((lane & 15) == 0) store_scale(s, fmt, lds, row, g, sc);
+    }
+    if ((lane & (LPG - 1)) == 0) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int g = rms_elem<VPL, WPR>(u * VPU, wv, lane) >> 7;
+        if (FULL || g < ngroups) store_scale(s, fmt, lds, row, g, scs[u]);
+      }
     }
   };
 

@@ -53,6 +53,12 @@ extern "C" {
 #define FP8BLK_ABI_VERSION 3
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
+/* Smallest accepted eps (2^-80, about 8.3e-25).  With eps at least this,
+   every scale is at least 2^-88.8, which keeps the kernels' shortcut
+   divisions (x / s from a reciprocal and one exact-residual correction)
+   exact for every quotient that can reach an fp8 code; smaller eps values
+   return FP8BLK_ERR_BAD_SHAPE.  The pages' value is 1e-10. */
+#define FP8BLK_MIN_EPS 8.271806125530277e-25f /* 2^-80 */
 
 /* status codes */
 #define FP8BLK_OK 0
@@ -142,7 +148,7 @@ const char *fp8_status_string(int status);
  *         (FP8BLK_FLAG_SCALE_MN_MAJOR: [K/128][lds], lds >= M;
  *          FP8BLK_FLAG_SCALE_E8M0: uint8 E8M0 bytes in that layout)
  *   flags: FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_SCALE_E8M0 | FP8BLK_FLAG_SCALE_MN_MAJOR.
- *   Requires K % 128 == 0, M >= 0, eps > 0 and finite.
+ *   Requires K % 128 == 0, M >= 0, eps >= FP8BLK_MIN_EPS and finite.
  */
 int fp8_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                     uint8_t *q, int64_t ldq, void *s, int64_t lds,
@@ -156,7 +162,7 @@ int fp8_group_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  * Format: autotuning page, "Helion Linear Backend" / "Scope" (128x128
  * weight scaling).
  *   w fp32 [N][ldw], ldw >= K;  q uint8 [N][ldq];  s fp32 [N/128][lds], lds >= K/128.
- *   Requires N % 128 == 0 and K % 128 == 0.
+ *   Requires N % 128 == 0, K % 128 == 0, eps >= FP8BLK_MIN_EPS and finite.
  */
 int fp8_weight_block_quant(const float *w, int64_t N, int64_t K, int64_t ldw,
                            uint8_t *q, int64_t ldq, float *s, int64_t lds,
@@ -260,7 +266,8 @@ int fp8_linear(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw
  * s[m] = max(amax, eps)/448 (power-of-two ceiling with FP8BLK_FLAG_UE8M0),
  * q[m][k] = e4m3fn_rne(clamp(x / s[m], -448, 448)).
  *   x bf16 [M][ldx], ldx >= K;  q uint8 [M][ldq], ldq >= K;  s fp32 [M].
- *   Requires K % 128 == 0 and K <= 32768 (a row is held in registers);
+ *   Requires K % 128 == 0, K <= 32768 (a row is held in registers) and
+ *   eps >= FP8BLK_MIN_EPS;
  *   x and q 16-byte aligned with 16-byte row pitches, s 4-byte aligned.
  */
 int fp8_token_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
@@ -272,7 +279,7 @@ int fp8_token_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  * weights): for every row n of W, s[n] = max(amax_row, eps)/448 [power-of-
  * two ceiling], q = e4m3fn_rne(clamp(w / s[n], -448, 448)) (IEEE division).
  *   w fp32 [N][ldw], ldw >= K;  q uint8 [N][ldq];  s fp32 [N].
- *   Requires K % 128 == 0 and K <= 32768.
+ *   Requires K % 128 == 0, K <= 32768 and eps >= FP8BLK_MIN_EPS.
  */
 int fp8_weight_channel_quant(const float *w, int64_t N, int64_t K, int64_t ldw,
                              uint8_t *q, int64_t ldq, float *s, float eps,
@@ -308,7 +315,7 @@ int fp8_scaled_mm(const uint8_t *a, const float *sa, int64_t lda,
  *   q      uint8 [M][ldq], ldq >= H
  *   s      as fp8_group_quant's with K = H (fp32 [M][lds], lds >= H/128;
  *          MN-major / E8M0 by the same flags)
- *   Requires H % 128 == 0, H <= 32768, M >= 0, eps > 0, eps_norm >= 0
+ *   Requires H % 128 == 0, H <= 32768, M >= 0, eps >= FP8BLK_MIN_EPS, eps_norm >= 0
  *   (both finite).  x, weight, q 16-byte aligned; ldx * 2 and ldq multiples
  *   of 16.  Finite inputs only.
  */
@@ -330,7 +337,7 @@ int fp8_rms_norm_per_block_quant(const uint16_t *x, int64_t M, int64_t H, int64_
  * exp(80): for g < -80, |y| < 1e-30 |g u| either way.
  *   x  bf16 [M][ldx], ldx >= 2I          q uint8 [M][ldq], ldq >= I
  *   s  as fp8_group_quant's with K = I
- *   Requires I % 128 == 0, I <= 4194304, M >= 0, eps > 0 and finite; alignment as
+ *   Requires I % 128 == 0, I <= 4194304, M >= 0, eps >= FP8BLK_MIN_EPS and finite; alignment as
  *   fp8_group_quant.  Finite inputs only.
  */
 int fp8_silu_and_mul_per_block_quant(const uint16_t *x, int64_t M, int64_t I, int64_t ldx,

@@ -56,6 +56,9 @@ def test_group_quant_argument_errors():
     assert _gq(group=64) == SHAPE
     assert _gq(eps=0.0) == SHAPE
     assert _gq(eps=float("inf")) == SHAPE
+    # eps below the floor 2^-80 is rejected; the floor itself is accepted
+    assert _gq(eps=2.0 ** -81) == SHAPE and _gq(eps=1e-38) == SHAPE
+    assert _gq(eps=2.0 ** -80, M=0) == OK
     assert _gq(flags=2) == CFG
     assert _gq(ldx=128) == STRIDE
     assert _gq(ldq=128) == STRIDE
@@ -78,6 +81,7 @@ def test_weight_quant_argument_errors():
     assert _wq(N=200) == SHAPE
     assert _wq(K=200, ldw=200, ldq=200) == SHAPE
     assert _wq(ldw=128) == STRIDE
+    assert _wq(eps=2.0 ** -81) == SHAPE and _wq(eps=0.0) == SHAPE
     assert _wq(w=A + 4) == MISAL
     assert _wq(ldw=257) == MISAL
     assert _wq(flags=4) == CFG
@@ -218,7 +222,7 @@ def test_linear_argument_errors():
     assert _lin(M=-1, cfg=sw1) == SHAPE
     assert _lin(K=(1 << 22) + 128, ldx=(1 << 22) + 128, ldw=(1 << 22) + 128, ldsw=1 << 16,
                 cfg=sw1) == SHAPE
-    assert _lin(eps=0.0, cfg=sw1) == SHAPE
+    assert _lin(eps=0.0, cfg=sw1) == SHAPE and _lin(eps=2.0 ** -81, cfg=sw1) == SHAPE
     assert _lin(eps=float("nan"), cfg=sw1) == SHAPE
     assert _lin(flags=2, cfg=sw1) == CFG
     assert _lin(ldx=128, cfg=sw1) == STRIDE
@@ -262,6 +266,7 @@ def test_dynamic_entry_argument_errors():
     assert tq(K=200, ldx=256, ldq=256) == SHAPE
     assert tq(K=32768 + 128, ldx=40000, ldq=40000) == SHAPE
     assert tq(M=-1) == SHAPE and tq(eps=0.0) == SHAPE and tq(flags=2) == CFG
+    assert tq(eps=2.0 ** -81) == SHAPE
     assert tq(ldx=128) == STRIDE and tq(ldq=128) == STRIDE
     assert tq(x=A + 2) == MISAL and tq(ldx=260) == MISAL and tq(s=C + 2) == MISAL
     assert tq(M=0, x=None, q=None, s=None) == OK
@@ -269,6 +274,7 @@ def test_dynamic_entry_argument_errors():
         L.fp8_weight_channel_quant(w, N, K, ldw, q, ldq, s, eps, flags, None)
     assert cq(w=None) == NULL and cq(K=100, ldw=256, ldq=256) == SHAPE and cq(ldw=200) == STRIDE
     assert cq(ldw=258) == MISAL and cq(N=0, w=None, q=None, s=None) == OK
+    assert cq(eps=2.0 ** -81) == SHAPE
     sm = lambda a=A, sa=B, lda=256, w=C, sw=D, ldw=256, y=E, ldy=256, M=8, N=256, K=256, cfg=None, ws=None, n=0: \
         L.fp8_scaled_mm(a, sa, lda, w, sw, ldw, y, ldy, M, N, K,
                         ctypes.byref(cfg) if cfg is not None else None, ws, n, None)
@@ -304,6 +310,7 @@ def test_fused_producer_argument_errors():
     assert rq(H=200, ldx=256, ldq=256) == SHAPE and rq(H=0) == SHAPE and rq(M=-1) == SHAPE
     assert rq(H=32768 + 128, ldx=40000, ldq=40000, lds=300) == SHAPE
     assert rq(eps=0.0) == SHAPE and rq(en=-1.0) == SHAPE and rq(en=float("inf")) == SHAPE
+    assert rq(eps=2.0 ** -81) == SHAPE
     assert rq(en=float("nan")) == SHAPE
     assert rq(ldx=128) == STRIDE and rq(ldq=128) == STRIDE and rq(lds=1) == STRIDE
     assert rq(flags=2) == CFG and rq(flags=8) == CFG and rq(flags=4, lds=3) == STRIDE
@@ -315,6 +322,7 @@ def test_fused_producer_argument_errors():
     assert sq(x=None) == NULL and sq(q=None) == NULL and sq(s=None) == NULL
     assert sq(I=200, ldx=512, ldq=256) == SHAPE and sq(I=0) == SHAPE and sq(M=-1) == SHAPE
     assert sq(eps=0.0) == SHAPE and sq(flags=2) == CFG and sq(flags=16) == CFG
+    assert sq(eps=2.0 ** -81) == SHAPE
     assert sq(ldx=511) == STRIDE and sq(ldx=256) == STRIDE and sq(ldq=128) == STRIDE
     assert sq(lds=1) == STRIDE and sq(flags=4, lds=3) == STRIDE
     assert sq(x=A + 2) == MISAL and sq(ldx=516) == MISAL and sq(s=C + 2) == MISAL

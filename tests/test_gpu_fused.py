@@ -128,6 +128,25 @@ def test_rms_norm_quant_edge_rows():
     assert q.shape == (0, H)
 
 
+@pytest.mark.parametrize("M,H", [(5, 4096), (1200, 4096), (3, 640)])
+def test_rms_norm_quant_smallest_eps(M, H):
+    # eps at the accepted floor 2^-80: zero groups get the scale 2^-80 / 448,
+    # and a group with amax just above eps (weights 2^-80) still matches the
+    # oracle bit for bit (the shortcut divisions stay exact down there)
+    x = _x(M, H, 13, dist="normal")
+    x[0] = 0                                      # zero row: eps_norm only, zero groups
+    x[1 % M, : H // 2] = 0                        # half a row of zero groups
+    w = synth.norm_weight_f32(H)
+    w[:128] = np.float32(2.0 ** -80)              # |x r| of a few units -> amax near 2^-79
+    eps = np.float32(2.0 ** -80)
+    for ue8m0 in (False, True):
+        say("rms smallest eps", M, H, ue8m0)
+        q, s = fb.rms_norm_quant(to_dev_bf16(x), to_dev(w), eps_norm=1e-6, eps=float(eps), ue8m0=ue8m0)
+        rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6, eps=eps, ue8m0=ue8m0)
+        _assert_exact(host(q), host(s), rq, rs, ("smallest eps", M, H, ue8m0))
+        assert rs[0, 0] == (np.float32(2.0 ** -88) if ue8m0 else eps / np.float32(448))
+
+
 def test_rms_norm_quant_strided_formats_and_padding():
     import torch
     M, H = 37, 1152
@@ -202,6 +221,29 @@ def test_silu_and_mul_quant_special_gates():
         q, s = _gpu_silu(x, ue8m0)
         rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
         _assert_exact(q, s, rq, rs, ("special", ue8m0))
+
+
+@pytest.mark.parametrize("M,I", [(4, 1024), (600, 12288)])
+def test_silu_and_mul_quant_smallest_eps(M, I):
+    # eps at the floor 2^-80: zero gates give zero groups with the scale
+    # 2^-80 / 448 exactly, and a row with gate 2^-40 and up near 2^-40 has
+    # group amaxes just above eps
+    x = _x(M, 2 * I, 17, dist="normal")
+    x[0, :I] = 0
+    gen = synth.generator(52)
+    x[1 % M, :I] = synth.to_bf16_bits(np.full((1, I), 2.0 ** -40, np.float32))[0]
+    x[1 % M, I:] = synth.to_bf16_bits((gen.standard_normal((1, I)) * 2.0 ** -40).astype(np.float32))[0]
+    eps = np.float32(2.0 ** -80)
+    for ue8m0 in (False, True):
+        say("silu smallest eps", M, I, ue8m0)
+        q, s = fb.silu_and_mul_quant(to_dev_bf16(x), eps=float(eps), ue8m0=ue8m0)
+        rq, rs = oracle.silu_and_mul_per_block_quant(x, eps=eps, ue8m0=ue8m0)
+        q, s = host(q), host(s)
+        assert np.all(s[0] == rs[0]) and np.all(q[0] == rq[0])  # zero groups: exact
+        if ue8m0:
+            assert np.array_equal(s, rs)
+        _assert_near(q, s, rq, rs, ("silu smallest eps", M, I, ue8m0), max_flip=max(1e-4, 1.0 / q.size))
+        assert np.all(rs[1 % M] < np.float32(2.0 ** -75))
 
 
 def test_silu_and_mul_quant_strided_formats_and_padding():
