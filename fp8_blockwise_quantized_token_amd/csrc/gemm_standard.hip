@@ -224,20 +224,41 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, -1, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc((void*)sc_base, (short)0, -1, kRsrcWord3);
 
-  auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
+  // The PER direct-to-LDS loads of one stage, numbered A tile rows, B tile
+  // rows, scales; issue_part issues those numbered [LO, HI).
+  auto issue_part = [&](auto lo_c, auto hi_c, uint8_t* la, uint8_t* lb, float* ls, int kb)
+                        __attribute__((always_inline)) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
     const int kbyte = kb * 128;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(la + (wave + i * S::WAVES) * 1024), 16,
-                                               (int)a_off[i], kbyte, 0, 0);
+      if (i >= LO && i < HI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(la + (wave + i * S::WAVES) * 1024), 16,
+                                                 (int)a_off[i], kbyte, 0, 0);
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16,
-                                               (int)b_off[i], kbyte, 0, 0);
+      if (S::A_INSTR + i >= LO && S::A_INSTR + i < HI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(lb + (wave + i * S::WAVES) * 1024), 16,
+                                                 (int)b_off[i], kbyte, 0, 0);
     // one 4-byte scale load per wave: waves < SA_INSTR load activation
     // scales, the others the weight scales (the same values, harmless)
-    if constexpr (!CH)
+    constexpr int IS = S::A_INSTR + S::B_INSTR;
+    if constexpr (!CH && IS >= LO && IS < HI)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(ls + sc_dst), 4, (int)(sc_off * 4u), kb * 4, 0, 0);
+  };
+  auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
+    issue_part(ic<0>{}, ic<PER>{}, la, lb, ls, kb);
+  };
+  // A stage's loads are spread over the first DMA_ROWS tile rows of the
+  // block before (DMA_PER per row) rather than issued in one burst: eight
+  // waves issuing all of theirs at once after a barrier stall on the
+  // vector-memory queue instead of feeding the matrix cores.
+  constexpr int DMA_ROWS = S::TM < 4 ? S::TM : 4;
+  constexpr int DMA_PER = (PER + DMA_ROWS - 1) / DMA_ROWS;
+  auto issue_row = [&](auto row_c, uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
+    constexpr int R = decltype(row_c)::value;
+    constexpr int LO = R * DMA_PER, HI = (R + 1) * DMA_PER < PER ? (R + 1) * DMA_PER : PER;
+    if constexpr (LO < PER) issue_part(ic<LO>{}, ic<HI>{}, la, lb, ls, kb);
   };
 
   v4f acc[S::TM][S::TN];
@@ -293,8 +314,14 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   };
 
   // One K block from the stage (la, ls) whose first fragments are already in
-  // registers; afterwards refill that stage (ra, rb, rs) with block kb_refill
-  // and read the first fragments of the next stage (na, nb, ns).
+  // registers; over its first rows it fills the stage (ra, rb, rs), which the
+  // block before consumed, with block kb_refill, and at its end it reads the
+  // first fragments of the next stage (na, nb, ns).
+  auto dma_row = [&](int i, uint8_t* ra, uint8_t* rb, float* rs, int kb_refill) __attribute__((always_inline)) {
+    static_for<DMA_ROWS>([&](auto r) __attribute__((always_inline)) {
+      if (i == decltype(r)::value) issue_row(r, ra, rb, rs, kb_refill);  // i is a constant once unrolled
+    });
+  };
   auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
                     int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns)
                     __attribute__((always_inline)) {
@@ -304,6 +331,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       for (int i = 0; i < S::TM; ++i) {
         const int cur = i & 1, prv = cur ^ 1;
         const uint32_t eac = __float_as_uint(ear) >> 23;
+        dma_row(i, ra, rb, rs, kb_refill);
         if (i + 1 < S::TM) {
           af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                              *(const u32x4*)(la + a_hi + (i + 1) * 2048));
@@ -326,14 +354,13 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       __syncthreads();
       read_first(na, nb, ns);
       __builtin_amdgcn_sched_barrier(0);
-      issue(ra, rb, rs, kb_refill);
-      __builtin_amdgcn_sched_barrier(0);
       return;
     }
     float scn = 0.f;  // activation scale of row i+1 (read during row i)
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
+      dma_row(i, ra, rb, rs, kb_refill);
       if (i + 1 < S::TM) {
         af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                            *(const u32x4*)(la + a_hi + (i + 1) * 2048));
@@ -367,7 +394,6 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     __syncthreads();
     read_first(na, nb, ns);
     __builtin_amdgcn_sched_barrier(0);
-    issue(ra, rb, rs, kb_refill);
     constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)
@@ -377,34 +403,37 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Stage s <- block kb0+s for every stage; stage 0 is waited for, the others
-  // stay in flight.  NS K blocks per trip so that every LDS buffer is a
-  // static object (the compiler then knows the stage being read and the
-  // stages being filled never alias and inserts no early wait); no branch
-  // inside a trip: block indices are clamped to the last block (re-loading it
-  // into an idle stage is harmless).  An empty K range (a trailing split)
-  // loads the last block and computes nothing.
+  // Stage s <- block kb0+s for s < NS-1; stage 0 is waited for, the others
+  // stay in flight.  The block in stage s is consumed by kblock(s), which
+  // meanwhile fills stage s-1 (consumed one block earlier; the barrier that
+  // ended that block has released it) with the block NS-1 ahead.  NS K
+  // blocks per trip so that every LDS buffer is a static object (the
+  // compiler then knows the stage being read and the stages being filled
+  // never alias and inserts no early wait); no branch inside a trip: block
+  // indices are clamped to the last block (re-loading it into an idle stage
+  // is harmless).  An empty K range (a trailing split) loads the last block
+  // and computes nothing.
   const int kblast = kb1 - 1;
-  static_for<NS>([&](auto st) __attribute__((always_inline)) {
+  static_for<NS - 1>([&](auto st) __attribute__((always_inline)) {
     issue(stage_a(st), stage_b(st), stage_s(st), min(kb0 + (int)decltype(st)::value, kblast));
   });
-  wait_vmcnt<(NS - 1) * PER>();
+  wait_vmcnt<(NS - 2) * PER>();
   __syncthreads();
   read_first(lds_a0, lds_b0, lds_s0);
   int kb = kb0;
   for (; kb + NS - 1 < kb1; kb += NS) {
     static_for<NS>([&](auto st) __attribute__((always_inline)) {
       constexpr int i = decltype(st)::value;
-      constexpr int nx = (i + 1) % NS;
-      kblock(stage_a(st), stage_s(st), stage_a(st), stage_b(st), stage_s(st), min(kb + i + NS, kblast),
-             stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+      constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
+      kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}),
+             min(kb + i + NS - 1, kblast), stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
     });
   }
   static_for<NS - 1>([&](auto st) __attribute__((always_inline)) {  // the remaining kb1 - kb < NS blocks
     constexpr int i = decltype(st)::value;
-    constexpr int nx = (i + 1) % NS;
+    constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
     if (kb + i < kb1)
-      kblock(stage_a(st), stage_s(st), stage_a(st), stage_b(st), stage_s(st), kblast,
+      kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}), kblast,
              stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
   });
   wait_vmcnt<0>();
