@@ -9,9 +9,10 @@
 //   * A workgroup owns a BM x BN output tile; its waves tile it as
 //     (BM/WM) x (BN/WN), each wave WM x WN = (WM/16) x (WN/16) 16x16 tiles.
 //   * Per 128-wide K block the fp8 tiles a[BM][128] and w[BN][128] and the
-//     activation scales sa[BM][kb] go HBM -> LDS with global_load_lds (the
-//     data never passes through VGPRs).  Two LDS stages: the loads of block
-//     kb+1 are in flight while the matrix cores work on block kb.
+//     activation scales sa[BM][kb] go HBM -> LDS with the buffer form of the
+//     direct-to-LDS load (the data never passes through VGPRs).  Two to four
+//     LDS stages: the loads of block kb+1 are in flight while the matrix
+//     cores work on block kb.
 //   * LDS rows are 128 bytes = eight 16-byte chunks; chunk c of row r is
 //     stored at c ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read
 //     (ds_read_b128; lane l: row l & 15, chunk 2 (l >> 4) [+1]) then puts
