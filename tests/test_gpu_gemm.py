@@ -265,3 +265,48 @@ def test_power_of_two_scale_mode_exact_cases():
     first = _run(qa, sa, qw, sw, fb.make_config(fb.STANDARD, 64, 128, 1))
     for cfg in _pow2_configs(N, K):
         assert np.array_equal(_run(qa, sa, qw, sw, cfg), first), str(cfg)
+
+
+def test_largest_operand_pitches():
+    # Row pitches just below 2^24 bytes (the largest accepted): a 256-row tile
+    # then spans almost 2^32 bytes, the range of the Standard kernel's 32-bit
+    # load offsets.  A and W live in 4 GiB buffers; the scale arrays get
+    # pitches just below 2^22 floats in a second pass.
+    import torch
+    M, N, K = 256, 256, 512
+    qa, sa, qw, sw = _random_operands(M, N, K, 9)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    big = (1 << 24) - 16
+    cfgs = [fb.make_config(fb.STANDARD, 256, 256), fb.make_config(fb.STANDARD, 128, 128, 2),
+            fb.make_config(fb.STANDARD, 64, 128, 1, 2, 4), fb.make_config(fb.STANDARD, 256, 128, 1, 1, 3)]
+    say("gemm largest pitches: A and W")
+    abuf = torch.zeros((M, big), dtype=torch.uint8, device=dev())
+    wbuf = torch.zeros((N, big), dtype=torch.uint8, device=dev())
+    abuf[:, :K] = to_dev(qa)
+    wbuf[:, :K] = to_dev(qw)
+    a, w = abuf[:, :K], wbuf[:, :K]
+    sad, swd = to_dev(sa), to_dev(sw)
+    for cfg in cfgs:
+        say("  ", cfg.as_dict())
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+        ws = torch.empty((fb.fp8_block_gemm_workspace_size(M, N, K, cfg) // 4 + 4,), dtype=torch.float32,
+                         device=dev())
+        fb.fp8_block_gemm(a, sad, w, swd, y, cfg, ws)
+        assert_close(host(y).astype(np.float64), ref, ("pitch A/W", cfg.as_dict()))
+    del abuf, wbuf, a, w
+    torch.cuda.empty_cache()
+    say("gemm largest pitches: scales")
+    sbig = (1 << 22) - 4
+    sabuf = torch.zeros((M, sbig), dtype=torch.float32, device=dev())
+    swbuf = torch.zeros((N // 128, sbig), dtype=torch.float32, device=dev())
+    sabuf[:, : K // 128] = sad
+    swbuf[:, : K // 128] = swd
+    for cfg in cfgs:
+        say("  ", cfg.as_dict())
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+        ws = torch.empty((fb.fp8_block_gemm_workspace_size(M, N, K, cfg) // 4 + 4,), dtype=torch.float32,
+                         device=dev())
+        fb.fp8_block_gemm(to_dev(qa), sabuf[:, : K // 128], to_dev(qw), swbuf[:, : K // 128], y, cfg, ws)
+        assert_close(host(y).astype(np.float64), ref, ("pitch scales", cfg.as_dict()))
+    del sabuf, swbuf
+    torch.cuda.empty_cache()
