@@ -310,3 +310,27 @@ def test_largest_operand_pitches():
         assert_close(host(y).astype(np.float64), ref, ("pitch scales", cfg.as_dict()))
     del sabuf, swbuf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kb", [1, 2, 3, 4, 5, 7, 9])
+def test_k_loop_depths_splits_and_stages(kb):
+    # The K loop consumes NS blocks per trip and fills each stage during the
+    # block after the one that consumed it; its tail handles the last
+    # kb mod NS blocks, and split-K can leave uneven or empty trailing
+    # splits.  Every depth 1..9 blocks against every stage count and split.
+    M, N, K = 70, 256, 128 * kb
+    qa, sa, qw, sw = _random_operands(M, N, K, 100 + kb)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    # power-of-two scale mode: the same operands with sa, sw rounded to 2^e
+    sa2 = np.exp2(np.round(np.log2(sa))).astype(np.float32)
+    sw2 = np.exp2(np.round(np.log2(sw))).astype(np.float32)
+    ref2 = oracle.block_gemm(qa, sa2, qw, sw2)
+    for (tm, tn, kw, stages) in ((64, 128, 1, 0), (64, 128, 1, 3), (64, 128, 1, 4), (64, 128, 2, 4),
+                                 (128, 128, 1, 3), (128, 128, 2, 3), (256, 256, 1, 0), (256, 128, 1, 3)):
+        for sk in (1, 2, 3, 4, 6):
+            if sk > kb:
+                continue
+            cfg = fb.make_config(fb.STANDARD, tm, tn, sk, kw, stages)
+            assert_close(_run(qa, sa, qw, sw, cfg), ref, ("fp32", kb, cfg.as_dict()))
+            cfg.scale_mode = fb.SCALES_POW2
+            assert_close(_run(qa, sa2, qw, sw2, cfg), ref2, ("pow2", kb, cfg.as_dict()))
