@@ -15,8 +15,9 @@
 //     wave in flight.
 //   - amax: packed u16 max of |bf16| bit patterns in registers, then a 4-step
 //     DPP reduction inside the row (no LDS, no barriers).
-//   - scale = max(amax, eps)/448 once per group (IEEE division), 1/scale once
-//     per group, and every element divided by the scale with a 3-instruction
+//   - scale = max(amax, eps)/448 once per group (the corrected product with
+//     RN(1/448), equal to IEEE division for eps >= 2^-80), 1/scale once per
+//     group, and every element divided by the scale with a 3-instruction
 //     correctly rounded division (Markstein) instead of a full IEEE divide.
 //   - clamp with v_med3 and encode two values per v_cvt_pk_fp8_f32; 8 bytes
 //     stored per lane.
