@@ -119,6 +119,17 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
   return (uint32_t)w;
 }
 
+// encode4 for quotients of the group rule: each is RN(x / s) with |x| <= amax
+// and s >= RN(amax / 448) (or the power-of-two ceiling), so |q| <= 448 (1 +
+// 2^-23) < 464, which gfx950's conversion rounds to 448 (0x7E): the clamp can
+// be left out.  (It turns values from 464 up into the NaN code; the
+// encoder for arbitrary values keeps the clamp.)
+__device__ __forceinline__ uint32_t encode4_q(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // 16x16x128 fp8 x fp8 -> fp32 matrix-core product (no block scaling).
 // Operand layout: lane l supplies row (l & 15) of its matrix and the 32
 // consecutive K bytes starting at 32 * (l >> 4).  Result: lane l holds

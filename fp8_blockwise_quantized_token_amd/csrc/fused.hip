@@ -62,9 +62,9 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float eps, bool ue8
   const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
   const Recip rc = recip_of_scale(sc);
   *sc_out = sc;
-  const uint32_t lo = encode4(div_by_scale_f32(y[0], sc, rc), div_by_scale_f32(y[1], sc, rc),
+  const uint32_t lo = encode4_q(div_by_scale_f32(y[0], sc, rc), div_by_scale_f32(y[1], sc, rc),
                               div_by_scale_f32(y[2], sc, rc), div_by_scale_f32(y[3], sc, rc));
-  const uint32_t hi = encode4(div_by_scale_f32(y[4], sc, rc), div_by_scale_f32(y[5], sc, rc),
+  const uint32_t hi = encode4_q(div_by_scale_f32(y[4], sc, rc), div_by_scale_f32(y[5], sc, rc),
                               div_by_scale_f32(y[6], sc, rc), div_by_scale_f32(y[7], sc, rc));
   return make_uint2(lo, hi);
 }
@@ -91,7 +91,7 @@ __device__ __forceinline__ u32x4 quant16(const float (&y)[16], float eps, bool u
   u32x4 c;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    c[k] = encode4(div_by_scale_f32(y[4 * k], sc, rc), div_by_scale_f32(y[4 * k + 1], sc, rc),
+    c[k] = encode4_q(div_by_scale_f32(y[4 * k], sc, rc), div_by_scale_f32(y[4 * k + 1], sc, rc),
                    div_by_scale_f32(y[4 * k + 2], sc, rc), div_by_scale_f32(y[4 * k + 3], sc, rc));
   return c;
 }

@@ -226,9 +226,9 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 w = xr[c];
-      op[2 * c] = (int)encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+      op[2 * c] = (int)encode4_q(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
                                div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
-      op[2 * c + 1] = (int)encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+      op[2 * c + 1] = (int)encode4_q(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
                                    div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
     }
   };
@@ -260,11 +260,11 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
     const float rc = 1.0f / s_own;
     uint32_t code[NW / 2 > 0 ? NW / 2 : 1];
     if (NW == 1) {
-      code[0] = encode4(div_by_scale(bf16_lo(wd[0]), s_own, rc), div_by_scale(bf16_hi(wd[0]), s_own, rc), 0.f, 0.f);
+      code[0] = encode4_q(div_by_scale(bf16_lo(wd[0]), s_own, rc), div_by_scale(bf16_hi(wd[0]), s_own, rc), 0.f, 0.f);
     } else {
 #pragma unroll
       for (int i = 0; i < NW / 2; ++i)
-        code[i] = encode4(div_by_scale(bf16_lo(wd[2 * i]), s_own, rc), div_by_scale(bf16_hi(wd[2 * i]), s_own, rc),
+        code[i] = encode4_q(div_by_scale(bf16_lo(wd[2 * i]), s_own, rc), div_by_scale(bf16_hi(wd[2 * i]), s_own, rc),
                           div_by_scale(bf16_lo(wd[2 * i + 1]), s_own, rc),
                           div_by_scale(bf16_hi(wd[2 * i + 1]), s_own, rc));
     }

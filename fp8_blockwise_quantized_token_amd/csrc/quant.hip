@@ -87,9 +87,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
       const float sc = scale_from_amax(amax, eps, UE8M0);
       const float rc = 1.0f / sc;
       const u32x4 w = v[u];
-      const uint32_t lo = encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+      const uint32_t lo = encode4_q(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
                                   div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
-      const uint32_t hi = encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+      const uint32_t hi = encode4_q(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
                                   div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
       if (valid[u]) {
         *(uint2*)(q + qo[u]) = make_uint2(lo, hi);
@@ -132,10 +132,10 @@ __global__ __launch_bounds__(256) void k_weight_block_quant(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint4 o;
-    o.x = encode4(v[4 * i].x / sc, v[4 * i].y / sc, v[4 * i].z / sc, v[4 * i].w / sc);
-    o.y = encode4(v[4 * i + 1].x / sc, v[4 * i + 1].y / sc, v[4 * i + 1].z / sc, v[4 * i + 1].w / sc);
-    o.z = encode4(v[4 * i + 2].x / sc, v[4 * i + 2].y / sc, v[4 * i + 2].z / sc, v[4 * i + 2].w / sc);
-    o.w = encode4(v[4 * i + 3].x / sc, v[4 * i + 3].y / sc, v[4 * i + 3].z / sc, v[4 * i + 3].w / sc);
+    o.x = encode4_q(v[4 * i].x / sc, v[4 * i].y / sc, v[4 * i].z / sc, v[4 * i].w / sc);
+    o.y = encode4_q(v[4 * i + 1].x / sc, v[4 * i + 1].y / sc, v[4 * i + 1].z / sc, v[4 * i + 1].w / sc);
+    o.z = encode4_q(v[4 * i + 2].x / sc, v[4 * i + 2].y / sc, v[4 * i + 2].z / sc, v[4 * i + 2].w / sc);
+    o.w = encode4_q(v[4 * i + 3].x / sc, v[4 * i + 3].y / sc, v[4 * i + 3].z / sc, v[4 * i + 3].w / sc);
     dst[i] = o;
   }
   if (t == 0) s[nb * lds + kb] = sc;
@@ -190,14 +190,14 @@ __global__ __launch_bounds__(NT) void k_row_quant(const uint8_t* __restrict__ x,
     if (idx >= nvec) continue;
     const u32x4 w = v[i];
     if (BF16) {
-      const uint32_t lo = encode4(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
+      const uint32_t lo = encode4_q(div_by_scale(bf16_lo(w.x), sc, rc), div_by_scale(bf16_hi(w.x), sc, rc),
                                   div_by_scale(bf16_lo(w.y), sc, rc), div_by_scale(bf16_hi(w.y), sc, rc));
-      const uint32_t hi = encode4(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
+      const uint32_t hi = encode4_q(div_by_scale(bf16_lo(w.z), sc, rc), div_by_scale(bf16_hi(w.z), sc, rc),
                                   div_by_scale(bf16_lo(w.w), sc, rc), div_by_scale(bf16_hi(w.w), sc, rc));
       *(uint2*)(dst + (int64_t)idx * EV) = make_uint2(lo, hi);
     } else {
       *(uint32_t*)(dst + (int64_t)idx * EV) =
-          encode4(__uint_as_float(w.x) / sc, __uint_as_float(w.y) / sc, __uint_as_float(w.z) / sc,
+          encode4_q(__uint_as_float(w.x) / sc, __uint_as_float(w.y) / sc, __uint_as_float(w.z) / sc,
                   __uint_as_float(w.w) / sc);
     }
   }
