@@ -229,3 +229,34 @@ def test_scale_output_formats(M, K):
             assert np.array_equal(got, want)
             padv = sh[:, M:] if mn else sh[:, G:]
             assert np.all(padv == (0x5A if e8m0 else -1.0)), "padding written"
+
+
+def test_largest_quotients_encode_to_448():
+    # Groups whose amax a has RN(a / 448) below a / 448, so that a / s lands
+    # just above 448: the quantizers convert without a clamp and must still
+    # give 0x7E / 0xFE there (the conversion maps everything below 464 to
+    # 448).  Group and per-token quantizers against the oracle.
+    sig = (np.arange(128, dtype=np.uint32) | np.uint32(0x3F80)) << 16        # bf16 values in [1, 2)
+    cand = np.concatenate([sig.view(np.float32) * np.float32(2.0 ** e) for e in (-7, 0, 6)])
+    s = (cand / np.float32(448)).astype(np.float32)
+    above = cand[s.astype(np.float64) * 448.0 < cand.astype(np.float64)]
+    assert above.size > 20
+    G = above.size
+    rows = np.zeros((G, 128), np.float32)
+    rows[:, 0], rows[:, 1] = above, -above
+    rows[:, 2:] = above[:, None] * np.linspace(-0.99, 0.99, 126, dtype=np.float32)[None, :]
+    bits = synth.to_bf16_bits(rows)
+    assert np.array_equal(synth.to_bf16_bits(above[:, None])[:, 0], bits[:, 0])   # amax exact in bf16
+    for ue8m0 in (False, True):
+        say("largest quotients", G, ue8m0)
+        q, sc = _gpu_group_quant(bits, ue8m0)
+        rq, rs = oracle.group_quant(bits, EPS, ue8m0)
+        assert np.array_equal(q, rq) and np.array_equal(sc, rs)
+        if not ue8m0:
+            assert np.all(q[:, 0] == 0x7E) and np.all(q[:, 1] == 0xFE)
+        import torch
+        qt = torch.empty((G, 128), dtype=torch.uint8, device=dev())
+        st = torch.empty((G,), dtype=torch.float32, device=dev())
+        fb.fp8_token_quant(to_dev_bf16(bits), qt, st, ue8m0=ue8m0)
+        tq, ts = oracle.token_quant(bits, ue8m0=ue8m0)
+        assert np.array_equal(host(qt), tq) and np.array_equal(host(st), ts)
