@@ -278,11 +278,12 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // factor sa[m][kb] * sw[nb][kb]) and the A fragment and activation scales
   // of row i+1 are read from LDS.  The products of two rows are live at a
   // time; the order (the next row's LDS reads, then 1 MFMA : 4 FMA) is
-  // requested from the scheduler per step.  The pipeline also runs across K
-  // blocks: once the last row's products are issued, the wave passes the
-  // stage barrier, refills the stage it has finished with (block kb+2),
-  // reads the next block's B fragments, first A fragment and scales, and
-  // folds the last row's products while those reads are in flight.
+  // requested from the scheduler per step.  The first rows also issue the
+  // direct-to-LDS loads that refill the stage the previous block consumed.
+  // The pipeline runs across K blocks: once the last row's products are
+  // issued, the wave passes the stage barrier, reads the next block's first
+  // A fragment, B fragments and scales, and folds the last row's products
+  // while those reads are in flight.
   static_assert(S::TM % 2 == 0, "row pipeline assumes an even number of tile rows");
   const int arow = wave_m * WM + frow;
   const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
@@ -314,15 +315,16 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       scl = ls[srow];
   };
 
-  // One K block from the stage (la, ls) whose first fragments are already in
-  // registers; over its first rows it fills the stage (ra, rb, rs), which the
-  // block before consumed, with block kb_refill, and at its end it reads the
-  // first fragments of the next stage (na, nb, ns).
+  // The loads due in tile row i (none past the first DMA_ROWS rows).
   auto dma_row = [&](int i, uint8_t* ra, uint8_t* rb, float* rs, int kb_refill) __attribute__((always_inline)) {
     static_for<DMA_ROWS>([&](auto r) __attribute__((always_inline)) {
       if (i == decltype(r)::value) issue_row(r, ra, rb, rs, kb_refill);  // i is a constant once unrolled
     });
   };
+  // One K block from the stage (la, ls) whose first fragments are already in
+  // registers; over its first rows it fills the stage (ra, rb, rs), which the
+  // block before consumed, with block kb_refill, and at its end it reads the
+  // first fragments of the next stage (na, nb, ns).
   auto kblock = [&](const uint8_t* la, const float* ls, uint8_t* ra, uint8_t* rb, float* rs,
                     int kb_refill, const uint8_t* na, const uint8_t* nb, const float* ns)
                     __attribute__((always_inline)) {
