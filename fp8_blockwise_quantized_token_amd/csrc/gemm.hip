@@ -358,8 +358,8 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
           *(float4*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
         else
           *(uint2*)(g.y + m * g.ldy + n) =
-              make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                         f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+              make_uint2(bf16x2_bits(v[0], v[1]),
+                         bf16x2_bits(v[2], v[3]));
       }
     }
   } else {
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
             *(float4*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
           else
             *(uint2*)(g.y + m * g.ldy + n) =
-                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+                make_uint2(bf16x2_bits(v[0], v[1]),
+                           bf16x2_bits(v[2], v[3]));
         }
       }
   }
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
       acc.z += v.z;
       acc.w += v.w;
     }
-    *(uint2*)(y + m * ldy + n) = make_uint2(f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16),
-                                            f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16));
+    *(uint2*)(y + m * ldy + n) = make_uint2(bf16x2_bits(acc.x, acc.y),
+                                            bf16x2_bits(acc.z, acc.w));
   }
 }
 

@@ -468,8 +468,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       if (SPLIT) {
         *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
       } else {
-        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        const uint32_t lo = bf16x2_bits(v[0], v[1]);
+        const uint32_t hi = bf16x2_bits(v[2], v[3]);
         *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
       }
     }

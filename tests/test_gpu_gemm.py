@@ -334,3 +334,46 @@ def test_k_loop_depths_splits_and_stages(kb):
             assert_close(_run(qa, sa, qw, sw, cfg), ref, ("fp32", kb, cfg.as_dict()))
             cfg.scale_mode = fb.SCALES_POW2
             assert_close(_run(qa, sa2, qw, sw2, cfg), ref2, ("pow2", kb, cfg.as_dict()))
+
+
+def test_bf16_output_rounding_ties_and_subnormals():
+    # y[m][n] = sa[m] exactly (one K block, a single 1.0 x 1.0 product per
+    # output, sw = 1), so the output bits are the bf16 rounding of sa[m]
+    # alone: ties go to the even neighbour, subnormals are kept.  Expected
+    # bits worked out by hand; every Standard tile and Swap-AB configuration.
+    targets = [
+        (1.0 + 2.0 ** -8, 0x3F80),                  # tie between 1 and 1 + 2^-7 -> even (1)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),              # tie between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),     # just above the tie -> up
+        (-(1.0 + 2.0 ** -8), 0xBF80),
+        (2.0 ** -130, 0x0008),                      # bf16 subnormal 8 * 2^-133
+        (1.5 * 2.0 ** -133, 0x0002),                # tie between 1 and 2 units of 2^-133 -> even (2)
+        (0.5 * 2.0 ** -133, 0x0000),                # tie between 0 and 2^-133 -> even (0)
+        (3.0, 0x4040),
+    ]
+    M, N, K = 16, 256, 128
+    sa = np.ones((M, 1), np.float32)
+    for i, (v, _) in enumerate(targets):
+        sa[i, 0] = np.float32(v)
+        assert float(sa[i, 0]) == v                 # exact in fp32
+    qa = np.zeros((M, K), np.uint8)
+    qa[:, 0] = 0x38                                 # e4m3 1.0
+    qw = np.zeros((N, K), np.uint8)
+    qw[:, 0] = 0x38
+    sw = np.ones((N // 128, 1), np.float32)
+    expect = np.full((M, N), 0x3F80, np.uint16)     # rows past the targets: sa = 1
+    for i, (_, bits) in enumerate(targets):
+        expect[i, :] = bits
+    cfgs = [fb.make_config(fb.STANDARD, tm, tn) for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256),
+                                                                (256, 256))]
+    cfgs += [fb.make_config(fb.STANDARD, 64, 128, 1, 2), fb.make_config(fb.STANDARD, 128, 128, 1, 2, 3)]
+    cfgs += [fb.make_config(fb.SWAPAB, tm, tn, 1, kw) for tm in (16, 32, 64) for tn in (16, 32, 64)
+             for kw in (1, 2) if not (tm == 64 and tn == 64)]
+    for cfg in cfgs:
+        say("bf16 rounding", cfg.as_dict())
+        import torch
+        y = fb.block_gemm(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), cfg)
+        got = host(y.view(torch.int16)).view(np.uint16)
+        if not np.array_equal(got, expect):
+            bad = np.argwhere(got != expect)[:4]
+            raise AssertionError((cfg.as_dict(), [(tuple(b), hex(got[tuple(b)]), hex(expect[tuple(b)])) for b in bad]))
