@@ -29,7 +29,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
 
-ABI_VERSION = 3  # FP8BLK_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4  # FP8BLK_ABI_VERSION of the header this binding follows
 GROUP = 128
 FLAG_UE8M0 = 1
 STANDARD = 0
@@ -46,13 +46,13 @@ class GemmConfig(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("kwaves", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("scale_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("scale_mode", ctypes.c_int32), ("split_tail", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"variant": "swapab" if self.variant == SWAPAB else "standard",
                 "tile_m": self.tile_m, "tile_n": self.tile_n,
                 "split_k": self.split_k, "kwaves": self.kwaves, "stages": self.stages,
-                "scale_mode": self.scale_mode}
+                "scale_mode": self.scale_mode, "split_tail": self.split_tail}
 
     def __repr__(self) -> str:
         return f"GemmConfig({self.as_dict()})"
@@ -63,10 +63,10 @@ SCALES_POW2 = 1
 
 
 def make_config(variant: int, tile_m: int, tile_n: int, split_k: int = 1, kwaves: int = 1,
-                stages: int = 0, scale_mode: int = SCALES_FP32) -> GemmConfig:
+                stages: int = 0, scale_mode: int = SCALES_FP32, split_tail: int = 0) -> GemmConfig:
     c = GemmConfig()
     c.variant, c.tile_m, c.tile_n, c.split_k, c.kwaves, c.stages = variant, tile_m, tile_n, split_k, kwaves, stages
-    c.scale_mode = scale_mode
+    c.scale_mode, c.split_tail = scale_mode, split_tail
     return c
 
 

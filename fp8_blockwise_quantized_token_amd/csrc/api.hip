@@ -24,7 +24,7 @@ int to_status(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HI
 
 int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   const int64_t kb = K / kG;
-  if (c.reserved[0] != 0) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.split_tail != 0 && (c.split_tail != 1 || c.variant != FP8BLK_STANDARD)) return FP8BLK_ERR_BAD_CONFIG;
   if (c.scale_mode != FP8BLK_SCALES_FP32 && c.scale_mode != FP8BLK_SCALES_POW2) return FP8BLK_ERR_BAD_CONFIG;
   if (c.scale_mode == FP8BLK_SCALES_POW2 && c.variant != FP8BLK_STANDARD) return FP8BLK_ERR_BAD_CONFIG;
   if (c.split_k < 1 || c.split_k > 256 || c.split_k > kb) return FP8BLK_ERR_BAD_CONFIG;
@@ -232,7 +232,7 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   g.ws = need > 0 ? (float*)workspace : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
-    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
                                                   c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
                                                                                        : fp8blk::kScalesBlock,
                                                   s));
@@ -314,7 +314,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   g.ldsa = K / kG;
   if (c.variant == FP8BLK_SWAPAB)
     return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
-  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
                                                 c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
                                                                                        : fp8blk::kScalesBlock,
                                                   s));
@@ -390,7 +390,7 @@ int fp8_scaled_mm(const uint8_t* a, const float* sa, int64_t lda, const uint8_t*
   g.ws = need > 0 ? (float*)workspace : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
-    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
                                                   fp8blk::kScalesChannel, s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s, true));
 }

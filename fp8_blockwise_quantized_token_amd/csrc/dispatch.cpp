@@ -22,8 +22,9 @@ struct Entry {
   fp8blk_gemm_config cfg;
 };
 
-#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, 0, 0, {0}}
-#define CFGS(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, 0, {0}}
+#define CFG(v, tm, tn, sk, kw) {v, tm, tn, sk, kw, 0, 0, 0}
+#define CFGS(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, 0, 0}
+#define CFGT(v, tm, tn, sk, kw, ns) {v, tm, tn, sk, kw, ns, 0, 1}  // split tail
 
 // Measured table (MI355X).  Entries are checked in order; the first bucket
 // containing M wins.
@@ -70,6 +71,16 @@ void heuristic(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* c) {
   while (tiles * split < kCUs && split * 2 * 4 <= kb && split < 256) split *= 2;
   c->split_k = (int32_t)split;
   c->kwaves = 1;
+  // Whole rounds of 256x256 tiles plus a partial round of at most half the
+  // CUs: split only that last round (one 256x256 workgroup per CU).
+  const int64_t tail = tiles % kCUs;
+  if (c->tile_m == 256 && c->tile_n == 256 && tiles > kCUs && tail <= kCUs / 2) {
+    const int64_t s = tail <= kCUs / 4 ? 4 : 2;
+    if (s * 2 <= kb) {
+      c->split_k = (int32_t)s;
+      c->split_tail = 1;
+    }
+  }
 }
 
 }  // namespace

@@ -35,7 +35,12 @@
 //     resident on one XCD share A and W slices in that XCD's L2.
 //   * Split-K: grid x split_k; split s covers a contiguous range of K blocks
 //     and writes fp32 partials to the workspace [split][M][N]; a separate
-//     kernel sums them in split order.
+//     kernel sums them in split order.  Split tail: when the tiles fill
+//     R >= 1 whole rounds of resident workgroups and leave a partial round,
+//     the tiles of the whole rounds run unsplit (bf16 out, no workspace)
+//     and only the remaining tiles are split, so the last round is filled
+//     with split_k times as many, shorter, workgroups; the sum then covers
+//     those tiles only.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -53,13 +58,30 @@ struct StdParams {
   GemmArgs g;
   int tiles_m, tiles_n;
   int kb_total, kb_per_split;
-  int remap;  // 1: XCD-contiguous remap (block count divisible by 8)
+  int tiles_dp;  // leading tiles (in walk order) computed unsplit; blocks [0, tiles_dp)
+  int tail;      // tiles after them, each split into split_k blocks
+  int remap_dp;  // 1: XCD-contiguous remap of the unsplit blocks (count divisible by 8)
+  int remap;     // 1: XCD-contiguous remap of the split blocks (count divisible by 8)
 };
 
 constexpr int kGroupM = 8;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit untyped data).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kXcds = 8;
+
+// Block b of a group of n blocks -> its tile slot, so that XCD x (blocks
+// are dealt round-robin to the 8 XCDs) takes slots [x n/8, (x+1) n/8).
+__device__ __forceinline__ int xcd_remap(int b, int n) { return (b % kXcds) * (n / kXcds) + b / kXcds; }
+
+// Tile t of the walk -> (tile row, tile column): column groups of kGroupM
+// tile-rows, column by column inside a group.
+__device__ __forceinline__ void walk_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group = kGroupM * tiles_n;
+  const int first_m = (t / group) * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m);
+  tm = first_m + (t % group) % gm;
+  tn = (t % group) / gm;
+}
 
 template <int BM, int BN, int WM, int WN>
 struct Shape {
@@ -166,24 +188,26 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const int wave_m = wave % S::WAVES_M;
   const int wave_n = wave / S::WAVES_M;
 
-  // ---- tile of this workgroup ----
-  const int tiles = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
-  if (p.remap) {
-    const int per_xcd = (int)(gridDim.x / kXcds);
-    bid = (bid % kXcds) * per_xcd + bid / kXcds;
+  // ---- tile of this workgroup: blocks [0, tiles_dp) take the leading tiles
+  // whole; the others take split (b / tail) of tile tiles_dp + b % tail ----
+  const bool whole = SPLIT && (int)blockIdx.x < p.tiles_dp;  // unsplit tile of a split launch
+  int t, split;
+  if (whole) {
+    t = p.remap_dp ? xcd_remap(blockIdx.x, p.tiles_dp) : (int)blockIdx.x;
+    split = 0;
+  } else {
+    const int nb = (int)gridDim.x - p.tiles_dp;
+    int b = (int)blockIdx.x - p.tiles_dp;
+    if (p.remap) b = xcd_remap(b, nb);
+    split = b / p.tail;
+    t = p.tiles_dp + (b - split * p.tail);
   }
-  const int split = bid / tiles;
-  const int t = bid - split * tiles;
-  const int group = kGroupM * p.tiles_n;
-  const int first_m = (t / group) * kGroupM;
-  const int gm = min(kGroupM, p.tiles_m - first_m);
-  const int tm = first_m + (t % group) % gm;
-  const int tn = (t % group) / gm;
+  int tm, tn;
+  walk_tile(t, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
-  const int kb0 = split * p.kb_per_split;
-  const int kb1 = min(kb0 + p.kb_per_split, p.kb_total);
+  const int kb0 = whole ? 0 : split * p.kb_per_split;
+  const int kb1 = whole ? p.kb_total : min(kb0 + p.kb_per_split, p.kb_total);
   const int64_t mlast = g.M - 1;
 
   // ---- direct-to-LDS sources: wave-uniform tile bases + 32-bit lane offsets
@@ -465,7 +489,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
       }
-      if (SPLIT) {
+      if (SPLIT && !whole) {
         *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
       } else {
         const uint32_t lo = bf16x2_bits(v[0], v[1]);
@@ -476,8 +500,52 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   }
 }
 
+// Sum of the split_k fp32 partials of the tail tiles (walk order tiles_dp
+// .. tiles_dp + gridDim.x / (BM / 16) - 1) -> bf16, in increasing split
+// order like the whole-output sum.  Workgroup: 16 rows of one tile.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void k_tail_reduce(const float* __restrict__ ws, int S, int64_t M, int64_t N,
+                                                     uint16_t* __restrict__ y, int64_t ldy, int tiles_m,
+                                                     int tiles_n, int tiles_dp) {
+  constexpr int CPR = BN / 4;          // threads per row (four columns each)
+  constexpr int RPP = 256 / CPR;       // rows per pass
+  const int u = (int)blockIdx.x / (BM / 16);
+  const int c = (int)blockIdx.x % (BM / 16);
+  int tm, tn;
+  walk_tile(tiles_dp + u, tiles_m, tiles_n, tm, tn);
+  const int64_t n = (int64_t)tn * BN + (threadIdx.x % CPR) * 4;
+#pragma unroll
+  for (int r = (int)threadIdx.x / CPR; r < 16; r += RPP) {
+    const int64_t m = (int64_t)tm * BM + c * 16 + r;
+    if (m >= M) break;
+    float4 acc = *(const float4*)(ws + m * N + n);
+    for (int s = 1; s < S; ++s) {
+      const float4 v = *(const float4*)(ws + ((int64_t)s * M + m) * N + n);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *(uint2*)(y + m * ldy + n) = make_uint2(bf16x2_bits(acc.x, acc.y), bf16x2_bits(acc.z, acc.w));
+  }
+}
+
+// Workgroups of one kernel resident at once on the current device (CUs x
+// workgroups per CU), cached per kernel and device.
+int resident_blocks(const void* kernel, int threads, int& cache_dev, int& cache_val) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (cache_val > 0 && cache_dev == dev) return cache_val;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  cache_dev = dev;
+  cache_val = cus * per_cu;
+  return cache_val;
+}
+
 template <int BM, int BN, int WM, int WN, int NS, int SM>
-hipError_t run_p(const GemmArgs& g, int split_k, hipStream_t stream) {
+hipError_t run_p(const GemmArgs& g, int split_k, bool split_tail, hipStream_t stream) {
   using S = Shape<BM, BN, WM, WN>;
   StdParams p;
   p.g = g;
@@ -485,20 +553,41 @@ hipError_t run_p(const GemmArgs& g, int split_k, hipStream_t stream) {
   p.tiles_n = (int)(g.N / BN);
   p.kb_total = (int)(g.K / 128);
   p.kb_per_split = (p.kb_total + split_k - 1) / split_k;
-  const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n * split_k;
-  p.remap = (blocks % kXcds == 0) ? 1 : 0;
-  if (split_k > 1)
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS, SM>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS, SM>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+  const int tiles = p.tiles_m * p.tiles_n;
+  p.tiles_dp = 0;
+  if (split_k > 1 && split_tail) {
+    static int cache_dev = -1, cache_val = 0;
+    const int slots = resident_blocks((const void*)k_gemm_lds<BM, BN, WM, WN, true, NS, SM>, S::NT, cache_dev,
+                                      cache_val);
+    if (slots <= 0) return hipErrorInvalidDevice;
+    p.tiles_dp = tiles / slots * slots;
+    if (p.tiles_dp == tiles) split_k = 1;  // whole rounds only: nothing to split
+  }
+  p.tail = tiles - p.tiles_dp;
+  p.remap_dp = (p.tiles_dp % kXcds == 0) ? 1 : 0;
+  const int64_t blocks = (int64_t)p.tiles_dp + (int64_t)p.tail * split_k;
+  p.remap = (split_k == 1 ? tiles : (int64_t)p.tail * split_k) % kXcds == 0 ? 1 : 0;
+  if (split_k == 1) {
+    p.tiles_dp = 0;
+    p.tail = tiles;
+    p.kb_per_split = p.kb_total;
+    hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, false, NS, SM>), dim3((unsigned)tiles), dim3(S::NT), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_gemm_lds<BM, BN, WM, WN, true, NS, SM>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.tiles_dp == 0) return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
+  hipLaunchKernelGGL((k_tail_reduce<BM, BN>), dim3((unsigned)(p.tail * (BM / 16))), dim3(256), 0, stream, g.ws,
+                     split_k, g.M, g.N, g.y, g.ldy, p.tiles_m, p.tiles_n, p.tiles_dp);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
-hipError_t run(const GemmArgs& g, int split_k, int sm, hipStream_t stream) {
-  if (sm == 1) return run_p<BM, BN, WM, WN, NS, 1>(g, split_k, stream);
-  if (sm == 2) return run_p<BM, BN, WM, WN, NS, 2>(g, split_k, stream);
-  return run_p<BM, BN, WM, WN, NS, 0>(g, split_k, stream);
+hipError_t run(const GemmArgs& g, int split_k, bool split_tail, int sm, hipStream_t stream) {
+  if (sm == 1) return run_p<BM, BN, WM, WN, NS, 1>(g, split_k, split_tail, stream);
+  if (sm == 2) return run_p<BM, BN, WM, WN, NS, 2>(g, split_k, split_tail, stream);
+  return run_p<BM, BN, WM, WN, NS, 0>(g, split_k, split_tail, stream);
 }
 
 }  // namespace
@@ -524,33 +613,32 @@ bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves) {
   return false;
 }
 
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages, int kwaves,
-                                int scale_mode, hipStream_t stream) {
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, bool split_tail, int stages,
+                                int kwaves, int scale_mode, hipStream_t stream) {
   const int sm = scale_mode;  // 0 block fp32, 1 block power-of-two, 2 per-token / per-channel
   const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
   if (kwaves == 2) {
     if (tile_m == 64 && tile_n == 128)
-      e = ns == 4 ? run<64, 128, 32, 32, 4>(g, split_k, sm, stream)
-        : ns == 3 ? run<64, 128, 32, 32, 3>(g, split_k, sm, stream)
-                  : run<64, 128, 32, 32, 2>(g, split_k, sm, stream);
+      e = ns == 4 ? run<64, 128, 32, 32, 4>(g, split_k, split_tail, sm, stream)
+        : ns == 3 ? run<64, 128, 32, 32, 3>(g, split_k, split_tail, sm, stream)
+                  : run<64, 128, 32, 32, 2>(g, split_k, split_tail, sm, stream);
     else if (tile_m == 128 && tile_n == 128)
-      e = ns == 3 ? run<128, 128, 64, 32, 3>(g, split_k, sm, stream) : run<128, 128, 64, 32, 2>(g, split_k, sm, stream);
+      e = ns == 3 ? run<128, 128, 64, 32, 3>(g, split_k, split_tail, sm, stream) : run<128, 128, 64, 32, 2>(g, split_k, split_tail, sm, stream);
   } else if (tile_m == 64 && tile_n == 128) {
-    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, sm, stream)
-      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, sm, stream)
-                : run<64, 128, 32, 64, 2>(g, split_k, sm, stream);
+    e = ns == 4 ? run<64, 128, 32, 64, 4>(g, split_k, split_tail, sm, stream)
+      : ns == 3 ? run<64, 128, 32, 64, 3>(g, split_k, split_tail, sm, stream)
+                : run<64, 128, 32, 64, 2>(g, split_k, split_tail, sm, stream);
   } else if (tile_m == 128 && tile_n == 128) {
-    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, sm, stream) : run<128, 128, 64, 64, 2>(g, split_k, sm, stream);
+    e = ns == 3 ? run<128, 128, 64, 64, 3>(g, split_k, split_tail, sm, stream) : run<128, 128, 64, 64, 2>(g, split_k, split_tail, sm, stream);
   } else if (tile_m == 256 && tile_n == 128) {
-    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, sm, stream) : run<256, 128, 64, 64, 2>(g, split_k, sm, stream);
+    e = ns == 3 ? run<256, 128, 64, 64, 3>(g, split_k, split_tail, sm, stream) : run<256, 128, 64, 64, 2>(g, split_k, split_tail, sm, stream);
   } else if (tile_m == 128 && tile_n == 256) {
-    e = run<128, 256, 64, 64, 2>(g, split_k, sm, stream);
+    e = run<128, 256, 64, 64, 2>(g, split_k, split_tail, sm, stream);
   } else if (tile_m == 256 && tile_n == 256) {
-    e = run<256, 256, 128, 64, 2>(g, split_k, sm, stream);
+    e = run<256, 256, 128, 64, 2>(g, split_k, split_tail, sm, stream);
   }
-  if (e != hipSuccess || split_k == 1) return e;
-  return launch_splitk_reduce(g.ws, split_k, g.M, g.N, g.y, g.ldy, stream);
+  return e;
 }
 
 }  // namespace fp8blk

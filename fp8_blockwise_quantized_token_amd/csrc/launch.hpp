@@ -63,8 +63,10 @@ struct GemmArgs {
 // matrix core), kScalesChannel (sa [M], sw [N]: per token / per channel).
 constexpr int kScalesBlock = 0, kScalesBlockPow2 = 1, kScalesChannel = 2;
 bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves);
-hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, int stages,
-                                int kwaves, int scale_mode, hipStream_t stream);
+// split_tail: split only the tiles past the last whole round of resident
+// workgroups (the reduction then covers those tiles only).
+hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int split_k, bool split_tail,
+                                int stages, int kwaves, int scale_mode, hipStream_t stream);
 
 // Swap-AB variant.
 bool swapab_tile_supported(int tile_m, int tile_n, int kwaves);

@@ -72,6 +72,13 @@ def candidates(M: int, N: int, K: int):
                 # twice the waves for grids of about one workgroup per CU
                 if (tm, tn) in ((64, 128), (128, 128)) and tiles * sk <= 1024:
                     out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 2, 0 if ns == 2 else ns))
+        # split tail: whole rounds unsplit, the partial last round split
+        # (rounds of 256 workgroups for the one-per-CU tiles, else 512)
+        rnd = 256 if tm * tn >= 256 * 128 else 512
+        if tiles > rnd and tiles % rnd:
+            for sk in (2, 3, 4, 6, 8):
+                if sk * 2 <= kb and (tiles % rnd) * sk <= 2 * rnd:
+                    out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, 0, split_tail=1))
     return out
 
 
@@ -186,7 +193,8 @@ def write_table(path: str, out_inc: str) -> None:
              "// by fp8_blockwise_quantized_token_amd/tune.py (HIP-graph replay, weights",
              f"// rotated past the Infinity Cache; timed call: {data.get('op', 'gemm')}).",
              "// Entry: {N, K, M_lo, M_hi,",
-             "// CFG(variant, tile_m, tile_n, split_k, kwaves) or CFGS(..., stages)};",
+             "// CFG(variant, tile_m, tile_n, split_k, kwaves), CFGS(..., stages) or",
+             "// CFGT(..., stages) (split tail)};",
              "// the first bucket containing M wins.",
              "static const Entry kTable[] = {"]
     for (N, K), ents in sorted(by_shape.items()):
@@ -199,7 +207,9 @@ def write_table(path: str, out_inc: str) -> None:
             if e is ents[-1]:
                 hi = 2147483647 if b["variant"] == "standard" else e["M"]
             ns = b.get("stages", 0)
-            cfg = (f"CFG({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']})" if ns == 0 else
+            cfg = (f"CFGT({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})"
+                   if b.get("split_tail", 0) else
+                   f"CFG({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']})" if ns == 0 else
                    f"CFGS({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})")
             lines.append(f"    {{{N}, {K}, {lo + 1}, {hi}, {cfg}}},  // {e['best_us']:.2f} us at M={e['M']}")
             lo = e["M"]

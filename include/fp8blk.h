@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 3
+#define FP8BLK_ABI_VERSION 4
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
 /* Smallest accepted eps (2^-80, about 8.3e-25).  With eps at least this,
@@ -111,7 +111,16 @@ extern "C" {
  *             tile_n (weight rows per workgroup) in {16, 32, 64},
  *             kwaves (waves sharing one tile, each on its own K range,
  *             summed in the workgroup) in {1, 2, 4, 8}; stages must be 0.
- *   split_k: 1 .. min(256, K/128). */
+ *   split_k: 1 .. min(256, K/128).
+ *   split_tail (STANDARD only; 0 or 1): 1 splits only the tiles that do not
+ *             fill a whole round of resident workgroups (CUs x workgroups
+ *             per CU on the current device; tiles are taken in the kernel's
+ *             walk order): the tiles of the whole rounds run over the full
+ *             K range and write bf16 directly, the remaining ones run as
+ *             split_k shorter workgroups each, so the last round is full.
+ *             With fewer tiles than one round this is plain Split-K; with
+ *             an exact number of rounds nothing is split.  The workspace
+ *             requirement is the same as for split_k alone. */
 typedef struct fp8blk_gemm_config {
     int32_t variant;
     int32_t tile_m;
@@ -120,7 +129,7 @@ typedef struct fp8blk_gemm_config {
     int32_t kwaves;
     int32_t stages;
     int32_t scale_mode;  /* FP8BLK_SCALES_FP32 or FP8BLK_SCALES_POW2 */
-    int32_t reserved[1]; /* must be 0 */
+    int32_t split_tail;  /* 0 or 1, see above */
 } fp8blk_gemm_config;
 
 /* Library ABI version (FP8BLK_ABI_VERSION of the build). */

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fb.fp8_abi_version() == fb.ABI_VERSION == 3
+    assert fb.fp8_abi_version() == fb.ABI_VERSION == 4
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert fb.fp8_status_string(st) != "unknown status"
     assert fb.fp8_status_string(-99) == "unknown status"
@@ -137,9 +137,10 @@ def test_gemm_argument_errors():
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_k=4)) == CFG  # K/128 = 2 blocks
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 3)) == CFG         # kwaves
     assert _gemm(M=40, cfg=fb.make_config(fb.SWAPAB, 32, 16, 1, 4)) == CFG   # M > tile_m
-    bad = fb.make_config(fb.STANDARD, 128, 128)
-    bad.reserved[0] = 5
-    assert _gemm(cfg=bad) == CFG
+    # split tail: 0 or 1, Standard only
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_tail=5)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_tail=-1)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, split_tail=1)) == CFG
     # scale modes: fp32 or power-of-two (Standard only)
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=2)) == CFG
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, scale_mode=fb.SCALES_POW2)) == CFG
@@ -202,6 +203,19 @@ def test_select_is_deterministic_and_swaps_small_m():
     # a shape no table holds still gets a valid configuration
     c = fb.fp8_block_gemm_select(777, 384, 1152)
     assert fb.fp8_block_gemm_workspace_size(777, 384, 1152, c) >= 0
+
+
+def test_select_splits_the_tail_round_of_untabled_shapes():
+    # N = 2560 is in no table: 256x256 tiles, 10 per tile row
+    for M, sk, tail in ((26 * 256, 4, 1), (30 * 256 - 100, 4, 1), (38 * 256, 2, 1), (40 * 256, 1, 0),
+                        (45 * 256, 1, 0)):
+        c = fb.fp8_block_gemm_select(M, 2560, 2560)
+        assert (c.tile_m, c.tile_n, c.split_k, c.split_tail) == (256, 256, sk, tail), (M, c.as_dict())
+        if tail:
+            assert fb.fp8_block_gemm_workspace_size(M, 2560, 2560, c) == sk * M * 2560 * 4
+    # too few K blocks to split: no tail split
+    c = fb.fp8_block_gemm_select(26 * 256, 2560, 384)
+    assert c.split_tail == 0 and c.split_k == 1
 
 
 def _lin(x=A, ldx=256, w=C, sw=D, ldw=256, ldsw=2, y=E, ldy=256, M=8, N=256, K=256, eps=1e-10,

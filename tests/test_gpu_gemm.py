@@ -377,3 +377,47 @@ def test_bf16_output_rounding_ties_and_subnormals():
         if not np.array_equal(got, expect):
             bad = np.argwhere(got != expect)[:4]
             raise AssertionError((cfg.as_dict(), [(tuple(b), hex(got[tuple(b)]), hex(expect[tuple(b)])) for b in bad]))
+
+
+def _walk(tiles_m, tiles_n):
+    """(tile row, tile column) of each tile in the Standard kernel's walk
+    order: column groups of 8 tile-rows, column by column inside a group."""
+    out = []
+    for t in range(tiles_m * tiles_n):
+        first = t // (8 * tiles_n) * 8
+        gm = min(8, tiles_m - first)
+        out.append((first + t % (8 * tiles_n) % gm, t % (8 * tiles_n) // gm))
+    return out
+
+
+@pytest.mark.parametrize("tm,tn,kw,ns", [(256, 256, 1, 0), (128, 256, 1, 0), (256, 128, 1, 3), (128, 128, 1, 0),
+                                         (128, 128, 2, 3), (64, 128, 1, 4)], ids=lambda v: str(v))
+def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw, ns):
+    """Split tail: the tiles of the whole rounds of resident workgroups run
+    unsplit, the rest split.  More tiles than any round (M = 4300, a ragged
+    last tile row), K = 640 (5 blocks: the splits are 3 + 2 and 2 + 2 + 1).
+    In the kernel's walk order, the tiles before some multiple d of the CU
+    count (d < tiles) must equal, bit for bit, the unsplit run's and the
+    tiles from d on the plain Split-K run's; both runs must differ from the
+    result somewhere; sampled rows match the oracle."""
+    import torch
+    M, N, K = 4300, 4096, 640
+    qa, sa, qw, sw = _random_operands(M, N, K, 31)
+    args = [to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw)]
+    walk = _walk(-(-M // tm), N // tn)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ref = oracle.block_gemm(qa, sa, qw, sw, rows=sample_rows(M, 8, 3))
+    for sk in (2, 3):
+        say("split tail", tm, tn, kw, ns, sk)
+        y1 = host(fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, 1, kw, ns)).view(torch.int16))
+        ys = host(fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns)).view(torch.int16))
+        yt_dev = fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns, split_tail=1))
+        yt = host(yt_dev.view(torch.int16))
+        tile = lambda a, r, c: a[r * tm:(r + 1) * tm, c * tn:(c + 1) * tn]
+        eq_u = np.array([np.array_equal(tile(yt, r, c), tile(y1, r, c)) for r, c in walk])
+        eq_s = np.array([np.array_equal(tile(yt, r, c), tile(ys, r, c)) for r, c in walk])
+        ok = [d for d in range(cus, len(walk), cus) if eq_u[:d].all() and eq_s[d:].all()]
+        assert ok, (tm, tn, sk, np.flatnonzero(~eq_u)[:8], np.flatnonzero(~eq_s)[:8])
+        assert not eq_u.all() and not eq_s.all(), (tm, tn, sk)
+        rows = sample_rows(M, 8, 3)
+        assert_close(host(yt_dev)[rows].astype(np.float64), ref, f"split tail {tm}x{tn} sk{sk}")
