@@ -337,7 +337,8 @@ def main() -> int:
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
         bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, lws=lws, qw=qw, sw=sw,
-                         fused=cfg.variant == fb.SWAPAB and cfg.tile_m <= 32 and not dynamic))
+                         fused=cfg.variant == fb.SWAPAB and not dynamic
+                         and (cfg.tile_m <= 32 or (cfg.tile_m == 64 and cfg.tile_n == 16))))
     torch.cuda.synchronize()
 
     def quant(b):

@@ -59,8 +59,10 @@ int64_t workspace_for(const fp8blk_gemm_config& c, int64_t M, int64_t N) {
 
 int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 
-// fp8_linear's workspace: Swap-AB with up to two token tiles (tile_m <= 32)
-// quantizes in the GEMM and needs only the split-K partials; the other
+// fp8_linear's workspace: Swap-AB with up to two token tiles (tile_m <= 32),
+// or four with 16 weight rows per workgroup (tile_m 64, tile_n 16; wider
+// tiles would not fit the raw activations in registers), quantizes in the
+// GEMM and needs only the split-K partials; the other
 // configurations first quantize into the workspace:
 // [q: M x K bytes][s: M x K/128 floats][split-K partials], each 256-aligned.
 struct LinearLayout {
@@ -70,7 +72,7 @@ struct LinearLayout {
 
 LinearLayout linear_layout(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   LinearLayout L;
-  L.fused = c.variant == FP8BLK_SWAPAB && c.tile_m <= 32;
+  L.fused = c.variant == FP8BLK_SWAPAB && (c.tile_m <= 32 || (c.tile_m == 64 && c.tile_n == 16));
   const int64_t split = workspace_for(c, M, N);
   if (L.fused) {
     L.q_off = L.s_off = L.ws_off = 0;

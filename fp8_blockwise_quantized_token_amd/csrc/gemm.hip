@@ -434,10 +434,12 @@ hipError_t run_swap(const GemmArgs& g, int kwaves, int split_k, bool ch, hipStre
     if (g.M <= 4) return run_swap3<TOKT, RN, 4>(p, grid, kwaves, sp, stream);
     if (g.M <= 8) return run_swap3<TOKT, RN, 8>(p, grid, kwaves, sp, stream);
     return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
-  } else if constexpr (TOKT == 2) {
+  } else if constexpr (TOKT == 2 || RN == 1) {
     return run_swap3<TOKT, RN, 16>(p, grid, kwaves, sp, stream);
   }
-  return hipErrorInvalidValue;  // the fused path serves up to two token tiles (M <= 32)
+  // four token tiles fuse only with 16 weight rows per workgroup: with more,
+  // the raw activations and the weight fragments exceed the registers
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

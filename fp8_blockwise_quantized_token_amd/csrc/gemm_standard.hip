@@ -41,6 +41,7 @@
 //     and only the remaining tiles are split, so the last round is filled
 //     with split_k times as many, shorter, workgroups; the sum then covers
 //     those tiles only.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -531,17 +532,19 @@ __global__ __launch_bounds__(256) void k_tail_reduce(const float* __restrict__ w
 }
 
 // Workgroups of one kernel resident at once on the current device (CUs x
-// workgroups per CU), cached per kernel and device.
-int resident_blocks(const void* kernel, int threads, int& cache_dev, int& cache_val) {
+// workgroups per CU).  Cached per kernel for the last device asked about, as
+// (device << 32) | count in one atomic word.
+int resident_blocks(const void* kernel, int threads, std::atomic<uint64_t>& cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (cache_val > 0 && cache_dev == dev) return cache_val;
+  const uint64_t c = cache.load(std::memory_order_relaxed);
+  if (c != 0 && (int)(c >> 32) == dev) return (int)(uint32_t)c;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
-  cache_dev = dev;
-  cache_val = cus * per_cu;
-  return cache_val;
+  const int n = cus * per_cu;
+  if (n > 0) cache.store(((uint64_t)(uint32_t)dev << 32) | (uint32_t)n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int SM>
@@ -556,9 +559,8 @@ hipError_t run_p(const GemmArgs& g, int split_k, bool split_tail, hipStream_t st
   const int tiles = p.tiles_m * p.tiles_n;
   p.tiles_dp = 0;
   if (split_k > 1 && split_tail) {
-    static int cache_dev = -1, cache_val = 0;
-    const int slots = resident_blocks((const void*)k_gemm_lds<BM, BN, WM, WN, true, NS, SM>, S::NT, cache_dev,
-                                      cache_val);
+    static std::atomic<uint64_t> cache{0};
+    const int slots = resident_blocks((const void*)k_gemm_lds<BM, BN, WM, WN, true, NS, SM>, S::NT, cache);
     if (slots <= 0) return hipErrorInvalidDevice;
     p.tiles_dp = tiles / slots * slots;
     if (p.tiles_dp == tiles) split_k = 1;  // whole rounds only: nothing to split

@@ -236,10 +236,10 @@ int fp8_block_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
  * CustomOps", the SM120 benchmark comment), and the pages count kernel
  * launches per forward pass as the cost fusion cuts (page "Helion-Kernel in
  * vLLM", section "Welche Kernel wurden in vLLM integriert").
- *   SWAPAB configurations with tile_m <= 32 (M <= 32, the small-M choices
- *   of the dispatcher) quantize each 1x128 group of x inside the GEMM's
- *   operand load: one kernel (plus the split-K sum), and no fp8 copy of x is
- *   written.  Codes and scales are the ones fp8_group_quant would produce,
+ *   SWAPAB configurations with tile_m <= 32, or tile_m 64 with tile_n 16
+ *   (M <= 64, the small-M choices of the dispatcher), quantize each 1x128
+ *   group of x inside the GEMM's operand load: one kernel (plus the split-K
+ *   sum), and no fp8 copy of x is written.  Codes and scales are the ones fp8_group_quant would produce,
  *   bit for bit.  Other configurations run fp8_group_quant into the
  *   workspace, then the GEMM.
  *   x  bf16 [M][ldx], ldx >= K            w, sw, y, ldw, ldsw, ldy as in

@@ -249,9 +249,11 @@ def test_linear_argument_errors():
     assert _lin(M=40, cfg=sw1) == CFG  # Swap-AB tile_m < M
     # Swap-AB with one token tile quantizes in the GEMM: workspace only for split-K partials
     assert fb.fp8_linear_workspace_size(8, 256, 256, sw1) == 0
-    # four token tiles quantize first: q [M][K] and s [M][K/128], each padded to 256 bytes
+    # two token tiles, and four with 16 weight rows, quantize in the GEMM too
     assert fb.fp8_linear_workspace_size(20, 256, 256, fb.make_config(fb.SWAPAB, 32, 16, 1, 2)) == 0
-    assert fb.fp8_linear_workspace_size(40, 256, 256, fb.make_config(fb.SWAPAB, 64, 16, 1, 2)) == 40 * 256 + 512
+    assert fb.fp8_linear_workspace_size(40, 256, 256, fb.make_config(fb.SWAPAB, 64, 16, 1, 2)) == 0
+    # four token tiles with 32 weight rows quantize first: q [M][K] and s [M][K/128], each padded to 256 bytes
+    assert fb.fp8_linear_workspace_size(40, 256, 256, fb.make_config(fb.SWAPAB, 64, 32, 1, 2)) == 40 * 256 + 512
     sk = fb.make_config(fb.SWAPAB, 16, 16, 2, 1)
     assert fb.fp8_linear_workspace_size(8, 256, 256, sk) == 2 * 8 * 256 * 4
     assert _lin(cfg=sk) == WS

@@ -71,7 +71,7 @@ def test_every_config_equals_separate_quant_and_gemm(M, N, K):
 def test_ue8m0_and_distributions():
     N, K = 512, 768
     qw, sw = oracle_weight(N, K, True)
-    for M in (3, 12, 24, 40):  # lean fused, full fused (1 and 2 token tiles), separate quantizer
+    for M in (3, 12, 24, 40):  # lean fused, full fused (1, 2 and 4 token tiles; tile_n 32 at M = 40: separate)
         tm = 16 if M <= 16 else (32 if M <= 32 else 64)
         for dist in ("normal", "normal_outlier", "student_t3"):
             x = _x(M, K, dist, key=3)
