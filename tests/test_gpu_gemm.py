@@ -214,6 +214,33 @@ def test_hip_graph_replay_matches_eager():
         assert np.array_equal(host(y), eager), f"replay {i}"
 
 
+def test_hip_graph_replay_of_split_tail():
+    """A split-tail launch (unsplit tiles, split tail tiles, the tail sum)
+    captured in a graph: every replay equals the eager result."""
+    import torch
+    M, N, K = 4300, 4096, 640
+    qa, sa, qw, sw = (to_dev(a) for a in _random_operands(M, N, K, 32))
+    cfg = fb.make_config(fb.STANDARD, 256, 256, 2, split_tail=1)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    ws = fb.workspace_for(M, N, K, cfg, dev())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fb.fp8_block_gemm(qa, sa, qw, sw, y, cfg, ws, stream=s)
+    s.synchronize()
+    eager = host(y.view(torch.int16)).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fb.fp8_block_gemm(qa, sa, qw, sw, y, cfg, ws, stream=s)
+    for i in range(3):
+        y.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        say("split tail graph replay", i)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y.view(torch.int16)), eager), f"replay {i}"
+
+
 def _pow2_configs(N, K):
     kb = K // 128
     out = []
