@@ -417,9 +417,14 @@ def _walk(tiles_m, tiles_n):
     return out
 
 
-@pytest.mark.parametrize("tm,tn,kw,ns", [(256, 256, 1, 0), (128, 256, 1, 0), (256, 128, 1, 3), (128, 128, 1, 0),
-                                         (128, 128, 2, 3), (64, 128, 1, 4)], ids=lambda v: str(v))
-def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw, ns):
+_TAIL_CASES = [(256, 256, 1, 0, "block"), (128, 256, 1, 0, "block"), (256, 128, 1, 3, "block"),
+               (128, 128, 1, 0, "block"), (128, 128, 2, 3, "block"), (64, 128, 1, 4, "block"),
+               (256, 256, 1, 0, "pow2"), (128, 128, 2, 0, "pow2"), (256, 256, 1, 0, "dynamic"),
+               (64, 128, 2, 3, "dynamic")]
+
+
+@pytest.mark.parametrize("tm,tn,kw,ns,mode", _TAIL_CASES, ids=lambda v: str(v))
+def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw, ns, mode):
     """Split tail: the tiles of the whole rounds of resident workgroups run
     unsplit, the rest split.  More tiles than any round (M = 4300, a ragged
     last tile row), K = 640 (5 blocks: the splits are 3 + 2 and 2 + 2 + 1).
@@ -430,15 +435,25 @@ def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw
     import torch
     M, N, K = 4300, 4096, 640
     qa, sa, qw, sw = _random_operands(M, N, K, 31)
+    rows = sample_rows(M, 8, 3)
+    if mode == "pow2":      # every scale a power of two, applied by the matrix core
+        sa, sw = (np.exp2(np.round(np.log2(v))).astype(np.float32) for v in (sa, sw))
+    if mode == "dynamic":   # per-token / per-channel scales (scaled_mm)
+        sa, sw = np.ascontiguousarray(sa[:, 0]), np.repeat(sw[:, 0], 128).astype(np.float32)
+        ref = oracle.scaled_mm(qa, sa, qw, sw, rows=rows)
+        run = fb.scaled_mm
+    else:
+        ref = oracle.block_gemm(qa, sa, qw, sw, rows=rows)
+        run = fb.block_gemm
+    sm = fb.SCALES_POW2 if mode == "pow2" else fb.SCALES_FP32
     args = [to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw)]
     walk = _walk(-(-M // tm), N // tn)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    ref = oracle.block_gemm(qa, sa, qw, sw, rows=sample_rows(M, 8, 3))
     for sk in (2, 3):
-        say("split tail", tm, tn, kw, ns, sk)
-        y1 = host(fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, 1, kw, ns)).view(torch.int16))
-        ys = host(fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns)).view(torch.int16))
-        yt_dev = fb.block_gemm(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns, split_tail=1))
+        say("split tail", tm, tn, kw, ns, mode, sk)
+        y1 = host(run(*args, fb.make_config(fb.STANDARD, tm, tn, 1, kw, ns, sm)).view(torch.int16))
+        ys = host(run(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns, sm)).view(torch.int16))
+        yt_dev = run(*args, fb.make_config(fb.STANDARD, tm, tn, sk, kw, ns, sm, split_tail=1))
         yt = host(yt_dev.view(torch.int16))
         tile = lambda a, r, c: a[r * tm:(r + 1) * tm, c * tn:(c + 1) * tn]
         eq_u = np.array([np.array_equal(tile(yt, r, c), tile(y1, r, c)) for r, c in walk])
@@ -446,5 +461,4 @@ def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw
         ok = [d for d in range(cus, len(walk), cus) if eq_u[:d].all() and eq_s[d:].all()]
         assert ok, (tm, tn, sk, np.flatnonzero(~eq_u)[:8], np.flatnonzero(~eq_s)[:8])
         assert not eq_u.all() and not eq_s.all(), (tm, tn, sk)
-        rows = sample_rows(M, 8, 3)
-        assert_close(host(yt_dev)[rows].astype(np.float64), ref, f"split tail {tm}x{tn} sk{sk}")
+        assert_close(host(yt_dev)[rows].astype(np.float64), ref, f"split tail {tm}x{tn} {mode} sk{sk}")
