@@ -62,14 +62,20 @@ def quant_bytes(c, dynamic: bool = False) -> int:
     return 2 * c.M * c.K + c.M * c.K + (4 * c.M if dynamic else 4 * c.M * c.K // 128)
 
 
-def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False) -> str:
+def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False, N: int = 0) -> str:
     """Name of the GEMM kernel a configuration launches, as rocprofv3 prints it."""
     b = lambda v: "true" if v else "false"
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
         wn = 32 if cfg.kwaves == 2 else 64
         sm = 2 if channel else cfg.scale_mode
-        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, {wn}, {b(cfg.split_k > 1)}, {cfg.stages or 2}, {sm}>"
+        split = cfg.split_k > 1
+        if split and cfg.split_tail and N:
+            # whole rounds only: the launcher runs the unsplit kernel (rounds of
+            # 256 CUs x workgroups per CU, one per CU for the largest tiles)
+            per_cu = 1 if cfg.tile_m * cfg.tile_n >= 256 * 128 else 2
+            split = (-(-M // cfg.tile_m) * (N // cfg.tile_n)) % (256 * per_cu) != 0
+        return f"k_gemm_lds<{cfg.tile_m}, {cfg.tile_n}, {wm}, {wn}, {b(split)}, {cfg.stages or 2}, {sm}>"
     fq = 0
     if fused:  # the fused quantizer variant the launcher picks for this M
         fq = 16 if cfg.tile_m > 16 or M > 8 else (1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8)
@@ -428,7 +434,7 @@ def main() -> int:
         fl = c.flops()
         gb = gemm_bytes(c, dynamic) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
         lb = gemm_bytes(c, dynamic) + quant_bytes(c, dynamic) if not b["fused"] else gb
-        sym = kernel_symbol(b["cfg"], b["fused"], c.M, dynamic)
+        sym = kernel_symbol(b["cfg"], b["fused"], c.M, dynamic, c.N)
         sym_time[sym] = sym_time.get(sym, 0.0) + tg
         w = sym_work.setdefault(sym, [0.0, 0.0, 0, 0])
         w[0] += fl
