@@ -25,8 +25,10 @@
  *     start at k = 0 and n = 0.
  *   - The caller owns every buffer.  The library never allocates device or
  *     host memory, never synchronizes, never reads device memory on the host
- *     and keeps no mutable global state: calls are thread-safe and can be
- *     captured into a HIP graph.  Work is ordered on the given stream
+ *     and keeps no mutable global state besides caches of device properties
+ *     (how many workgroups of a kernel fit the device at once, queried from
+ *     the runtime on first use; not stream operations): calls are
+ *     thread-safe and can be captured into a HIP graph.  Work is ordered on the given stream
  *     (a hipStream_t passed as void*; NULL is the default stream).
  *   - Outputs are fully overwritten; inputs are never modified.
  *   - Invalid arguments return a negative status before anything is
