@@ -8,12 +8,16 @@
 // shapes the table does not hold (the pages fall back to a default config
 // rather than failing when no tuned config exists).  Lookup is O(1) and
 // deterministic; nothing is tuned at run time.
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/fp8blk.h"
 #include "dispatch.hpp"
 
 namespace fp8blk {
+
+bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves);  // gemm_standard.hip
+
 namespace {
 
 struct Entry {
@@ -31,6 +35,9 @@ struct Entry {
 #include "dispatch_table.inc"
 
 constexpr int kCUs = 256;
+// Beyond this distance (a factor of about 4.5 in N times K) the nearest
+// tabled shape says little and the heuristic decides.
+constexpr double kMaxShapeDistance = 1.5;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -74,13 +81,42 @@ void heuristic(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* c) {
   // Whole rounds of 256x256 tiles plus a partial round of at most half the
   // CUs: split only that last round (one 256x256 workgroup per CU).
   const int64_t tail = tiles % kCUs;
-  if (c->tile_m == 256 && c->tile_n == 256 && tiles > kCUs && tail <= kCUs / 2) {
+  if (c->tile_m == 256 && c->tile_n == 256 && tiles > kCUs && tail > 0 && tail <= kCUs / 2) {
     const int64_t s = tail <= kCUs / 4 ? 4 : 2;
     if (s * 2 <= kb) {
       c->split_k = (int32_t)s;
       c->split_tail = 1;
     }
   }
+}
+
+// A tabled configuration is usable for another (M, N, K) when its tile
+// divides N, its split fits K and its Swap-AB token tile holds M.
+bool usable(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
+  const int64_t kb = K / 128;
+  if (c.split_k > kb) return false;
+  if (c.variant == FP8BLK_SWAPAB) return M <= c.tile_m;
+  return N % c.tile_n == 0 && standard_tile_supported(c.tile_m, c.tile_n, c.stages, c.kwaves == 0 ? 1 : c.kwaves);
+}
+
+// Nearest tabled weight shape: the entry whose M bucket holds M and whose
+// (N, K) is closest in |ln(N/n)| + |ln(K/k)| among the usable ones (first
+// in table order on ties).  Layers of other models of similar size get the
+// configuration measured for their neighbour instead of the heuristic's.
+bool nearest(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* out) {
+  double best = 1e30;
+  const Entry* pick = nullptr;
+  for (const Entry& e : kTable) {
+    if (M < e.m_lo || M > e.m_hi || !usable(e.cfg, M, N, K)) continue;
+    const double d = fabs(log((double)N / e.n)) + fabs(log((double)K / e.k));
+    if (d < best) {
+      best = d;
+      pick = &e;
+    }
+  }
+  if (pick == nullptr || best > kMaxShapeDistance) return false;
+  *out = pick->cfg;
+  return true;
 }
 
 }  // namespace
@@ -94,6 +130,7 @@ void select_config(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8blk_gemm_
       break;
     }
   }
+  if (!found) found = nearest(M, N, K, out);
   if (!found) heuristic(M, N, K, out);
   // UE8M0 scales are powers of two: the Standard kernels apply them in the
   // matrix core (v_mfma_scale) instead of one VALU rescale per K block.

@@ -133,7 +133,8 @@ def run_sweep(args) -> dict:
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
-    shapes = shape_sets(args.shapes)
+    shapes = ([tuple(int(v) for v in nk.split("x")) for nk in args.nk.split(",")] if args.nk
+              else shape_sets(args.shapes))
     ms = [int(m) for m in args.ms.split(",")] if args.ms else M_VALUES
     results = {"device": torch.cuda.get_device_name(0), "op": args.op, "entries": []}
     ws_pool = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)  # 1 GiB split-K workspace pool
@@ -161,13 +162,17 @@ def run_sweep(args) -> dict:
             flops = 2.0 * M * N * K
             reps = int(min(50, max(4, 2e-3 / max(flops / 2.0e15, wbytes / 6.0e12))))
             timings = []
-            for cfg in candidates(M, N, K):
+            dsel = fb.fp8_block_gemm_select(M, N, K)
+            disp = dsel.as_dict()
+            cands = candidates(M, N, K)
+            if all(c.as_dict() != disp for c in cands):
+                cands.append(dsel)  # the current choice is always timed
+            for cfg in cands:
                 if workspace_bytes(fb, args.op, M, N, K, cfg) > ws_pool.numel():
                     continue
                 us = time_config(fb, torch, bufs, cfg, reps, args.op)
                 timings.append((us, cfg.as_dict()))
             timings.sort(key=lambda t: t[0])
-            disp = fb.fp8_block_gemm_select(M, N, K).as_dict()
             disp_us = next((t for t, c in timings if c == disp), None)
             best_us, best = timings[0]
             results["entries"].append({"M": M, "N": N, "K": K, "best": best, "best_us": best_us,
@@ -222,6 +227,7 @@ def write_table(path: str, out_inc: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--shapes", default="all", help="all or a comma list of 1.7b,8b,32b")
+    ap.add_argument("--nk", default="", help="weight shapes NxK, comma separated (instead of --shapes)")
     ap.add_argument("--ms", default="", help="comma list of M values (default: the standard set)")
     ap.add_argument("--out", default="tune.json")
     ap.add_argument("--op", choices=("linear", "gemm"), default="linear")

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import fp8_blockwise_quantized_token_amd as fb
@@ -206,16 +207,37 @@ def test_select_is_deterministic_and_swaps_small_m():
 
 
 def test_select_splits_the_tail_round_of_untabled_shapes():
-    # N = 2560 is in no table: 256x256 tiles, 10 per tile row
-    for M, sk, tail in ((26 * 256, 4, 1), (30 * 256 - 100, 4, 1), (38 * 256, 2, 1), (40 * 256, 1, 0),
-                        (45 * 256, 1, 0)):
-        c = fb.fp8_block_gemm_select(M, 2560, 2560)
+    # N = 512, K = 1024 is far from every tabled shape (the heuristic decides):
+    # 256x256 tiles, 2 per tile row
+    for M, sk, tail in ((130 * 256, 4, 1), (150 * 256 - 100, 4, 1), (190 * 256, 2, 1), (200 * 256, 1, 0),
+                        (256 * 256, 1, 0)):  # the last: whole rounds only
+        c = fb.fp8_block_gemm_select(M, 512, 1024)
         assert (c.tile_m, c.tile_n, c.split_k, c.split_tail) == (256, 256, sk, tail), (M, c.as_dict())
         if tail:
-            assert fb.fp8_block_gemm_workspace_size(M, 2560, 2560, c) == sk * M * 2560 * 4
+            assert fb.fp8_block_gemm_workspace_size(M, 512, 1024, c) == sk * M * 512 * 4
     # too few K blocks to split: no tail split
-    c = fb.fp8_block_gemm_select(26 * 256, 2560, 384)
+    c = fb.fp8_block_gemm_select(130 * 256, 512, 384)
     assert c.split_tail == 0 and c.split_k == 1
+
+
+def test_select_takes_the_nearest_tabled_shape():
+    # Llama-like layers next to tabled Qwen3 ones get their neighbour's configuration
+    for (n, k), (tn, tk) in (((28672, 4096), (24576, 4096)), ((4096, 14336), (4096, 12288)),
+                             ((57344, 8192), (51200, 5120)), ((8192, 28672), (5120, 25600))):
+        for M in (1, 8, 32, 64, 256, 1024, 8192):
+            a = fb.fp8_block_gemm_select(M, n, k).as_dict()
+            b = fb.fp8_block_gemm_select(M, tn, tk).as_dict()
+            assert a == b, (M, n, k, a, b)
+
+
+def test_selected_configs_are_valid_for_any_shape():
+    rng = np.random.default_rng(5)
+    for _ in range(3000):
+        M = int(rng.integers(1, 20000))
+        N = 128 * int(rng.integers(1, 600))
+        K = 128 * int(rng.integers(1, 300))
+        c = fb.fp8_block_gemm_select(M, N, K)
+        assert fb.fp8_block_gemm_workspace_size(M, N, K, c) >= 0, (M, N, K, c.as_dict())
 
 
 def _lin(x=A, ldx=256, w=C, sw=D, ldw=256, ldsw=2, y=E, ldy=256, M=8, N=256, K=256, eps=1e-10,
