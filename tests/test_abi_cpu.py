@@ -236,8 +236,10 @@ def test_selected_configs_are_valid_for_any_shape():
         M = int(rng.integers(1, 20000))
         N = 128 * int(rng.integers(1, 600))
         K = 128 * int(rng.integers(1, 300))
-        c = fb.fp8_block_gemm_select(M, N, K)
-        assert fb.fp8_block_gemm_workspace_size(M, N, K, c) >= 0, (M, N, K, c.as_dict())
+        for flags in (0, fb.FLAG_UE8M0):
+            c = fb.fp8_block_gemm_select(M, N, K, flags)
+            assert fb.fp8_block_gemm_workspace_size(M, N, K, c) >= 0, (M, N, K, flags, c.as_dict())
+            assert fb.fp8_linear_workspace_size(M, N, K, c) >= 0, (M, N, K, flags, c.as_dict())
 
 
 def _lin(x=A, ldx=256, w=C, sw=D, ldw=256, ldsw=2, y=E, ldy=256, M=8, N=256, K=256, eps=1e-10,
