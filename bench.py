@@ -338,7 +338,7 @@ def main() -> int:
         qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
         sa = torch.empty((c.M,) if dynamic else (c.M, c.K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
-        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, fb.FLAG_UE8M0 if c.ue8m0 else 0)
+        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, (fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2) if c.ue8m0 else 0)
         ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
@@ -365,7 +365,7 @@ def main() -> int:
             gemm(b)
         else:
             fb.fp8_linear(b["x"], b["qw"], b["sw"], b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
-                          workspace=b["lws"], stream=stream)
+                          workspace=b["lws"], stream=stream, weight_pow2=b["case"].ue8m0)
 
     def step():
         for b in bufs:

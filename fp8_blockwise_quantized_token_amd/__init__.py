@@ -29,9 +29,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
 
-ABI_VERSION = 4  # FP8BLK_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5  # FP8BLK_ABI_VERSION of the header this binding follows
 GROUP = 128
 FLAG_UE8M0 = 1
+FLAG_WEIGHT_POW2 = 8  # the weight scales are powers of two (fp8_linear, fp8_block_gemm_select)
 STANDARD = 0
 SWAPAB = 1
 DEFAULT_EPS = 1e-10
@@ -283,8 +284,12 @@ def fp8_linear_workspace_size(M: int, N: int, K: int, cfg: GemmConfig | None = N
 
 
 def fp8_linear(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
-               cfg: GemmConfig | None = None, workspace=None, stream=None) -> None:
-    """y[M, N] (bf16) = blockwise GEMM of group-quantized x[M, K] (bf16) and w[N, K]^T."""
+               cfg: GemmConfig | None = None, workspace=None, stream=None,
+               weight_pow2: bool = False) -> None:
+    """y[M, N] (bf16) = blockwise GEMM of group-quantized x[M, K] (bf16) and w[N, K]^T.
+
+    ue8m0: power-of-two activation scales; weight_pow2: the caller's weight
+    scales sw are powers of two (both are needed for the power-of-two GEMM mode)."""
     M, K = x.shape
     N = w.shape[0]
     if w.shape[1] != K or y.shape != (M, N) or x.element_size() != 2:
@@ -293,7 +298,7 @@ def fp8_linear(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().fp8_linear(x.data_ptr(), _ld(x, "x"), w.data_ptr(), sw.data_ptr(), _ld(w, "w"),
                           _ld(sw, "sw"), y.data_ptr(), _ld(y, "y"), M, N, K, eps,
-                          FLAG_UE8M0 if ue8m0 else 0,
+                          (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_WEIGHT_POW2 if weight_pow2 else 0),
                           ctypes.byref(cfg) if cfg is not None else None,
                           ws_ptr, ws_bytes, _stream(stream))
     _check(st, "fp8_linear")
@@ -377,14 +382,14 @@ def linear_workspace(M: int, N: int, K: int, cfg: GemmConfig | None, device):
 
 
 def linear(x, qw, sw, eps: float = DEFAULT_EPS, ue8m0: bool = False, cfg: GemmConfig | None = None,
-           stream=None):
+           stream=None, weight_pow2: bool = False):
     """The whole FP8 linear layer (fp8_linear): quantize x per 1x128 group, then the blockwise GEMM."""
     import torch
     M, K = x.shape
     N = qw.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     ws = linear_workspace(M, N, K, cfg, x.device)
-    fp8_linear(x, qw, sw, y, eps, ue8m0, cfg, ws, stream)
+    fp8_linear(x, qw, sw, y, eps, ue8m0, cfg, ws, stream, weight_pow2)
     return y
 
 

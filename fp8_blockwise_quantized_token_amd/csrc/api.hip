@@ -172,6 +172,7 @@ int fp8_block_gemm_select(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8bl
   if (!out) return FP8BLK_ERR_NULL_PTR;
   const int st = check_gemm_shape(M, N, K);
   if (st != FP8BLK_OK) return st;
+  if ((flags & ~(FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2)) != 0) return FP8BLK_ERR_BAD_CONFIG;
   fp8blk::select_config(M, N, K, flags, out);
   return FP8BLK_OK;
 }
@@ -263,7 +264,7 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   int st = check_gemm_shape(M, N, K);
   if (st != FP8BLK_OK) return st;
   if (K > kMaxK) return FP8BLK_ERR_BAD_SHAPE;
-  st = check_quant_args(eps, flags);
+  st = check_quant_args(eps, flags & ~FP8BLK_FLAG_WEIGHT_POW2);
   if (st != FP8BLK_OK) return st;
   fp8blk_gemm_config c;
   if (cfg) {
@@ -273,6 +274,10 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
   }
   st = check_config(c, M, N, K);
   if (st != FP8BLK_OK) return st;
+  // the matrix core keeps only the exponent bits of every scale: both the
+  // quantizer's scales and the caller's weight scales must be powers of two
+  const uint32_t pow2_flags = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2;
+  if (c.scale_mode == FP8BLK_SCALES_POW2 && (flags & pow2_flags) != pow2_flags) return FP8BLK_ERR_BAD_CONFIG;
   if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
   if (ldw >= kMaxPitch || ldsw * 4 >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
   if (M == 0) return FP8BLK_OK;

@@ -6,10 +6,14 @@
 // "Per-shape Config Tuning").  Here the choice is a compiled-in table keyed
 // on (N, K) and a bucket of M, measured on MI355X, with a heuristic for
 // shapes the table does not hold (the pages fall back to a default config
-// rather than failing when no tuned config exists).  Lookup is O(1) and
-// deterministic; nothing is tuned at run time.
+// rather than failing when no tuned config exists).  Lookup is a binary
+// search over the tabled weight shapes, then a scan of that shape's M
+// buckets; deterministic; nothing is tuned at run time.
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "../../include/fp8blk.h"
 #include "dispatch.hpp"
@@ -99,20 +103,77 @@ bool usable(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   return N % c.tile_n == 0 && standard_tile_supported(c.tile_m, c.tile_n, c.stages, c.kwaves == 0 ? 1 : c.kwaves);
 }
 
+// The table's entries grouped by weight shape: one run per (N, K), its
+// entries in table order, the runs in order of first appearance, plus an
+// index of the runs sorted by (N, K) and the logarithms the nearest-shape
+// rule needs.  Built once (thread-safe static initialization), read-only
+// afterwards.
+struct Run {
+  int32_t n, k;
+  double ln_n, ln_k;
+  std::vector<const Entry*> entries;
+};
+struct Index {
+  std::vector<Run> runs;
+  std::vector<int> by_shape;  // run numbers sorted by (n, k)
+};
+
+const Index& table_index() {
+  static const Index idx = [] {
+    Index x;
+    for (const Entry& e : kTable) {
+      auto it = std::find_if(x.runs.begin(), x.runs.end(), [&](const Run& r) { return r.n == e.n && r.k == e.k; });
+      if (it == x.runs.end()) {
+        x.runs.push_back(Run{e.n, e.k, log((double)e.n), log((double)e.k), {}});
+        it = x.runs.end() - 1;
+      }
+      it->entries.push_back(&e);
+    }
+    for (int i = 0; i < (int)x.runs.size(); ++i) x.by_shape.push_back(i);
+    std::sort(x.by_shape.begin(), x.by_shape.end(), [&](int a, int b) {
+      const Run &ra = x.runs[a], &rb = x.runs[b];
+      return ra.n != rb.n ? ra.n < rb.n : ra.k < rb.k;
+    });
+    return x;
+  }();
+  return idx;
+}
+
+// The first entry of a run whose M bucket holds M (and, if asked, whose
+// configuration is usable for the shape), or nullptr.
+const Entry* bucket(const Run& r, int64_t M, int64_t N, int64_t K, bool need_usable) {
+  for (const Entry* e : r.entries)
+    if (M >= e->m_lo && M <= e->m_hi && (!need_usable || usable(e->cfg, M, N, K))) return e;
+  return nullptr;
+}
+
+// The tabled entry for exactly (N, K) whose bucket holds M.
+const Entry* exact(int64_t M, int64_t N, int64_t K) {
+  const Index& x = table_index();
+  auto it = std::lower_bound(x.by_shape.begin(), x.by_shape.end(), 0, [&](int a, int) {
+    const Run& r = x.runs[a];
+    return r.n != N ? r.n < N : r.k < K;
+  });
+  if (it == x.by_shape.end() || x.runs[*it].n != N || x.runs[*it].k != K) return nullptr;
+  return bucket(x.runs[*it], M, N, K, false);
+}
+
 // Nearest tabled weight shape: the entry whose M bucket holds M and whose
-// (N, K) is closest in |ln(N/n)| + |ln(K/k)| among the usable ones (first
-// in table order on ties).  Layers of other models of similar size get the
-// configuration measured for their neighbour instead of the heuristic's.
+// (N, K) is closest in |ln(N/n)| + |ln(K/k)| among the usable ones (the
+// shape tabled first on ties).  Layers of other models of similar size get
+// the configuration measured for their neighbour instead of the heuristic's.
 bool nearest(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* out) {
+  const Index& x = table_index();
+  const double ln_n = log((double)N), ln_k = log((double)K);
   double best = 1e30;
   const Entry* pick = nullptr;
-  for (const Entry& e : kTable) {
-    if (M < e.m_lo || M > e.m_hi || !usable(e.cfg, M, N, K)) continue;
-    const double d = fabs(log((double)N / e.n)) + fabs(log((double)K / e.k));
-    if (d < best) {
-      best = d;
-      pick = &e;
-    }
+  for (const Run& r : x.runs) {
+    const double d = fabs(ln_n - r.ln_n) + fabs(ln_k - r.ln_k);
+    if (d >= best) continue;
+    const Entry* e = bucket(r, M, N, K, true);
+    if (e == nullptr) continue;
+    best = d;
+    pick = e;
   }
   if (pick == nullptr || best > kMaxShapeDistance) return false;
   *out = pick->cfg;
@@ -122,19 +183,16 @@ bool nearest(int64_t M, int64_t N, int64_t K, fp8blk_gemm_config* out) {
 }  // namespace
 
 void select_config(int64_t M, int64_t N, int64_t K, uint32_t flags, fp8blk_gemm_config* out) {
-  bool found = false;
-  for (const Entry& e : kTable) {
-    if (e.n == N && e.k == K && M >= e.m_lo && M <= e.m_hi) {
-      *out = e.cfg;
-      found = true;
-      break;
-    }
-  }
+  const Entry* e = exact(M, N, K);
+  bool found = e != nullptr;
+  if (found) *out = e->cfg;
   if (!found) found = nearest(M, N, K, out);
   if (!found) heuristic(M, N, K, out);
-  // UE8M0 scales are powers of two: the Standard kernels apply them in the
-  // matrix core (v_mfma_scale) instead of one VALU rescale per K block.
-  if ((flags & FP8BLK_FLAG_UE8M0) && out->variant == FP8BLK_STANDARD) out->scale_mode = FP8BLK_SCALES_POW2;
+  // Power-of-two activation and weight scales: the Standard kernels apply
+  // them in the matrix core (v_mfma_scale) instead of one VALU rescale per
+  // K block.  Both operands must be powers of two for that.
+  const uint32_t both = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2;
+  if ((flags & both) == both && out->variant == FP8BLK_STANDARD) out->scale_mode = FP8BLK_SCALES_POW2;
 }
 
 }  // namespace fp8blk

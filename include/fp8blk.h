@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 4
+#define FP8BLK_ABI_VERSION 5
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
 /* Smallest accepted eps (2^-80, about 8.3e-25).  With eps at least this,
@@ -77,12 +77,18 @@ extern "C" {
                                 "float32 ceiling E8M0"): page "Helion-Kernel in
                                 vLLM", section "Praktische Einschränkungen";
                                 RFC page, H100 end-to-end settings */
+#define FP8BLK_FLAG_WEIGHT_POW2 8u /* fp8_linear, fp8_block_gemm_select: the caller
+                                guarantees that every weight scale sw is a power of
+                                two (weights quantized with FP8BLK_FLAG_UE8M0).
+                                Together with FP8BLK_FLAG_UE8M0 it lets STANDARD
+                                configurations use FP8BLK_SCALES_POW2. */
 
 /* How the GEMM applies the K-block scales (fp8blk_gemm_config.scale_mode) */
 #define FP8BLK_SCALES_FP32 0 /* any fp32 scales: one fp32 rescale per K block */
 #define FP8BLK_SCALES_POW2 1 /* every sa and sw is a power of two (UE8M0):
                                 applied exactly by the matrix core (STANDARD
-                                only; results unspecified for other scales) */
+                                only; results unspecified for other scales:
+                                only the exponent bits of each scale are used) */
 
 /* Scale output of fp8_group_quant for other consumers (German page,
  * "Praktische Einschränkungen": UE8M0 scales for GEMMs that take them) */
@@ -190,10 +196,13 @@ int fp8_e4m3_encode(const float *t, uint8_t *q, int64_t n, void *stream);
  * Per-shape dispatch: the configuration fp8_block_gemm uses when cfg is NULL.
  * A table tuned on MI355X keyed on (N, K) and a bucket of M, with a
  * heuristic for shapes not in the table (autotuning page, "Hybrid Dispatch"
- * and "Per-shape Config Tuning").  With FP8BLK_FLAG_UE8M0 in flags (the
- * caller guarantees power-of-two scales) STANDARD choices get
- * scale_mode = FP8BLK_SCALES_POW2.  Deterministic, host-only.
- * Returns FP8BLK_OK or FP8BLK_ERR_BAD_SHAPE / FP8BLK_ERR_NULL_PTR.
+ * and "Per-shape Config Tuning").  flags: FP8BLK_FLAG_UE8M0 (the activation
+ * scales are powers of two) and FP8BLK_FLAG_WEIGHT_POW2 (the weight scales
+ * are powers of two); with both, STANDARD choices get scale_mode =
+ * FP8BLK_SCALES_POW2.  Deterministic, host-only: a binary search over the
+ * tabled weight shapes, then a scan of that shape's M buckets.
+ * Returns FP8BLK_OK, or FP8BLK_ERR_BAD_SHAPE / FP8BLK_ERR_NULL_PTR /
+ * FP8BLK_ERR_BAD_CONFIG (unknown flags).
  */
 int fp8_block_gemm_select(int64_t M, int64_t N, int64_t K, uint32_t flags,
                           fp8blk_gemm_config *out);
@@ -246,8 +255,13 @@ int fp8_block_gemm(const uint8_t *a, const float *sa, int64_t lda, int64_t ldsa,
  *   workspace, then the GEMM.
  *   x  bf16 [M][ldx], ldx >= K            w, sw, y, ldw, ldsw, ldy as in
  *                                           fp8_block_gemm
- *   eps, flags as in fp8_group_quant (flags: FP8BLK_FLAG_UE8M0 or 0).
- *   cfg NULL selects through fp8_block_gemm_select.
+ *   eps as in fp8_group_quant.  flags: FP8BLK_FLAG_UE8M0 (power-of-two
+ *   activation scales, as in fp8_group_quant) and FP8BLK_FLAG_WEIGHT_POW2
+ *   (the caller's weight scales sw are powers of two).  The power-of-two
+ *   GEMM mode needs both: cfg NULL selects through fp8_block_gemm_select with
+ *   these flags (so UE8M0 activations with fp32 weight scales keep the fp32
+ *   mode), and a caller cfg with scale_mode = FP8BLK_SCALES_POW2 without
+ *   both flags returns FP8BLK_ERR_BAD_CONFIG.
  *   workspace: device buffer of at least fp8_linear_workspace_size bytes,
  *   16-byte aligned (may be NULL when that is 0); concurrent calls must not
  *   share one.  Layout: fp8 x [M][K] and its scales [M][K/128] (unless the

@@ -70,10 +70,14 @@ def oracle_weight(N: int, K: int, ue8m0: bool):
     return _WCACHE[key]
 
 
-def sample_rows(M: int, n: int = 12, key: int = 0) -> np.ndarray:
-    """First, last and a seeded spread of rows."""
+def sample_rows(M: int, n: int = 12, key: int = 0, band: int = 256) -> np.ndarray:
+    """First, last, one seeded row in every band of `band` rows (so every
+    256-row tile row of the GEMM is checked) and a seeded spread of n - 2
+    more rows."""
     if M <= n:
         return np.arange(M)
     rng = synth.generator(500, M, key)
     mid = rng.choice(np.arange(1, M - 1), size=n - 2, replace=False)
-    return np.unique(np.concatenate([[0, M - 1], mid]))
+    starts = np.arange(0, M, band)
+    per_band = starts + (rng.random(starts.size) * np.minimum(band, M - starts)).astype(np.int64)
+    return np.unique(np.concatenate([[0, M - 1], mid, per_band]))

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fb.fp8_abi_version() == fb.ABI_VERSION == 4
+    assert fb.fp8_abi_version() == fb.ABI_VERSION == 5
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert fb.fp8_status_string(st) != "unknown status"
     assert fb.fp8_status_string(-99) == "unknown status"
@@ -182,17 +182,42 @@ def test_select_and_workspace_queries():
             assert 1 <= c.split_k <= case.K // 128
 
 
-def test_select_ue8m0_flag_sets_power_of_two_mode():
+def test_select_power_of_two_mode_needs_both_flags():
+    both = fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2
     for config in ("prefill_8b", "ue8m0_32b", "decode_8b"):
         for case in synth.cases(config):
             plain = fb.fp8_block_gemm_select(case.M, case.N, case.K, 0)
-            p2 = fb.fp8_block_gemm_select(case.M, case.N, case.K, fb.FLAG_UE8M0)
+            p2 = fb.fp8_block_gemm_select(case.M, case.N, case.K, both)
             assert plain.scale_mode == fb.SCALES_FP32
             want = fb.SCALES_POW2 if plain.variant == fb.STANDARD else fb.SCALES_FP32
             assert p2.scale_mode == want
+            # one of the two alone: power-of-two activations with fp32 weight
+            # scales (or the converse) keep the fp32 mode
+            for one in (fb.FLAG_UE8M0, fb.FLAG_WEIGHT_POW2):
+                assert fb.fp8_block_gemm_select(case.M, case.N, case.K, one).scale_mode == fb.SCALES_FP32
             d1, d2 = plain.as_dict(), p2.as_dict()
             d1.pop("scale_mode"), d2.pop("scale_mode")
             assert d1 == d2
+
+
+def test_select_rejects_unknown_flags():
+    c = fb.GemmConfig()
+    for flags in (2, 4, 16, 1 << 31):
+        assert fb.lib().fp8_block_gemm_select(64, 4096, 4096, flags, ctypes.byref(c)) == CFG
+
+
+def test_linear_power_of_two_config_needs_both_flags():
+    # the matrix core keeps only the exponent bits of every scale: a caller's
+    # power-of-two configuration is refused unless the activation scales
+    # (FP8BLK_FLAG_UE8M0) and the weight scales (FP8BLK_FLAG_WEIGHT_POW2) are
+    # both powers of two; nothing is launched
+    p2 = fb.make_config(fb.STANDARD, 128, 128, scale_mode=fb.SCALES_POW2)
+    n = fb.fp8_linear_workspace_size(8, 256, 256, p2)
+    for flags in (0, fb.FLAG_UE8M0, fb.FLAG_WEIGHT_POW2):
+        assert _lin(flags=flags, cfg=p2, ws=0x70000, ws_bytes=n) == CFG, flags
+    # unknown flag bits are refused too
+    assert _lin(flags=16, cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2)) == CFG
+    assert _lin(flags=fb.FLAG_UE8M0 | 2, cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2)) == CFG
 
 
 def test_select_is_deterministic_and_swaps_small_m():
@@ -236,7 +261,7 @@ def test_selected_configs_are_valid_for_any_shape():
         M = int(rng.integers(1, 20000))
         N = 128 * int(rng.integers(1, 600))
         K = 128 * int(rng.integers(1, 300))
-        for flags in (0, fb.FLAG_UE8M0):
+        for flags in (0, fb.FLAG_UE8M0, fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2):
             c = fb.fp8_block_gemm_select(M, N, K, flags)
             assert fb.fp8_block_gemm_workspace_size(M, N, K, c) >= 0, (M, N, K, flags, c.as_dict())
             assert fb.fp8_linear_workspace_size(M, N, K, c) >= 0, (M, N, K, flags, c.as_dict())

@@ -183,17 +183,48 @@ def test_graph_replay_of_fused_linear():
 
 @pytest.mark.parametrize("case", [c for c in synth.cases("ue8m0_32b")], ids=lambda c: c.cid)
 def test_full_size_ue8m0_linear_dispatched(case):
-    """The UE8M0 layers through fp8_linear with the UE8M0 flag (Standard
-    configurations then scale in the matrix core), against the oracle on
-    sampled rows."""
+    """The UE8M0 layers through fp8_linear with power-of-two activation and
+    weight scales (Standard configurations then scale in the matrix core),
+    against the oracle on sampled rows."""
     import torch
     x = synth.activations_bf16(case)
     qw, sw = oracle_weight(case.N, case.K, True)
-    cfg = fb.fp8_block_gemm_select(case.M, case.N, case.K, fb.FLAG_UE8M0)
+    cfg = fb.fp8_block_gemm_select(case.M, case.N, case.K, fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2)
     say("ue8m0 linear", case.cid, cfg.as_dict())
-    y = fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=True)
+    y = fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=True, weight_pow2=True)
     torch.cuda.synchronize()
     rows = sample_rows(case.M, 8)
     qa_ref, sa_ref = oracle.group_quant(x[rows], ue8m0=True)
     ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
     assert_close(host(y)[rows].astype(np.float64), ref, case.cid)
+
+
+@pytest.mark.parametrize("M,N,K", [(96, 1024, 1024), (640, 2048, 1536), (4096, 5120, 2048)])
+def test_ue8m0_activations_with_fp32_weight_scales(M, N, K):
+    """Power-of-two activation scales with arbitrary fp32 weight scales: the
+    dispatched Standard configuration must keep the fp32 scale mode (only the
+    caller's FP8BLK_FLAG_WEIGHT_POW2 allows the power-of-two mode), and the
+    result must match the oracle.  A power-of-two configuration with the
+    UE8M0 flag alone is refused."""
+    import torch
+    x = _x(M, K, "normal_outlier", key=M % 7)
+    qw, sw = oracle_weight(N, K, False)
+    assert np.any(sw != pow2_floor(sw)), "weight scales must not all be powers of two here"
+    cfg = fb.fp8_block_gemm_select(M, N, K, fb.FLAG_UE8M0)
+    assert cfg.variant == fb.STANDARD and cfg.scale_mode == fb.SCALES_FP32, cfg
+    say("ue8m0 activations, fp32 weight scales", M, N, K, cfg.as_dict())
+    y = fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 16, key=M)
+    qa_ref, sa_ref = oracle.group_quant(x[rows], ue8m0=True)
+    ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
+    assert_close(host(y)[rows].astype(np.float64), ref, "ue8m0 x fp32 weights")
+    p2 = fb.fp8_block_gemm_select(M, N, K, fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2)
+    assert p2.scale_mode == fb.SCALES_POW2
+    with pytest.raises(fb.Fp8BlkError) as e:
+        fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=True, cfg=p2)
+    assert e.value.status == -6
+
+
+def pow2_floor(s):
+    return (s.view(np.uint32) & np.uint32(0x7F800000)).view(np.float32)
