@@ -67,6 +67,14 @@ def _load():
     lib.orc_rms_norm_per_block_quant.argtypes = [P, P, I64, I64, ctypes.c_float, P, P, ctypes.c_float, ctypes.c_int]
     lib.orc_silu_and_mul_per_block_quant.restype = None
     lib.orc_silu_and_mul_per_block_quant.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_group_quant_f32.restype = None
+    lib.orc_group_quant_f32.argtypes = [P, I64, I64, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_rms_norm_inv_rms.restype = None
+    lib.orc_rms_norm_inv_rms.argtypes = [P, I64, I64, ctypes.c_float, P]
+    lib.orc_rms_norm_apply.restype = None
+    lib.orc_rms_norm_apply.argtypes = [P, P, I64, I64, P, P, P, ctypes.c_float, ctypes.c_int]
+    lib.orc_silu_and_mul_values.restype = None
+    lib.orc_silu_and_mul_values.argtypes = [P, I64, I64, P]
     lib.orc_scaled_mm.restype = ctypes.c_int
     lib.orc_scaled_mm.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
     _lib = lib
@@ -247,6 +255,58 @@ def silu_and_mul_per_block_quant(x_bf16_bits: np.ndarray, eps=DEFAULT_EPS, ue8m0
     s = np.empty((M, I // GROUP), dtype=np.float32)
     lib.orc_silu_and_mul_per_block_quant(_ptr(x), M, I, _ptr(q), _ptr(s), float(np.float32(eps)), int(ue8m0))
     return q, s
+
+
+def group_quant_f32(y: np.ndarray, eps=DEFAULT_EPS, ue8m0: bool = False):
+    """The group rule on float32 values Y [M, K] already computed (the last step
+    of both fused producers).  Returns (q uint8 [M, K], s float32 [M, K/128])."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, K = y.shape
+    assert K % GROUP == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // GROUP), dtype=np.float32)
+    lib.orc_group_quant_f32(_ptr(y), M, K, _ptr(q), _ptr(s), float(np.float32(eps)), int(ue8m0))
+    return q, s
+
+
+def rms_norm_inv_rms(x_bf16_bits: np.ndarray, eps_norm=1e-6) -> np.ndarray:
+    """RMSNorm's 1/rms of every row of X [M, H] in float64, before the oracle
+    rounds it to float32."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, H = x.shape
+    r = np.empty((M,), dtype=np.float64)
+    lib.orc_rms_norm_inv_rms(_ptr(x), M, H, float(np.float32(eps_norm)), _ptr(r))
+    return r
+
+
+def rms_norm_apply(x_bf16_bits: np.ndarray, w: np.ndarray, r: np.ndarray, eps=DEFAULT_EPS,
+                   ue8m0: bool = False):
+    """rms_norm_per_block_quant with the float32 1/rms of every row given."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    M, H = x.shape
+    assert H % GROUP == 0 and w.shape == (H,) and r.shape == (M,)
+    q = np.empty((M, H), dtype=np.uint8)
+    s = np.empty((M, H // GROUP), dtype=np.float32)
+    lib.orc_rms_norm_apply(_ptr(x), _ptr(w), M, H, _ptr(r), _ptr(q), _ptr(s), float(np.float32(eps)),
+                           int(ue8m0))
+    return q, s
+
+
+def silu_and_mul_values(x_bf16_bits: np.ndarray) -> np.ndarray:
+    """silu(gate) * up of X [M, 2I] in float64, before the oracle rounds it to
+    float32.  Returns float64 [M, I]."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, I2 = x.shape
+    I = I2 // 2
+    y = np.empty((M, I), dtype=np.float64)
+    lib.orc_silu_and_mul_values(_ptr(x), M, I, _ptr(y))
+    return y
 
 
 def lib_path() -> str:

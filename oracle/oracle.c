@@ -254,25 +254,73 @@ static void group_quant_row(const float *y, int64_t n, uint8_t *q, float *s, flo
         s[g] = quantize_row(y + g * ORC_GROUP, ORC_GROUP, q + g * ORC_GROUP, eps, ue8m0);
 }
 
+/* Group quantization of M rows of K float values (the group rule on values
+ * already computed in float): q [M][K], s [M][K/128]. */
+void orc_group_quant_f32(const float *y, int64_t M, int64_t K, uint8_t *q, float *s,
+                         float eps, int ue8m0)
+{
+    for (int64_t m = 0; m < M; ++m)
+        group_quant_row(y + m * K, K, q + m * K, s + m * (K / ORC_GROUP), eps, ue8m0);
+}
+
+/* RMSNorm's 1/rms of one row, in double (before its rounding to float):
+ * variance = sum of squares / H, 1 / sqrt(variance + eps_norm). */
+static double rms_inv_rms_row(const uint16_t *xr, int64_t H, float eps_norm)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+        double v = (double)bf16_value(xr[j]);
+        ss += v * v;
+    }
+    double var = ss / (double)H;
+    return 1.0 / sqrt(var + (double)eps_norm);
+}
+
+/* The normalized row y = (x * r) * w in float for a float 1/rms r, then the
+ * group quantizer. */
+static void rms_apply_row(const uint16_t *xr, const float *w, int64_t H, float r, float *y,
+                          uint8_t *q, float *s, float eps, int ue8m0)
+{
+    for (int64_t j = 0; j < H; ++j)
+        y[j] = (bf16_value(xr[j]) * r) * w[j];
+    group_quant_row(y, H, q, s, eps, ue8m0);
+}
+
 /* rms_norm_per_block_quant: x bf16 [M][H], w fp32 [H] -> q [M][H], s [M][H/128]. */
 void orc_rms_norm_per_block_quant(const uint16_t *x, const float *w, int64_t M, int64_t H,
                               float eps_norm, uint8_t *q, float *s, float eps, int ue8m0)
 {
     float *y = (float *)malloc((size_t)H * sizeof(float));
     for (int64_t m = 0; m < M; ++m) {
-        const uint16_t *xr = x + m * H;
-        double ss = 0.0;
-        for (int64_t j = 0; j < H; ++j) {
-            double v = (double)bf16_value(xr[j]);
-            ss += v * v;
-        }
-        double var = ss / (double)H;
-        float r = (float)(1.0 / sqrt(var + (double)eps_norm));
-        for (int64_t j = 0; j < H; ++j)
-            y[j] = (bf16_value(xr[j]) * r) * w[j];
-        group_quant_row(y, H, q + m * H, s + m * (H / ORC_GROUP), eps, ue8m0);
+        float r = (float)rms_inv_rms_row(x + m * H, H, eps_norm);
+        rms_apply_row(x + m * H, w, H, r, y, q + m * H, s + m * (H / ORC_GROUP), eps, ue8m0);
     }
     free(y);
+}
+
+/* The double 1/rms of every row, before the rounding to float (r64 [M]). */
+void orc_rms_norm_inv_rms(const uint16_t *x, int64_t M, int64_t H, float eps_norm, double *r64)
+{
+    for (int64_t m = 0; m < M; ++m)
+        r64[m] = rms_inv_rms_row(x + m * H, H, eps_norm);
+}
+
+/* rms_norm_per_block_quant with the float 1/rms of every row given (r [M]). */
+void orc_rms_norm_apply(const uint16_t *x, const float *w, int64_t M, int64_t H, const float *r,
+                        uint8_t *q, float *s, float eps, int ue8m0)
+{
+    float *y = (float *)malloc((size_t)H * sizeof(float));
+    for (int64_t m = 0; m < M; ++m)
+        rms_apply_row(x + m * H, w, H, r[m], y, q + m * H, s + m * (H / ORC_GROUP), eps, ue8m0);
+    free(y);
+}
+
+/* silu(g) * u = g / (1 + e^-g) * u in double, before its rounding to float. */
+static double silu_mul_value(uint16_t gb, uint16_t ub)
+{
+    double g = (double)bf16_value(gb);
+    double u = (double)bf16_value(ub);
+    return g / (1.0 + exp(-g)) * u;
 }
 
 /* silu_and_mul_per_block_quant: x bf16 [M][2I] = [gate | up] -> q [M][I], s [M][I/128]. */
@@ -282,14 +330,20 @@ void orc_silu_and_mul_per_block_quant(const uint16_t *x, int64_t M, int64_t I, u
     float *y = (float *)malloc((size_t)I * sizeof(float));
     for (int64_t m = 0; m < M; ++m) {
         const uint16_t *xr = x + m * 2 * I;
-        for (int64_t j = 0; j < I; ++j) {
-            double g = (double)bf16_value(xr[j]);
-            double u = (double)bf16_value(xr[I + j]);
-            y[j] = (float)(g / (1.0 + exp(-g)) * u);
-        }
+        for (int64_t j = 0; j < I; ++j)
+            y[j] = (float)silu_mul_value(xr[j], xr[I + j]);
         group_quant_row(y, I, q + m * I, s + m * (I / ORC_GROUP), eps, ue8m0);
     }
     free(y);
+}
+
+/* The double silu(g) * u of every element, before the rounding to float
+ * (y64 [M][I]). */
+void orc_silu_and_mul_values(const uint16_t *x, int64_t M, int64_t I, double *y64)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < I; ++j)
+            y64[m * I + j] = silu_mul_value(x[m * 2 * I + j], x[m * 2 * I + I + j]);
 }
 
 /* ------------------------------------------------------------------ */
