@@ -28,10 +28,8 @@
 //   current one is reduced and quantized.
 //
 // SiLU-and-mul: x row = [gate (I values) | up (I values)]; y = silu(g) * u
-// in fp32, quantized from fp32.  At 5 bytes per element the kernel must stay
-// near 30 VALU cycles per element to remain on the HBM roofline, so large
-// problems take the logistic function from a correctly rounded table (LDS)
-// and small ones compute it with a trimmed exp2 and a corrected division.
+// from a float64 product with a correctly rounded float64 logistic table,
+// rounded once to fp32 and quantized from fp32.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -333,60 +331,26 @@ hipError_t launch_rms(const uint16_t* x, int64_t ldx, const float* w, uint8_t* q
 // Grid-stride over the groups, the next iteration's loads issued before the
 // current groups are computed.
 //
-// Two ways to the sigmoid (TAB):
-//   - table: s(g) = 1 / (1 + e^-g) correctly rounded to fp32 for every bf16
-//     g, copied once per workgroup into LDS (8196 floats; see
-//     sigmoid_table.inc) and looked up by the bits of g: 6 integer/LDS
-//     operations per value; y = RN(RN(g u) s) with g u exact, within an ulp.
-//     Used when the problem is large enough to amortize the table copy.
-//   - arithmetic: (g u) / (1 + e^-g) with the hardware exp2 and a corrected
-//     division (about 1.5 ulp); no set-up, for small problems.
+// The logistic function comes from a table of t(a) = 1 / (1 + e^a) for
+// every bf16 magnitude a, correctly rounded to float64 (sigmoid_table.inc):
+// s(g) = t(|g|) for g <= 0 and 1 - t(|g|) for g > 0, and y = (g u) s(g) in
+// float64 (g u exact there), rounded once to float32.  The float64 value is
+// within 2^-51 (relative) of the exact silu(g) u, so the float32 y is the
+// correctly rounded one except next to a rounding midpoint.  Large problems
+// copy the table (61 KB) into LDS once per workgroup (TAB); small ones,
+// where that copy would not pay, read it from global memory (L2).
 constexpr int kSiluUnroll = 2;
 
 #include "sigmoid_table.inc"
 
-constexpr float kLog2eHi = 0x1.715476p+0f;   // log2(e) rounded to fp32
-constexpr float kLog2eLo = 0x1.4ae0c0p-26f;  // log2(e) - kLog2eHi
-constexpr float kLn2 = 0x1.62e430p-1f;
-
-// e^n for n <= 80: 2^p with p = RN(n log2 e) from the hardware exp2, times
-// (1 + p_lo ln 2) for the part of n log2 e that p dropped (p_lo from two
-// FMAs: the exact residual of n * kLog2eHi plus n * kLog2eLo).  Within about
-// an ulp; underflows to 0 for n below about -87 (where 1 + e^n rounds to 1).
-__device__ __forceinline__ float exp_capped(float n) {
-  const float p = n * kLog2eHi;
-  const float plo = __builtin_fmaf(n, kLog2eLo, __builtin_fmaf(n, kLog2eHi, -p));
-  const float e0 = __builtin_amdgcn_exp2f(p);
-  return __builtin_fmaf(e0 * plo, kLn2, e0);
-}
-
-// silu(g) * u = (g u) / (1 + e^-g).  g u is exact in fp32 (two 8-bit
-// significands).  1 + e is rounded to d with its error t recovered exactly
-// (Fast2Sum on the larger and smaller of 1 and e), the quotient by d taken
-// from the hardware reciprocal and corrected once with the exact residual
-// g u - q d, less q t for the rounding of the divisor.  The result is within
-// a fraction of an ulp of (g u) / (1 + e), so only exp's error (about an
-// ulp) remains.  e^-g is capped at e^80 so that d and 1/d stay normal; for
-// g < -80 the true value is below 1e-30 |g u| either way.  The sign is that
-// of g u.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float gu = g * u;
-  const float e = exp_capped(__builtin_amdgcn_fmed3f(-g, -1.0e30f, 80.0f));
-  const float a = fmaxf(1.0f, e), b = fminf(1.0f, e);
-  const float d = a + b;
-  const float t = b - (d - a);
-  const float rd = __builtin_amdgcn_rcpf(d);
-  const float q = gu * rd;
-  const float r = __builtin_fmaf(-q, d, gu);
-  const float r2 = __builtin_fmaf(-q, t, r);
-  return __builtin_copysignf(__builtin_fmaf(r2, rd, q), gu);
-}
-
-// Table lookup of s(g) for the bf16 bit pattern h (low 16 bits): the
-// magnitude bits clamped to the table's span, the sign selecting the half.
-__device__ __forceinline__ float sigmoid_lookup(uint32_t h, const float* tab) {
+// silu(g) * u for the bf16 gate bits h (low 16 bits) and the gate and up
+// values widened to fp32.  The sign of a zero product is that of g u (a
+// multiplication by the positive s(g)).
+__device__ __forceinline__ float silu_mul64(uint32_t h, float g, float u, const double* tab) {
   const int i = min(max((int)(h & 0x7FFFu) - kSigmoidBase, 0), kSigmoidSpan - 1);
-  return tab[i + (int)((h >> 15) & 1u) * kSigmoidSpan];
+  const double t = tab[i];
+  const double sg = (h & 0x8000u) ? t : 1.0 - t;
+  return (float)(((double)g * (double)u) * sg);
 }
 
 // One iteration's inputs for kSiluUnroll groups per 16 lanes, with each
@@ -420,9 +384,9 @@ __device__ __forceinline__ void silu_load(SiluFrag& f, const uint16_t* __restric
   }
 }
 
-template <bool TAB, uint32_t NS>
+template <uint32_t NS>
 __device__ __forceinline__ void silu_compute_store(const SiluFrag& f, uint32_t base, uint32_t slot,
-                                                   uint32_t sub, uint32_t total, const float* tab,
+                                                   uint32_t sub, uint32_t total, const double* tab,
                                                    uint8_t* __restrict__ q, void* __restrict__ s,
                                                    int64_t lds, int64_t row0, float eps, int ue8m0,
                                                    int fmt) {
@@ -434,13 +398,8 @@ __device__ __forceinline__ void silu_compute_store(const SiluFrag& f, uint32_t b
     float y[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (TAB) {
-        y[2 * j] = (bf16_lo(gc[j]) * bf16_lo(uc[j])) * sigmoid_lookup(gc[j], tab);
-        y[2 * j + 1] = (bf16_hi(gc[j]) * bf16_hi(uc[j])) * sigmoid_lookup(gc[j] >> 16, tab);
-      } else {
-        y[2 * j] = silu_mul(bf16_lo(gc[j]), bf16_lo(uc[j]));
-        y[2 * j + 1] = silu_mul(bf16_hi(gc[j]), bf16_hi(uc[j]));
-      }
+      y[2 * j] = silu_mul64(gc[j], bf16_lo(gc[j]), bf16_lo(uc[j]), tab);
+      y[2 * j + 1] = silu_mul64(gc[j] >> 16, bf16_hi(gc[j]), bf16_hi(uc[j]), tab);
     }
     float sc;
     const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);
@@ -460,7 +419,8 @@ __global__ __launch_bounds__(NT) void k_silu_mul_quant(
     uint32_t I, float eps, int ue8m0, int fmt) {
   constexpr uint32_t kSlots = NT / 16;
   constexpr uint32_t kPerIter = kSlots * kSiluUnroll;
-  __shared__ float tab[TAB ? 2 * kSigmoidSpan : 1];
+  __shared__ double lds_tab[TAB ? kSigmoidSpan : 1];
+  const double* tab = TAB ? lds_tab : kSigmoidTable;
   const uint32_t sub = threadIdx.x & 15u;
   const uint32_t slot = threadIdx.x >> 4;
   const uint32_t step = gridDim.x * kPerIter;
@@ -469,7 +429,7 @@ __global__ __launch_bounds__(NT) void k_silu_mul_quant(
   SiluFrag fa, fb;
   silu_load<kSlots>(fa, x, ldx, ldq, base, slot, sub, total, gpr, magic, I);
   if (TAB) {
-    for (int i = threadIdx.x; i < 2 * kSigmoidSpan; i += NT) tab[i] = kSigmoidTable[i];
+    for (int i = threadIdx.x; i < kSigmoidSpan; i += NT) lds_tab[i] = kSigmoidTable[i];
     __syncthreads();
   }
   // two fragments used in turn: the loads of one are in flight while the
@@ -477,12 +437,12 @@ __global__ __launch_bounds__(NT) void k_silu_mul_quant(
   for (;;) {
     uint32_t nb = base + step;
     if (nb < total) silu_load<kSlots>(fb, x, ldx, ldq, nb, slot, sub, total, gpr, magic, I);
-    silu_compute_store<TAB, kSlots>(fa, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
+    silu_compute_store<kSlots>(fa, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
     base = nb;
     if (base >= total) break;
     nb = base + step;
     if (nb < total) silu_load<kSlots>(fa, x, ldx, ldq, nb, slot, sub, total, gpr, magic, I);
-    silu_compute_store<TAB, kSlots>(fb, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
+    silu_compute_store<kSlots>(fb, base, slot, sub, total, tab, q, s, lds, row0, eps, ue8m0, fmt);
     base = nb;
     if (base >= total) break;
   }
@@ -582,12 +542,12 @@ hipError_t launch_silu_mul_quant(const uint16_t* x, int64_t M, int64_t I, int64_
     const int64_t rows = (M - r0) < rows_per_chunk ? (M - r0) : rows_per_chunk;
     const uint32_t total = (uint32_t)(rows * gpr);
     // the LDS table pays off once every resident workgroup has several
-    // iterations to run (4 workgroups of 512 threads per CU)
-    const bool tab = total >= (uint32_t)cus * 4 * (512 / 16) * kSiluUnroll * 2;
+    // iterations to run (2 workgroups of 512 threads per CU: 61 KB of LDS each)
+    const bool tab = total >= (uint32_t)cus * 2 * (512 / 16) * kSiluUnroll * 2;
     const int nt = tab ? 512 : 256;
     const uint32_t per_iter = (uint32_t)(nt / 16) * kSiluUnroll;
     int64_t blocks = (total + per_iter - 1) / per_iter;
-    const int64_t max_blocks = (int64_t)cus * (tab ? 4 : 8);
+    const int64_t max_blocks = (int64_t)cus * (tab ? 2 : 8);
     if (blocks > max_blocks) blocks = max_blocks;
     const int u = ue8m0 ? 1 : 0;
     const uint16_t* xr = x + r0 * ldx;

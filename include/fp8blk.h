@@ -353,13 +353,13 @@ int fp8_rms_norm_per_block_quant(const uint16_t *x, int64_t M, int64_t H, int64_
  * silu_and_mul_per_block_quant -- SiLU(gate) * up fused with the 1x128
  * group quantizer (German page, "Welche Kernel wurden in vLLM integriert";
  * RFC page, "Motivation").  Row m of x holds [gate | up], I values each:
- *   y[m][j] = silu(g) * u = (g * u) / (1 + exp(-g)),  g = x[m][j], u = x[m][I + j]
- * in fp32, then fp8_group_quant's rule on every 128-group of y.  The
- * division is corrected to within a fraction of an ulp and exp is within
- * an ulp, so y may differ from the correctly rounded value by up to about
- * 1.5 ulp; codes can then
- * differ by one step next to a rounding midpoint.  exp(-g) is capped at
- * exp(80): for g < -80, |y| < 1e-30 |g u| either way.
+ *   y[m][j] = silu(g) * u = g * u / (1 + exp(-g)),  g = x[m][j], u = x[m][I + j]
+ * as the fp32 rounding of a float64 value within 2^-51 (relative) of the
+ * exact one: g * u exact in float64, times the logistic function taken from
+ * a correctly rounded float64 table of 1 / (1 + e^|g|) (1 minus it for
+ * g > 0).  y is thus the correctly rounded fp32 value except where the
+ * exact value lies within 2^-51 of a rounding midpoint.  Then
+ * fp8_group_quant's rule on every 128-group of y.
  *   x  bf16 [M][ldx], ldx >= 2I          q uint8 [M][ldq], ldq >= I
  *   s  as fp8_group_quant's with K = I
  *   Requires I % 128 == 0, I <= 4194304, M >= 0, eps >= FP8BLK_MIN_EPS and finite; alignment as

@@ -3,17 +3,18 @@ silu_and_mul_per_block_quant against the CPU oracle, through the C ABI.
 
 RMSNorm: the kernel takes every precision decision the oracle takes (sum of
 squares of bf16 values in fp64, 1/sqrt in fp64 rounded once to fp32, two
-fp32 products, fp32 quotient by the scale), so codes and scales must match
-bit for bit.  The only freedom is the order of the fp64 additions; for the
-seeded inputs here that does not reach the fp32 rounding of 1/rms.
+fp32 products, fp32 quotient by the scale).  The only freedom is the order
+of the fp64 additions, so codes and scales must match bit for bit except in
+a row whose fp64 1/rms (from the oracle) lies within the summation-order
+bound of an fp32 rounding midpoint: such a row accepts either rounding.
 
-SiLU-and-mul: the kernel's fp32 y (small problems: hardware exp2 with a
-corrected argument and a corrected division, about 1.5 ulp; large problems:
-a correctly rounded sigmoid table times the exact g u, within an ulp) can
-differ from the oracle's once-rounded double, so a result is accepted
-when every scale is within 2 ulp of the oracle's (and most are identical)
-and every code equals the oracle's or is its neighbour, with neighbours in
-at most 1e-4 of the positions (codes flip only next to a rounding midpoint).
+SiLU-and-mul: the kernel's y is the float32 rounding of a float64 value
+within 2^-51 of silu(g) u (exact g u times a correctly rounded float64
+logistic table); the oracle rounds its own float64 value once.  Codes and
+scales must match bit for bit, except in a group holding a value whose
+oracle float64 lies within 2^-48 of a float32 rounding midpoint: such a
+group accepts the oracle's group rule applied with either rounding of that
+value.  The count of such values is printed and bounded.
 """
 import numpy as np
 import pytest
@@ -23,6 +24,7 @@ import oracle
 from fp8_blockwise_quantized_token_amd import synth
 
 from gpu_common import dev, host, say, to_dev, to_dev_bf16
+from near_midpoint import assert_groups_match, assert_rms_rows_match
 
 pytestmark = pytest.mark.gpu
 
@@ -52,17 +54,23 @@ def _assert_exact(q, s, rq, rs, what):
         raise AssertionError((what, "codes", [(tuple(i), q[tuple(i)], rq[tuple(i)]) for i in bad]))
 
 
-def _assert_near(q, s, rq, rs, what, max_flip=1e-4):
-    rel = np.abs(s.astype(np.float64) - rs) / rs
-    assert np.all(rel <= 2.0 ** -22), (what, "scale off by more than 2 ulp", float(rel.max()))
-    if s.size >= 64:  # no systematic offset: most scales are identical
-        assert np.mean(s == rs) > 0.5, (what, "too few identical scales", float(np.mean(s == rs)))
-    diff = q != rq
-    if diff.any():
-        same_sign = (q & 0x80) == (rq & 0x80)
-        step = np.abs((q & 0x7F).astype(np.int32) - (rq & 0x7F).astype(np.int32))
-        assert np.all(same_sign & (step <= 1)), (what, "a code differs by more than one step")
-        assert np.mean(diff) <= max_flip, (what, "too many neighbouring codes", float(np.mean(diff)))
+def _assert_silu(q, s, x, what, eps=EPS, ue8m0=False, max_flag_rate=1e-5):
+    """Exact parity with the oracle up to near-midpoint values (see above)."""
+    y64 = oracle.silu_and_mul_values(x)
+    n = assert_groups_match(q, s, y64, lambda y32: oracle.group_quant_f32(y32, eps=eps, ue8m0=ue8m0), what,
+                            max_flag_rate=max_flag_rate)
+    say("  near-midpoint values:", n, "of", y64.size)
+    return n
+
+
+def _assert_rms(q, s, x, w, eps_norm, what, eps=EPS, ue8m0=False):
+    """Exact parity with the oracle up to rows whose 1/rms is next to a midpoint."""
+    r64 = oracle.rms_norm_inv_rms(x, eps_norm=eps_norm)
+    n = assert_rms_rows_match(q, s, r64, lambda rows, r32: oracle.rms_norm_apply(x[rows], w, r32, eps=eps,
+                                                                                   ue8m0=ue8m0), what)
+    if n:
+        say("  rows with 1/rms next to a midpoint:", n, "of", x.shape[0])
+    return n
 
 
 # ----------------------------------------------------------------- RMSNorm
@@ -87,8 +95,7 @@ def test_rms_norm_quant_matches_oracle(M, H):
     for ue8m0 in (False, True):
         say("rms_norm_per_block_quant", M, H, "ue8m0" if ue8m0 else "fp32")
         q, s = _gpu_rms(x, w, 1e-6, ue8m0)
-        rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6, ue8m0=ue8m0)
-        _assert_exact(q, s, rq, rs, (M, H, ue8m0))
+        _assert_rms(q, s, x, w, 1e-6, (M, H, ue8m0), ue8m0=ue8m0)
 
 
 @pytest.mark.parametrize("M,H", [(8192, 4096), (4096, 5120), (16384, 2048)])
@@ -98,8 +105,7 @@ def test_rms_norm_quant_full_size(M, H):
     w = synth.norm_weight_f32(H)
     say("rms_norm_per_block_quant full size", M, H)
     q, s = _gpu_rms(x, w, 1e-6, False)
-    rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6)
-    _assert_exact(q, s, rq, rs, (M, H))
+    _assert_rms(q, s, x, w, 1e-6, (M, H))
 
 
 def test_rms_norm_quant_edge_rows():
@@ -121,8 +127,7 @@ def test_rms_norm_quant_edge_rows():
                 xs, wn = x, w
             say("rms edge rows", eps_norm, ue8m0)
             q, s = _gpu_rms(xs, wn, eps_norm, ue8m0)
-            rq, rs = oracle.rms_norm_per_block_quant(xs, wn, eps_norm=eps_norm, ue8m0=ue8m0)
-            _assert_exact(q, s, rq, rs, ("edge", eps_norm, ue8m0))
+            _assert_rms(q, s, xs, wn, eps_norm, ("edge", eps_norm, ue8m0), ue8m0=ue8m0)
     # M = 0 is a no-op
     q, s = fb.rms_norm_quant(torch.empty((0, H), dtype=torch.bfloat16, device=dev()), to_dev(w))
     assert q.shape == (0, H)
@@ -142,9 +147,8 @@ def test_rms_norm_quant_smallest_eps(M, H):
     for ue8m0 in (False, True):
         say("rms smallest eps", M, H, ue8m0)
         q, s = fb.rms_norm_quant(to_dev_bf16(x), to_dev(w), eps_norm=1e-6, eps=float(eps), ue8m0=ue8m0)
-        rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=1e-6, eps=eps, ue8m0=ue8m0)
-        _assert_exact(host(q), host(s), rq, rs, ("smallest eps", M, H, ue8m0))
-        assert rs[0, 0] == (np.float32(2.0 ** -88) if ue8m0 else eps / np.float32(448))
+        _assert_rms(host(q), host(s), x, w, 1e-6, ("smallest eps", M, H, ue8m0), eps=eps, ue8m0=ue8m0)
+        assert host(s)[0, 0] == (np.float32(2.0 ** -88) if ue8m0 else eps / np.float32(448))
 
 
 def test_rms_norm_quant_strided_formats_and_padding():
@@ -157,8 +161,6 @@ def test_rms_norm_quant_strided_formats_and_padding():
     big[:, :H] = x
     xd = to_dev_bf16(big)[:, :H]
     wd = to_dev(w)
-    rq, rs = oracle.rms_norm_per_block_quant(x, w, ue8m0=True)
-    e8 = (rs.view(np.uint32) >> 23).astype(np.uint8)
     for e8m0 in (False, True):
         for mn in (False, True):
             say("rms strided", "e8m0" if e8m0 else "fp32", "mn" if mn else "row")
@@ -169,9 +171,10 @@ def test_rms_norm_quant_strided_formats_and_padding():
             fb.fp8_rms_norm_per_block_quant(xd, wd, q[:, :H], sv, ue8m0=True, scale_e8m0=e8m0,
                                             scale_mn_major=mn)
             qh, sh = host(q), host(s)
-            assert np.array_equal(qh[:, :H], rq) and np.all(qh[:, H:] == 0xAB)
+            assert np.all(qh[:, H:] == 0xAB)
             got = sh[:, :M].T if mn else sh[:, :G]
-            assert np.array_equal(got, e8 if e8m0 else rs)
+            got_f = ((got.astype(np.uint32) << 23).view(np.float32)) if e8m0 else got
+            _assert_rms(qh[:, :H], np.ascontiguousarray(got_f), x, w, 1e-6, ("strided", e8m0, mn), ue8m0=True)
             assert np.all((sh[:, M:] if mn else sh[:, G:]) == (0x5A if e8m0 else -1.0))
 
 
@@ -186,12 +189,7 @@ def test_silu_and_mul_quant_matches_oracle(M, I):
     for ue8m0 in (False, True):
         say("silu_and_mul_per_block_quant", M, I, "ue8m0" if ue8m0 else "fp32")
         q, s = _gpu_silu(x, ue8m0)
-        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
-        # power-of-two scales: the ceiling absorbs the few-ulp differences
-        if ue8m0:
-            assert np.array_equal(s, rs)
-        # tiny cases: a single flip would exceed the rate bound, allow one
-        _assert_near(q, s, rq, rs, (M, I, ue8m0), max_flip=max(1e-4, 1.0 / q.size))
+        _assert_silu(q, s, x, (M, I, ue8m0), ue8m0=ue8m0)
 
 
 @pytest.mark.parametrize("M,I", [(8192, 12288), (4096, 25600)])
@@ -199,9 +197,9 @@ def test_silu_and_mul_quant_full_size(M, I):
     # Qwen3-8B / 32B intermediate sizes at prefill token counts
     x = _x(M, 2 * I, 3)
     say("silu_and_mul_per_block_quant full size", M, I)
-    q, s = _gpu_silu(x, False)
-    rq, rs = oracle.silu_and_mul_per_block_quant(x)
-    _assert_near(q, s, rq, rs, (M, I))
+    for ue8m0 in (False, True):
+        q, s = _gpu_silu(x, ue8m0)
+        _assert_silu(q, s, x, (M, I, ue8m0), ue8m0=ue8m0)
 
 
 def test_silu_and_mul_quant_special_gates():
@@ -221,6 +219,7 @@ def test_silu_and_mul_quant_special_gates():
         q, s = _gpu_silu(x, ue8m0)
         rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
         _assert_exact(q, s, rq, rs, ("special", ue8m0))
+        assert _assert_silu(q, s, x, ("special", ue8m0), ue8m0=ue8m0) == 0
 
 
 @pytest.mark.parametrize("M,I", [(4, 1024), (600, 12288)])
@@ -240,9 +239,7 @@ def test_silu_and_mul_quant_smallest_eps(M, I):
         rq, rs = oracle.silu_and_mul_per_block_quant(x, eps=eps, ue8m0=ue8m0)
         q, s = host(q), host(s)
         assert np.all(s[0] == rs[0]) and np.all(q[0] == rq[0])  # zero groups: exact
-        if ue8m0:
-            assert np.array_equal(s, rs)
-        _assert_near(q, s, rq, rs, ("silu smallest eps", M, I, ue8m0), max_flip=max(1e-4, 1.0 / q.size))
+        _assert_silu(q, s, x, ("silu smallest eps", M, I, ue8m0), eps=eps, ue8m0=ue8m0)
         assert np.all(rs[1 % M] < np.float32(2.0 ** -75))
 
 
@@ -268,7 +265,7 @@ def test_silu_and_mul_quant_strided_formats_and_padding():
             assert np.all(qh[:, I:] == 0xAB)
             got = sh[:, :M].T if mn else sh[:, :G]
             got_f = ((got.astype(np.uint32) << 23).view(np.float32)) if e8m0 else got
-            _assert_near(qh[:, :I], got_f, rq, rs, ("strided", e8m0, mn), max_flip=1e-3)
+            _assert_silu(qh[:, :I], np.ascontiguousarray(got_f), x, ("strided", e8m0, mn), ue8m0=True)
             assert np.all((sh[:, M:] if mn else sh[:, G:]) == (0x5A if e8m0 else -1.0))
 
 
@@ -282,11 +279,15 @@ def test_silu_and_mul_quant_table_path_all_gate_ranges():
     gate[:, ::97] = 0.0
     up = gen.standard_normal((M, I)).astype(np.float32)
     x = synth.to_bf16_bits(np.concatenate([gate, up], axis=1))
+    # Gates of 2^-24 .. 2^-16 make exact ties common: there silu(g) u is
+    # g u / 2 + g^2 u / 4 up to a relative g^2 / 12, and both terms have few
+    # significant bits, so the value often lies within about 2^-70 of a float32
+    # midpoint, closer than either float64 evaluation can resolve.  Those
+    # values are flagged (about 2.4e-4 of this input) and accept either rounding.
     for ue8m0 in (False, True):
         say("silu table path, all gate ranges", M, I, ue8m0)
         q, s = _gpu_silu(x, ue8m0)
-        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
-        _assert_near(q, s, rq, rs, ("table path", ue8m0))
+        _assert_silu(q, s, x, ("table path", ue8m0), ue8m0=ue8m0, max_flag_rate=1e-3)
 
 
 def test_silu_and_mul_quant_row_chunks_with_a_wide_pitch():
@@ -305,8 +306,7 @@ def test_silu_and_mul_quant_row_chunks_with_a_wide_pitch():
         say("silu wide pitch, chunked rows", M, I, pitch, ue8m0)
         q, s = fb.silu_and_mul_quant(xd, ue8m0=ue8m0)
         q, s = host(q), host(s)
-        rq, rs = oracle.silu_and_mul_per_block_quant(x, ue8m0=ue8m0)
-        _assert_near(q, s, rq, rs, ("wide pitch", ue8m0), max_flip=1.0 / q.size)
+        _assert_silu(q, s, x, ("wide pitch", ue8m0), ue8m0=ue8m0)
     del big
     torch.cuda.empty_cache()
 
@@ -339,13 +339,13 @@ def test_producers_feed_the_block_gemm(M):
     y = fb.block_gemm(qh, shh, to_dev(qdn), to_dev(sdn))
     # oracle chain
     rqa, rsa = oracle.rms_norm_per_block_quant(x, w_norm)
-    _assert_exact(host(qa), host(sa), rqa, rsa, ("mlp rmsnorm", M))
+    _assert_rms(host(qa), host(sa), x, w_norm, 1e-6, ("mlp rmsnorm", M))
     rows = sample_rows(M, 8, key=M)
     h_ref = oracle.block_gemm(rqa, rsa, qgu, sgu, rows=rows)
     assert_close(host(h)[rows].astype(np.float64), h_ref, "gate_up")
     # the library's own bf16 h (within tolerance of the oracle) feeds both sides
     hb = h.view(torch.int16).cpu().numpy().view(np.uint16)
     rqh, rsh = oracle.silu_and_mul_per_block_quant(hb)
-    _assert_near(host(qh), host(shh), rqh, rsh, ("mlp silu", M), max_flip=max(1e-4, 2.0 / rqh.size))
+    _assert_silu(host(qh), host(shh), hb, ("mlp silu", M))
     y_ref = oracle.block_gemm(host(qh), host(shh), qdn, sdn, rows=rows)
     assert_close(host(y)[rows].astype(np.float64), y_ref, "down")
