@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
   fp8_block_gemm         blockwise-scaled FP8 GEMM, bf16 out
   fp8_linear_workspace_size
   fp8_linear             the whole layer (quantize x, then the GEMM; fused for Swap-AB)
+  fp8_linear_noalloc     fp8_linear with the library's per-GPU scratch array as workspace
   fp8_token_quant        per-token quantization (FP8_Dynamic activations)
   fp8_weight_channel_quant  per-channel weight quantization (FP8_Dynamic weights)
   fp8_scaled_mm          GEMM with per-token / per-channel scales
@@ -119,6 +120,9 @@ def lib() -> ctypes.CDLL:
     L.fp8_linear.restype = ctypes.c_int
     L.fp8_linear.argtypes = [P, I64, P, P, I64, I64, P, I64, I64, I64, I64, F, U32,
                              ctypes.POINTER(GemmConfig), P, I64, P]
+    L.fp8_linear_noalloc.restype = ctypes.c_int
+    L.fp8_linear_noalloc.argtypes = [P, I64, P, P, I64, I64, P, I64, I64, I64, I64, F, U32,
+                                     ctypes.POINTER(GemmConfig), P]
     L.fp8_rms_norm_per_block_quant.restype = ctypes.c_int
     L.fp8_rms_norm_per_block_quant.argtypes = [P, I64, I64, I64, P, F, P, I64, P, I64, F, U32, P]
     L.fp8_silu_and_mul_per_block_quant.restype = ctypes.c_int
@@ -302,6 +306,24 @@ def fp8_linear(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
                           ctypes.byref(cfg) if cfg is not None else None,
                           ws_ptr, ws_bytes, _stream(stream))
     _check(st, "fp8_linear")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FP8BLK_NOALLOC_SCRATCH_BYTES
+
+
+def fp8_linear_noalloc(x, w, sw, y, eps: float = DEFAULT_EPS, ue8m0: bool = False,
+                       cfg: GemmConfig | None = None, stream=None, weight_pow2: bool = False) -> None:
+    """fp8_linear without a workspace: the library's own per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES) stands in for it; calls on one GPU must not overlap."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or y.shape != (M, N) or x.element_size() != 2:
+        raise ValueError("fp8_linear_noalloc: shape/dtype mismatch")
+    st = lib().fp8_linear_noalloc(x.data_ptr(), _ld(x, "x"), w.data_ptr(), sw.data_ptr(), _ld(w, "w"),
+                                  _ld(sw, "sw"), y.data_ptr(), _ld(y, "y"), M, N, K, eps,
+                                  (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_WEIGHT_POW2 if weight_pow2 else 0),
+                                  ctypes.byref(cfg) if cfg is not None else None, _stream(stream))
+    _check(st, "fp8_linear_noalloc")
 
 
 def fp8_token_quant(x, q, s, eps: float = DEFAULT_EPS, ue8m0: bool = False, stream=None) -> None:

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fp8blk.h"
 #include "dispatch.hpp"
 #include "launch.hpp"
@@ -104,6 +106,109 @@ int check_quant_args(float eps, uint32_t flags) {
   if ((flags & ~FP8BLK_FLAG_UE8M0) != 0) return FP8BLK_ERR_BAD_CONFIG;
   return FP8BLK_OK;
 }
+
+// ---- the scratch array of fp8_linear_noalloc ----
+// One array per GPU, allocated with the code object and held until the
+// process ends.  In host code its name is only a stand-in: the device
+// address is looked up once per device (hipGetSymbolAddress with that device
+// current) and used instead everywhere.
+constexpr int64_t kScratchBytes = int64_t(FP8BLK_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[FP8BLK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> scratch_ptr[kMaxDevices];  // device address per device id (nullptr: not looked up yet)
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8BLK_ERR_HIP;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP8BLK_ERR_HIP;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FP8BLK_OK;
+}
+
+// fp8_linear's work for both of its entry points.  from_scratch: the
+// workspace is this device's scratch array (fp8_linear_noalloc), looked up
+// after the arguments are validated and the size is checked against it.
+int linear_call(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw, int64_t ldw,
+                int64_t ldsw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, float eps,
+                uint32_t flags, const fp8blk_gemm_config* cfg, void* workspace, int64_t workspace_bytes,
+                bool from_scratch, void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st != FP8BLK_OK) return st;
+  if (K > kMaxK) return FP8BLK_ERR_BAD_SHAPE;
+  st = check_quant_args(eps, flags & ~FP8BLK_FLAG_WEIGHT_POW2);
+  if (st != FP8BLK_OK) return st;
+  fp8blk_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    fp8blk::select_config(M, N, K, flags, &c);
+  }
+  st = check_config(c, M, N, K);
+  if (st != FP8BLK_OK) return st;
+  // the matrix core keeps only the exponent bits of every scale: both the
+  // quantizer's scales and the caller's weight scales must be powers of two
+  const uint32_t pow2_flags = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2;
+  if (c.scale_mode == FP8BLK_SCALES_POW2 && (flags & pow2_flags) != pow2_flags) return FP8BLK_ERR_BAD_CONFIG;
+  if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (ldw >= kMaxPitch || ldsw * 4 >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
+  const LinearLayout L = linear_layout(c, M, N, K);
+  if (from_scratch) {
+    if (L.total > kScratchBytes) return FP8BLK_ERR_WORKSPACE;
+    st = scratch_of_current_device(&workspace);
+    if (st != FP8BLK_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned4(sw) || (ldx * 2) % 16 != 0 ||
+      ldw % 16 != 0 || (ldy * 2) % 16 != 0)
+    return FP8BLK_ERR_MISALIGNED;
+  if (L.total > 0) {
+    if (!workspace || workspace_bytes < L.total) return FP8BLK_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
+  }
+  const bool ue8m0 = (flags & FP8BLK_FLAG_UE8M0) != 0;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)workspace;
+  fp8blk::GemmArgs g{};
+  g.w = w;
+  g.sw = sw;
+  g.ldw = ldw;
+  g.ldsw = ldsw;
+  g.y = y;
+  g.ldy = ldy;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ws = c.split_k > 1 ? (float*)(base + L.ws_off) : nullptr;
+  if (L.fused) {
+    g.x = x;
+    g.ldx = ldx;
+    g.eps = eps;
+    g.ue8m0 = ue8m0 ? 1 : 0;
+    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
+  }
+  uint8_t* q = (uint8_t*)(base + L.q_off);
+  float* sc = (float*)(base + L.s_off);
+  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, 0, s);
+  if (e != hipSuccess) return FP8BLK_ERR_HIP;
+  g.a = q;
+  g.sa = sc;
+  g.lda = K;
+  g.ldsa = K / kG;
+  if (c.variant == FP8BLK_SWAPAB)
+    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
+                                                c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
+                                                                                       : fp8blk::kScalesBlock,
+                                                  s));
+}
+
 
 }  // namespace
 
@@ -261,70 +366,14 @@ int fp8_linear(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw
                int64_t ldsw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, float eps,
                uint32_t flags, const fp8blk_gemm_config* cfg, void* workspace,
                int64_t workspace_bytes, void* stream) {
-  int st = check_gemm_shape(M, N, K);
-  if (st != FP8BLK_OK) return st;
-  if (K > kMaxK) return FP8BLK_ERR_BAD_SHAPE;
-  st = check_quant_args(eps, flags & ~FP8BLK_FLAG_WEIGHT_POW2);
-  if (st != FP8BLK_OK) return st;
-  fp8blk_gemm_config c;
-  if (cfg) {
-    c = *cfg;
-  } else {
-    fp8blk::select_config(M, N, K, flags, &c);
-  }
-  st = check_config(c, M, N, K);
-  if (st != FP8BLK_OK) return st;
-  // the matrix core keeps only the exponent bits of every scale: both the
-  // quantizer's scales and the caller's weight scales must be powers of two
-  const uint32_t pow2_flags = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2;
-  if (c.scale_mode == FP8BLK_SCALES_POW2 && (flags & pow2_flags) != pow2_flags) return FP8BLK_ERR_BAD_CONFIG;
-  if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
-  if (ldw >= kMaxPitch || ldsw * 4 >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
-  if (M == 0) return FP8BLK_OK;
-  if (!x || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned4(sw) || (ldx * 2) % 16 != 0 ||
-      ldw % 16 != 0 || (ldy * 2) % 16 != 0)
-    return FP8BLK_ERR_MISALIGNED;
-  const LinearLayout L = linear_layout(c, M, N, K);
-  if (L.total > 0) {
-    if (!workspace || workspace_bytes < L.total) return FP8BLK_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
-  }
-  const bool ue8m0 = (flags & FP8BLK_FLAG_UE8M0) != 0;
-  hipStream_t s = (hipStream_t)stream;
-  char* base = (char*)workspace;
-  fp8blk::GemmArgs g{};
-  g.w = w;
-  g.sw = sw;
-  g.ldw = ldw;
-  g.ldsw = ldsw;
-  g.y = y;
-  g.ldy = ldy;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.ws = c.split_k > 1 ? (float*)(base + L.ws_off) : nullptr;
-  if (L.fused) {
-    g.x = x;
-    g.ldx = ldx;
-    g.eps = eps;
-    g.ue8m0 = ue8m0 ? 1 : 0;
-    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
-  }
-  uint8_t* q = (uint8_t*)(base + L.q_off);
-  float* sc = (float*)(base + L.s_off);
-  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, 0, s);
-  if (e != hipSuccess) return FP8BLK_ERR_HIP;
-  g.a = q;
-  g.sa = sc;
-  g.lda = K;
-  g.ldsa = K / kG;
-  if (c.variant == FP8BLK_SWAPAB)
-    return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
-  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
-                                                c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
-                                                                                       : fp8blk::kScalesBlock,
-                                                  s));
+  return linear_call(x, ldx, w, sw, ldw, ldsw, y, ldy, M, N, K, eps, flags, cfg, workspace, workspace_bytes,
+                     false, stream);
+}
+
+int fp8_linear_noalloc(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* sw, int64_t ldw,
+                       int64_t ldsw, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, float eps,
+                       uint32_t flags, const fp8blk_gemm_config* cfg, void* stream) {
+  return linear_call(x, ldx, w, sw, ldw, ldsw, y, ldy, M, N, K, eps, flags, cfg, nullptr, 0, true, stream);
 }
 
 int fp8_token_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,

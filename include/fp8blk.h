@@ -279,6 +279,35 @@ int fp8_linear(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw
                int64_t workspace_bytes, void *stream);
 
 /*
+ * fp8_linear without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that may not
+ * call hipMalloc, harnesses that forbid allocation.  Same arguments (minus
+ * the workspace), results and configuration choice as fp8_linear.  The
+ * workspace is instead a scratch array of FP8BLK_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds on every GPU it runs on until the process
+ * ends; nothing is allocated, freed or synchronized by the call.
+ *   - A call whose workspace need (fp8_linear_workspace_size for the same
+ *     M, N, K and configuration) exceeds that size returns
+ *     FP8BLK_ERR_WORKSPACE with nothing launched.  Every dispatched
+ *     configuration of the tabled Qwen3 shapes up to M = 256 fits (decode
+ *     M <= 64 needs at most 12.3 MiB); large prefill calls generally do not.
+ *   - The array is shared by every call on one GPU and keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that may
+ *     overlap on one GPU (several streams or host threads) race on it and
+ *     must be serialized by the caller.
+ *   - The first call on a device looks up the array's device address there
+ *     (with that device current; no stream work).  A call with M = 0 does
+ *     only that and returns FP8BLK_OK, so one such call per device before a
+ *     graph capture keeps the lookup out of the capture.  FP8BLK_ERR_HIP if
+ *     the lookup fails.
+ */
+#define FP8BLK_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fp8_linear_noalloc(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw,
+                       int64_t ldw, int64_t ldsw, uint16_t *y, int64_t ldy, int64_t M,
+                       int64_t N, int64_t K, float eps, uint32_t flags,
+                       const fp8blk_gemm_config *cfg, void *stream);
+
+/*
  * FP8_Dynamic: per-token activation scales and per-channel weight scales
  * (autotuning page, "Helion Linear Backend" / "Scope": the first of its
  * three formats).  Quantizer dynamic_per_token_scaled_fp8_quant and GEMM

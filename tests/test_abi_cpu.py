@@ -392,3 +392,25 @@ def test_fused_producer_argument_errors():
     assert sq(lds=1) == STRIDE and sq(flags=4, lds=3) == STRIDE
     assert sq(x=A + 2) == MISAL and sq(ldx=516) == MISAL and sq(s=C + 2) == MISAL
     assert sq(M=0, x=None, q=None, s=None) == OK
+
+
+def test_linear_noalloc_argument_errors():
+    # every argument error, and a workspace need beyond the library's scratch
+    # array, is reported before the array is looked up or anything launched
+    L = fb.lib()
+
+    def f(M=8, N=256, K=256, ldx=None, cfg=None, flags=0):
+        ldx = K if ldx is None else ldx
+        return L.fp8_linear_noalloc(A, ldx, C, D, K, K // 128, E, N, M, N, K, 1e-10, flags,
+                                    ctypes.byref(cfg) if cfg is not None else None, None)
+    assert f(K=200) == SHAPE and f(N=200) == SHAPE and f(M=-1) == SHAPE
+    assert f(ldx=128) == STRIDE
+    assert f(flags=16) == CFG
+    assert f(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=fb.SCALES_POW2), flags=fb.FLAG_UE8M0) == CFG
+    assert f(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2), M=17) == CFG
+    M, N, K = 16384, 4096, 12288
+    assert fb.fp8_linear_workspace_size(M, N, K, None) > fb.NOALLOC_SCRATCH_BYTES
+    assert f(M=M, N=N, K=K) == WS
+    big = fb.make_config(fb.STANDARD, 64, 128, split_k=8)
+    assert fb.fp8_linear_workspace_size(4096, 4096, 4096, big) > fb.NOALLOC_SCRATCH_BYTES
+    assert f(M=4096, N=4096, K=4096, cfg=big) == WS
