@@ -122,6 +122,96 @@ def traffic_from_profiles(symbol: str):
     return ent.get("bytes_per_launch")
 
 
+ROTATE_BYTES = 1 << 30  # bytes each timing cycle touches: four times the Infinity Cache
+TRIALS = 5
+
+
+def rotation_copies(copies, nbytes: int, dev, limit: int = 64):
+    """At least ROTATE_BYTES / nbytes (at most limit, at least len(copies))
+    device copies of an operand, made by cloning the given ones in turn."""
+    want = min(limit, max(len(copies), -(-ROTATE_BYTES // max(nbytes, 1))))
+    out = list(copies)
+    i = 0
+    while len(out) < want:
+        out.append(tuple(t.clone() for t in copies[i % len(copies)]))
+        i += 1
+    return out
+
+
+def graph_time(stream, launches) -> float:
+    """Median over TRIALS replays of one captured graph of the given launches,
+    seconds per launch (HIP events on the launch stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for fn in launches:
+            fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    with torch.cuda.stream(stream):
+        g.replay()
+        for _ in range(TRIALS):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3 / len(launches))
+    del g
+    times.sort()
+    return times[len(times) // 2]
+
+
+def extra_measurements(stream, dev):
+    """Two figures beside the step, each timed like the per-case ones:
+    the UE8M0 Qwen3-32B layers at M = 4096 (power-of-two scales applied by
+    the matrix core) and the standalone quantizer at M = 16384 x K in
+    {12288, 25600} from the wide sweep."""
+    import numpy as np
+    import torch
+    import fp8_blockwise_quantized_token_amd as fb
+    from fp8_blockwise_quantized_token_amd import synth
+
+    out = {"ue8m0_32b_m4096": [], "quant_m16384": []}
+    flags = fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2
+    for c in synth.cases("ue8m0_32b"):
+        if c.M != 4096:
+            continue
+        w = torch.from_numpy(synth.weights_f32(c.N, c.K)).to(dev)
+        qw, sw = fb.quantize_weight(w, ue8m0=True, stream=stream)
+        del w
+        x = torch.from_numpy(synth.activations_bf16(c).view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, flags)
+        ws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
+        stream.synchronize()
+        wc = rotation_copies([(qw, sw)], c.N * c.K, dev)
+        t = graph_time(stream, [lambda r=r: fb.fp8_linear(x, wc[r % len(wc)][0], wc[r % len(wc)][1], y,
+                                                          ue8m0=True, cfg=cfg, workspace=ws, stream=stream,
+                                                          weight_pow2=True)
+                                for r in range(max(len(wc), 8))])
+        tf = c.flops() / t / 1e12
+        out["ue8m0_32b_m4096"].append({"case": c.cid, "cfg": cfg.as_dict(), "linear_us": round(t * 1e6, 2),
+                                       "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4)})
+        print(f"[bench] {c.cid}: {t * 1e6:.1f} us, {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        del x, y, ws, wc, qw, sw
+    for c in synth.cases("sweep"):
+        if c.M != 16384 or c.K not in (12288, 25600) or c.N not in (4096, 5120):
+            continue
+        x = torch.from_numpy(synth.activations_bf16(c).view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
+        s = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
+        xc = rotation_copies([(x,)], 2 * c.M * c.K, dev)
+        t = graph_time(stream, [lambda r=r: fb.fp8_group_quant(xc[r % len(xc)][0], q, s, stream=stream)
+                                for r in range(max(len(xc), 4))])
+        gbps = quant_bytes(c) / t / 1e9
+        out["quant_m16384"].append({"M": c.M, "K": c.K, "us": round(t * 1e6, 2), "gbps": round(gbps, 1),
+                                    "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)})
+        print(f"[bench] quant {c.M}x{c.K}: {t * 1e6:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        del x, q, s, xc
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cases, xs, budget_s: float, dynamic: bool = False):
     """The oracle (untuned) on a bounded sample: every case's quantization and
     fp64 GEMM on its first rows, doubling the rows until one pass takes
@@ -210,7 +300,6 @@ def bench_producers(args) -> int:
                 fn = (lambda x=x, q=q, s=s: fb.fp8_silu_and_mul_per_block_quant(x, q, s, stream=stream))
             cases.append((op, M, xh, fn))
     torch.cuda.synchronize()
-    reps = max(args.kernel_reps, 10)
     rows = []
     tot_b = tot_t = 0.0
     for op, M, _, fn in cases:
@@ -218,19 +307,12 @@ def bench_producers(args) -> int:
             for _ in range(args.warmup):
                 fn()
         stream.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for _ in range(reps):
-                fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            g.replay()
-            e0.record(stream)
-            for _ in range(args.steps):
-                g.replay()
-            e1.record(stream)
-        stream.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / (args.steps * reps)
+        # rotate over copies of x so that every cycle reads >= 1 GiB
+        x0 = fn.__defaults__[0]
+        xs_rot = rotation_copies([(x0,)], x0.numel() * 2, dev)
+        t = graph_time(stream, [lambda r=r: fn(x=xs_rot[r % len(xs_rot)][0])
+                                for r in range(max(len(xs_rot), args.kernel_reps))])
+        del xs_rot
         b = producer_bytes(op, M)
         tot_b += b
         tot_t += t
@@ -243,7 +325,8 @@ def bench_producers(args) -> int:
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16-in/fp32-compute/e4m3-out", "data": "synthetic (seeded)",
            "config": {"workload": "producers_qwen3_8b", "H": PRODUCER_H, "I": PRODUCER_I,
-                      "m_values": list(PRODUCER_M), "graph_replay": True, "launches_per_graph": reps},
+                      "m_values": list(PRODUCER_M), "graph_replay": True,
+                      "timing": "graph replays rotating >= 1 GiB of input copies, median of 5"},
            "roofline": [{"bound": "hbm", "op": r["op"], "kernel": PRODUCER_SYMBOLS[r["op"]],
                          "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": r["hbm_frac"], "avg_launch_us": r["us"],
@@ -278,6 +361,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the UE8M0 32B M=4096 layers and the M=16384 quantizer figures")
     ap.add_argument("--format", choices=("block", "dynamic"), default="block",
                     help="block: Block_FP8 (1x128 / 128x128 scales, the default); "
                          "dynamic: FP8_Dynamic (per-token / per-channel scales)")
@@ -347,24 +432,27 @@ def main() -> int:
                          and (cfg.tile_m <= 32 or (cfg.tile_m == 64 and cfg.tile_n == 16))))
     torch.cuda.synchronize()
 
-    def quant(b):
+    def quant(b, x=None):
+        x = b["x"] if x is None else x
         if dynamic:
-            fb.fp8_token_quant(b["x"], b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+            fb.fp8_token_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
         else:
-            fb.fp8_group_quant(b["x"], b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+            fb.fp8_group_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
 
-    def gemm(b):
+    def gemm(b, w=None):
+        qw, sw = (b["qw"], b["sw"]) if w is None else w
         if dynamic:
-            fb.fp8_scaled_mm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+            fb.fp8_scaled_mm(b["qa"], b["sa"], qw, sw, b["y"], b["cfg"], b["ws"], stream=stream)
         else:
-            fb.fp8_block_gemm(b["qa"], b["sa"], b["qw"], b["sw"], b["y"], b["cfg"], b["ws"], stream=stream)
+            fb.fp8_block_gemm(b["qa"], b["sa"], qw, sw, b["y"], b["cfg"], b["ws"], stream=stream)
 
-    def linear(b):
+    def linear(b, w=None):
+        qw, sw = (b["qw"], b["sw"]) if w is None else w
         if dynamic:  # FP8_Dynamic: per-token quantization, then scaled_mm
             quant(b)
-            gemm(b)
+            fb.fp8_scaled_mm(b["qa"], b["sa"], qw, sw, b["y"], b["cfg"], b["ws"], stream=stream)
         else:
-            fb.fp8_linear(b["x"], b["qw"], b["sw"], b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
+            fb.fp8_linear(b["x"], qw, sw, b["y"], ue8m0=b["case"].ue8m0, cfg=b["cfg"],
                           workspace=b["lws"], stream=stream, weight_pow2=b["case"].ue8m0)
 
     def step():
@@ -404,33 +492,33 @@ def main() -> int:
     total_flops = sum(b["case"].flops() for b in bufs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-case and per-kernel durations (HIP events on the launch stream) ----
-    # quant: fp8_group_quant alone; gemm: the GEMM kernel of the step's call
-    # (fused Swap-AB: fp8_linear itself; Standard: fp8_block_gemm on the
-    # quantized input; a split-K call includes its reduce kernel); linear:
-    # the step's fp8_linear call.
-    reps = args.kernel_reps
-
-    def timed(fn):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            fn()
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-        stream.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e-3
-
+    # ---- per-case and per-kernel durations ----
+    # Every case is timed from a captured graph of launches replayed TRIALS
+    # times (median), HIP events on the launch stream.  The launches rotate
+    # over enough copies of the weight (and, for the quantizer, of X) that
+    # each cycle touches at least ROTATE_BYTES, so no launch finds its
+    # operand in the 256 MB Infinity Cache.  quant: fp8_group_quant alone;
+    # gemm: the GEMM kernel of the step's call (fused Swap-AB: fp8_linear
+    # itself; otherwise fp8_block_gemm on the quantized input; a split-K call
+    # includes its reduce kernel); linear: the step's fp8_linear call.
     per_case = []
     sym_time = {}
     sym_work = {}
     for b in bufs:
         c = b["case"]
-        tq = timed(lambda: quant(b))
-        tl = timed(lambda: linear(b))
-        tg = tl if b["fused"] else timed(lambda: gemm(b))
+        wcopies = rotation_copies(wq[(c.N, c.K, c.ue8m0)], c.N * c.K, dev)
+        xcopies = rotation_copies([(b["x"],)], 2 * c.M * c.K, dev, limit=8)
+        nq = max(len(xcopies), 8)
+        tq = graph_time(stream, [lambda r=r: quant(b, x=xcopies[r % len(xcopies)][0]) for r in range(nq)])
+        lin = [lambda r=r: linear(b, w=wcopies[r % len(wcopies)]) for r in range(max(len(wcopies), 8))]
+        tl = graph_time(stream, lin)
+        if b["fused"]:
+            tg = tl
+        else:
+            quant(b)
+            tg = graph_time(stream, [lambda r=r: gemm(b, w=wcopies[r % len(wcopies)])
+                                     for r in range(max(len(wcopies), 8))])
+        del wcopies, xcopies
         fl = c.flops()
         gb = gemm_bytes(c, dynamic) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
         lb = gemm_bytes(c, dynamic) + quant_bytes(c, dynamic) if not b["fused"] else gb
@@ -448,8 +536,10 @@ def main() -> int:
             "gemm_tflops": round(fl / tg / 1e12, 2), "gemm_gbps": round(gb / tg / 1e9, 1),
             "gemm_roofline_frac": round(roof_t / tg, 4),
             "linear_tflops": round(fl / tl / 1e12, 2), "linear_gbps": round(lb / tl / 1e9, 1),
-            "quant_gbps": round(quant_bytes(c) / tq / 1e9, 1),
+            "quant_gbps": round(quant_bytes(c, dynamic) / tq / 1e9, 1),
         })
+        print(f"[bench] {c.cid}: linear {tl * 1e6:.2f} us, gemm {tg * 1e6:.2f} us, quant {tq * 1e6:.2f} us",
+              file=sys.stderr, flush=True)
 
     dom = max(sym_time, key=sym_time.get)
     dflops, dbytes, dlaunches, dsplit = sym_work[dom]
@@ -468,7 +558,9 @@ def main() -> int:
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic}
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
-    roof["launches_measured"] = dlaunches * reps
+    roof["launches_measured"] = dlaunches
+    roof["timing"] = ("HIP events over graph replays of back-to-back launches rotating >= 1 GiB of weight "
+                      "copies, median of 5")
     roof["algorithmic_per_launch"] = {"flop": flop_per_launch, "bytes": byte_per_launch}
     if dsplit:
         roof["note"] = "split-K calls: duration includes the reduce kernel"
@@ -509,6 +601,10 @@ def main() -> int:
         "cases": per_case,
         "wall_s_timed": round(t_wall, 3),
     }
+    if not args.no_extra and args.workload == "qwen3_8b" and not dynamic:
+        del bufs
+        torch.cuda.empty_cache()
+        out["extra"] = extra_measurements(stream, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cases, xs, args.cpu_budget, dynamic)

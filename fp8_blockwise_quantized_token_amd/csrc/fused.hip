@@ -343,14 +343,21 @@ constexpr int kSiluUnroll = 2;
 
 #include "sigmoid_table.inc"
 
-// silu(g) * u for the bf16 gate bits h (low 16 bits) and the gate and up
-// values widened to fp32.  The sign of a zero product is that of g u (a
-// multiplication by the positive s(g)).
-__device__ __forceinline__ float silu_mul64(uint32_t h, float g, float u, const double* tab) {
-  const int i = min(max((int)(h & 0x7FFFu) - kSigmoidBase, 0), kSigmoidSpan - 1);
-  const double t = tab[i];
-  const double sg = (h & 0x8000u) ? t : 1.0 - t;
-  return (float)(((double)g * (double)u) * sg);
+// silu(g) * u for the gate and up values widened to fp32 (gb: the gate's
+// fp32 bits).  With q = |g| u (exact in float64) and c = 1 for a positive
+// sign bit, 0 for a negative one: s(g) = c - t(|g|) for g > 0 and
+// -(c - t) = t for g < 0, so silu(g) u = g u s(g) = q (c - t) in both cases,
+// with one float64 subtraction (exact for g < 0), one product and one
+// rounding to fp32.  Signed zeros come out right as well: g = +0 gives
+// q (1 - 1/2), g = -0 gives q (0 - 1/2), i.e. the sign of g u.
+__device__ __forceinline__ float silu_mul64(uint32_t gb, float g, float u, const double* tab) {
+  const uint32_t mag = (gb >> 16) & 0x7FFFu;
+  const uint32_t i = min(max(mag, (uint32_t)kSigmoidBase), (uint32_t)(kSigmoidBase + kSigmoidSpan - 1));
+  const double t = tab[i - (uint32_t)kSigmoidBase];
+  const uint32_t c_hi = (int32_t)gb < 0 ? 0u : 0x3FF00000u;  // 1.0 or 0.0
+  const double c = __builtin_bit_cast(double, (uint64_t)c_hi << 32);
+  const double q = __builtin_fabs((double)g) * (double)u;
+  return (float)(q * (c - t));
 }
 
 // One iteration's inputs for kSiluUnroll groups per 16 lanes, with each
@@ -398,8 +405,9 @@ __device__ __forceinline__ void silu_compute_store(const SiluFrag& f, uint32_t b
     float y[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      y[2 * j] = silu_mul64(gc[j], bf16_lo(gc[j]), bf16_lo(uc[j]), tab);
-      y[2 * j + 1] = silu_mul64(gc[j] >> 16, bf16_hi(gc[j]), bf16_hi(uc[j]), tab);
+      const float g0 = bf16_lo(gc[j]), g1 = bf16_hi(gc[j]);
+      y[2 * j] = silu_mul64(__float_as_uint(g0), g0, bf16_lo(uc[j]), tab);
+      y[2 * j + 1] = silu_mul64(__float_as_uint(g1), g1, bf16_hi(uc[j]), tab);
     }
     float sc;
     const uint2 codes = quant8(y, eps, ue8m0 != 0, &sc);

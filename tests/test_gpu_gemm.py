@@ -138,32 +138,33 @@ def test_scaling_activations_by_two_doubles_output():
 
 
 def _full_cases():
-    out = list(synth.cases("single")) + list(synth.cases("decode_8b")) + \
-        list(synth.cases("prefill_8b")) + list(synth.cases("ue8m0_32b"))
-    for c in synth.cases("sweep"):
-        if c.M in (1, 64, 2048) or (c.M == 16384 and c.K == 25600) or (c.M == 16384 and c.N == 12288):
-            out.append(c)
+    """Every case of every workload: C1 single, C2 decode, C3 prefill, C4 the
+    UE8M0 32B layers and all 180 cases of the C5 sweep."""
+    out = []
+    for config in ("single", "decode_8b", "prefill_8b", "ue8m0_32b", "sweep"):
+        out += list(synth.cases(config))
     return out
 
 
 @pytest.mark.parametrize("case", _full_cases(), ids=lambda c: c.cid)
 def test_full_size_linear(case):
-    """The whole layer at full size in the dispatched configuration: GPU
-    activation quantization must equal the oracle's bytes; the GEMM is
-    compared with the oracle on sampled rows (every N tile and K block)."""
+    """fp8_linear -- the call the benchmark times -- at full size in the
+    dispatched configuration (UE8M0 cases with power-of-two activation and
+    weight scales, so Standard tiles scale in the matrix core), against the
+    oracle (its quantization of the same rows, then the fp64 GEMM) on sampled
+    rows: the first and last, one in every 256-row band and up to 254 more."""
     import torch
     x = synth.activations_bf16(case)
-    qa_ref, sa_ref = oracle.group_quant(x, ue8m0=case.ue8m0)
     qw, sw = oracle_weight(case.N, case.K, case.ue8m0)
-    say("full", case.cid, fb.fp8_block_gemm_select(case.M, case.N, case.K).as_dict())
-    xd = to_dev_bf16(x)
-    qa, sa = fb.quantize_activations(xd, ue8m0=case.ue8m0)
-    y = fb.block_gemm(qa, sa, to_dev(qw), to_dev(sw))
+    flags = (fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2) if case.ue8m0 else 0
+    say("full", case.cid, fb.fp8_block_gemm_select(case.M, case.N, case.K, flags).as_dict())
+    y = fb.linear(to_dev_bf16(x), to_dev(qw), to_dev(sw), ue8m0=case.ue8m0, weight_pow2=case.ue8m0)
     torch.cuda.synchronize()
-    assert np.array_equal(host(sa), sa_ref) and np.array_equal(host(qa), qa_ref), "activation quant differs"
-    rows = sample_rows(case.M, 8 if case.N * case.K > 1e8 else 16)
-    ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw, rows=rows)
+    rows = sample_rows(case.M, 256, key=case.N)
+    qa_ref, sa_ref = oracle.group_quant(x[rows], ue8m0=case.ue8m0)
+    ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
     yh = host(y)[rows].astype(np.float64)
+    del y
     assert_close(yh, ref, case.cid)
 
 

@@ -122,20 +122,16 @@ def test_group_quant_every_bf16_value():
 
 
 def _quant_cases():
+    """The activation operand of every workload once per (M, K): C1-C4, and the
+    105 standalone quantizer cases of the C5 sweep (15 M x 7 K)."""
     seen, out = set(), []
-    for config in ("single", "decode_8b", "prefill_8b", "ue8m0_32b"):
+    for config in ("single", "decode_8b", "prefill_8b", "ue8m0_32b", "sweep"):
         for c in synth.cases(config):
             key = (config, c.M, c.K)
             if key not in seen:
                 seen.add(key)
                 out.append(c)
-    sweep = synth.cases("sweep")
-    picks = {(1, None), (16, None), (1024, None), (16384, 25600), (16384, 2048), (4096, 6144)}
-    for c in sweep:
-        for m, k in picks:
-            if c.M == m and (k is None or c.K == k) and ("sweep", c.M, c.K) not in seen:
-                seen.add(("sweep", c.M, c.K))
-                out.append(c)
+    assert sum(1 for k in seen if k[0] == "sweep") == 105
     return out
 
 

@@ -65,9 +65,12 @@ def test_table_edges_follow_from_the_bounds():
     assert abs(t - mpmath.mpf(0.5)) < mpmath.mpf(2) ** -55  # closer to 0.5 than half the spacing below it
     assert vals[0] == 0.5
     # |g| >= 256: |g u t(|g|)| <= 256 e^-256 * (largest bf16) < 2^-150, so the
-    # float32 result is a signed zero whatever t is (a |g| t(|g|) decreases for |g| > 1)
-    assert vals[-1] == 0.0
+    # float32 result is a signed zero for the true t (|g| t(|g|) decreases for
+    # |g| > 1) and for the table's 2^-1022 alike (the largest |g u| times it is
+    # far below 2^-150); the entry is positive so that 0 - t < 0
+    assert vals[-1] == 2.0 ** -1022
     largest_bf16 = float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])
     assert 256 * math.exp(-256) * largest_bf16 < 2.0 ** -150
+    assert largest_bf16 * largest_bf16 * 2.0 ** -1022 < 2.0 ** -150
     # the first tabled magnitude is 2^-53 itself
     assert (e_lo - 127) == -53
