@@ -68,7 +68,7 @@ def kernel_symbol(cfg, fused: bool = False, M: int = 0, channel: bool = False, N
     if cfg.variant == 0:
         wm = {64: 32, 128: 64, 256: 128 if cfg.tile_n == 256 else 64}[cfg.tile_m]
         wn = 32 if cfg.kwaves == 2 else 64
-        sm = 2 if channel else cfg.scale_mode
+        sm = 2 if channel else cfg.scale_mode & 1  # bit 1 is the activation-scale layout
         split = cfg.split_k > 1
         if split and cfg.split_tail and N:
             # whole rounds only: the launcher runs the unsplit kernel (rounds of
@@ -421,13 +421,18 @@ def main() -> int:
         xs.append(xh)
         x = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
         qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
-        sa = torch.empty((c.M,) if dynamic else (c.M, c.K // 128), dtype=torch.float32, device=dev)
+        # block format: token-contiguous activation scales, as fp8_linear lays
+        # them out for its GEMM
+        sa = torch.empty((c.M,) if dynamic else (c.K // 128, c.M), dtype=torch.float32, device=dev)
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
         cfg = fb.fp8_block_gemm_select(c.M, c.N, c.K, (fb.FLAG_UE8M0 | fb.FLAG_WEIGHT_POW2) if c.ue8m0 else 0)
+        gcfg = cfg if dynamic else fb.make_config(cfg.variant, cfg.tile_m, cfg.tile_n, cfg.split_k, cfg.kwaves,
+                                                  cfg.stages, cfg.scale_mode | fb.SCALES_SA_MN_MAJOR,
+                                                  cfg.split_tail)
         ws = fb.workspace_for(c.M, c.N, c.K, cfg, dev)
         lws = fb.linear_workspace(c.M, c.N, c.K, cfg, dev)
         qw, sw = wq[(c.N, c.K, c.ue8m0)][i % WEIGHT_COPIES]
-        bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, ws=ws, lws=lws, qw=qw, sw=sw,
+        bufs.append(dict(case=c, x=x, qa=qa, sa=sa, y=y, cfg=cfg, gcfg=gcfg, ws=ws, lws=lws, qw=qw, sw=sw,
                          fused=cfg.variant == fb.SWAPAB and not dynamic
                          and (cfg.tile_m <= 32 or (cfg.tile_m == 64 and cfg.tile_n == 16))))
     torch.cuda.synchronize()
@@ -437,14 +442,14 @@ def main() -> int:
         if dynamic:
             fb.fp8_token_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
         else:
-            fb.fp8_group_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+            fb.fp8_group_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream, scale_mn_major=True)
 
     def gemm(b, w=None):
         qw, sw = (b["qw"], b["sw"]) if w is None else w
         if dynamic:
             fb.fp8_scaled_mm(b["qa"], b["sa"], qw, sw, b["y"], b["cfg"], b["ws"], stream=stream)
         else:
-            fb.fp8_block_gemm(b["qa"], b["sa"], qw, sw, b["y"], b["cfg"], b["ws"], stream=stream)
+            fb.fp8_block_gemm(b["qa"], b["sa"], qw, sw, b["y"], b["gcfg"], b["ws"], stream=stream)
 
     def linear(b, w=None):
         qw, sw = (b["qw"], b["sw"]) if w is None else w

@@ -30,7 +30,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
 
-ABI_VERSION = 5  # FP8BLK_ABI_VERSION of the header this binding follows
+ABI_VERSION = 6  # FP8BLK_ABI_VERSION of the header this binding follows
 GROUP = 128
 FLAG_UE8M0 = 1
 FLAG_WEIGHT_POW2 = 8  # the weight scales are powers of two (fp8_linear, fp8_block_gemm_select)
@@ -62,6 +62,7 @@ class GemmConfig(ctypes.Structure):
 
 SCALES_FP32 = 0
 SCALES_POW2 = 1
+SCALES_SA_MN_MAJOR = 2  # bit: fp8_block_gemm's activation scales are [K/128, >= M]
 
 
 def make_config(variant: int, tile_m: int, tile_n: int, split_k: int = 1, kwaves: int = 1,

@@ -24,11 +24,16 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HIP; }
 
+// scale_mode without the activation-scale layout bit
+int scale_rule(const fp8blk_gemm_config& c) { return c.scale_mode & ~FP8BLK_SCALES_SA_MN_MAJOR; }
+bool sa_mn_major(const fp8blk_gemm_config& c) { return (c.scale_mode & FP8BLK_SCALES_SA_MN_MAJOR) != 0; }
+
 int check_config(const fp8blk_gemm_config& c, int64_t M, int64_t N, int64_t K) {
   const int64_t kb = K / kG;
   if (c.split_tail != 0 && (c.split_tail != 1 || c.variant != FP8BLK_STANDARD)) return FP8BLK_ERR_BAD_CONFIG;
-  if (c.scale_mode != FP8BLK_SCALES_FP32 && c.scale_mode != FP8BLK_SCALES_POW2) return FP8BLK_ERR_BAD_CONFIG;
-  if (c.scale_mode == FP8BLK_SCALES_POW2 && c.variant != FP8BLK_STANDARD) return FP8BLK_ERR_BAD_CONFIG;
+  if (c.scale_mode < 0 || (scale_rule(c) != FP8BLK_SCALES_FP32 && scale_rule(c) != FP8BLK_SCALES_POW2))
+    return FP8BLK_ERR_BAD_CONFIG;
+  if (scale_rule(c) == FP8BLK_SCALES_POW2 && c.variant != FP8BLK_STANDARD) return FP8BLK_ERR_BAD_CONFIG;
   if (c.split_k < 1 || c.split_k > 256 || c.split_k > kb) return FP8BLK_ERR_BAD_CONFIG;
   if (c.variant == FP8BLK_STANDARD) {
     if (!fp8blk::standard_tile_supported(c.tile_m, c.tile_n, c.stages, c.kwaves == 0 ? 1 : c.kwaves))
@@ -52,6 +57,27 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0) return FP8BLK_ERR_BAD_SHAPE;
   if (K % kG != 0 || N % kG != 0) return FP8BLK_ERR_BAD_SHAPE;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8BLK_ERR_BAD_SHAPE;
+  return FP8BLK_OK;
+}
+
+int kernel_scale_mode(const fp8blk_gemm_config& c) {
+  return scale_rule(c) == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2 : fp8blk::kScalesBlock;
+}
+
+// Activation scales of fp8_block_gemm: row-major [M][ldsa] (ldsa >= K/128) or
+// token-contiguous [K/128][ldsa] (ldsa >= M); a K block's offset kb * ldsa * 4
+// must stay below 2^31 bytes (the kernels' 32-bit scalar offsets).
+int set_sa_layout(fp8blk::GemmArgs& g, bool mn, int64_t ldsa, int64_t M, int64_t K) {
+  if (mn) {
+    if (ldsa < M) return FP8BLK_ERR_BAD_STRIDE;
+    if ((K / kG) * ldsa * 4 >= (int64_t(1) << 31)) return FP8BLK_ERR_BAD_STRIDE;
+    g.sa_row = 1;
+    g.sa_kb = ldsa;
+  } else {
+    if (ldsa < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+    g.sa_row = ldsa;
+    g.sa_kb = 1;
+  }
   return FP8BLK_OK;
 }
 
@@ -153,7 +179,7 @@ int linear_call(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* s
   // the matrix core keeps only the exponent bits of every scale: both the
   // quantizer's scales and the caller's weight scales must be powers of two
   const uint32_t pow2_flags = FP8BLK_FLAG_UE8M0 | FP8BLK_FLAG_WEIGHT_POW2;
-  if (c.scale_mode == FP8BLK_SCALES_POW2 && (flags & pow2_flags) != pow2_flags) return FP8BLK_ERR_BAD_CONFIG;
+  if (scale_rule(c) == FP8BLK_SCALES_POW2 && (flags & pow2_flags) != pow2_flags) return FP8BLK_ERR_BAD_CONFIG;
   if (ldx < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
   if (ldw >= kMaxPitch || ldsw * 4 >= kMaxPitch) return FP8BLK_ERR_BAD_STRIDE;
   const LinearLayout L = linear_layout(c, M, N, K);
@@ -195,18 +221,22 @@ int linear_call(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* s
   }
   uint8_t* q = (uint8_t*)(base + L.q_off);
   float* sc = (float*)(base + L.s_off);
-  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, K / kG, eps, ue8m0, 0, s);
+  // The scales go to the workspace token-contiguous ([K/128][M]): a Standard
+  // tile then loads each K block's 256 activation scales as one contiguous
+  // run instead of 256 scattered words (row-major when a K block's offset
+  // would not fit 31 bits).
+  const bool mn = (K / kG) * M * 4 < (int64_t(1) << 31);
+  hipError_t e = fp8blk::launch_group_quant(x, M, K, ldx, q, K, sc, mn ? M : K / kG, eps, ue8m0, mn ? 1 : 0, s);
   if (e != hipSuccess) return FP8BLK_ERR_HIP;
   g.a = q;
   g.sa = sc;
   g.lda = K;
-  g.ldsa = K / kG;
+  g.ldsa = mn ? M : K / kG;
+  set_sa_layout(g, mn, g.ldsa, M, K);
   if (c.variant == FP8BLK_SWAPAB)
     return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
-  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
-                                                c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
-                                                                                       : fp8blk::kScalesBlock,
-                                                  s));
+  return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages,
+                                                c.kwaves == 0 ? 1 : c.kwaves, kernel_scale_mode(c), s));
 }
 
 
@@ -310,9 +340,12 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   }
   st = check_config(c, M, N, K);
   if (st != FP8BLK_OK) return st;
-  if (lda < K || ldw < K || ldy < N || ldsa < K / kG || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
+  if (lda < K || ldw < K || ldy < N || ldsw < K / kG) return FP8BLK_ERR_BAD_STRIDE;
   if (lda >= kMaxPitch || ldw >= kMaxPitch || ldsa * 4 >= kMaxPitch || ldsw * 4 >= kMaxPitch)
     return FP8BLK_ERR_BAD_STRIDE;
+  fp8blk::GemmArgs g{};
+  st = set_sa_layout(g, sa_mn_major(c), ldsa, M, K);
+  if (st != FP8BLK_OK) return st;
   if (M == 0) return FP8BLK_OK;
   if (!a || !sa || !w || !sw || !y) return FP8BLK_ERR_NULL_PTR;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned4(sa) || !aligned4(sw) ||
@@ -323,7 +356,6 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
     if (!workspace || workspace_bytes < need) return FP8BLK_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FP8BLK_ERR_MISALIGNED;
   }
-  fp8blk::GemmArgs g{};
   g.a = a;
   g.sa = sa;
   g.lda = lda;
@@ -340,10 +372,8 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, int64_t lda, int64_t ldsa,
   g.ws = need > 0 ? (float*)workspace : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (c.variant == FP8BLK_STANDARD)
-    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages, c.kwaves == 0 ? 1 : c.kwaves,
-                                                  c.scale_mode == FP8BLK_SCALES_POW2 ? fp8blk::kScalesBlockPow2
-                                                                                       : fp8blk::kScalesBlock,
-                                                  s));
+    return to_status(fp8blk::launch_gemm_standard(g, c.tile_m, c.tile_n, c.split_k, c.split_tail != 0, c.stages,
+                                                  c.kwaves == 0 ? 1 : c.kwaves, kernel_scale_mode(c), s));
   return to_status(fp8blk::launch_gemm_swapab(g, c.tile_m, c.tile_n, c.kwaves, c.split_k, s));
 }
 
@@ -435,6 +465,8 @@ int fp8_scaled_mm(const uint8_t* a, const float* sa, int64_t lda, const uint8_t*
   g.a = a;
   g.sa = sa;
   g.lda = lda;
+  g.sa_row = 1;
+  g.sa_kb = 0;
   g.w = w;
   g.sw = sw;
   g.ldw = ldw;

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
       xbsrc[t] = g.x + mc * g.ldx + kq;
     } else {
       xsrc[t] = g.a + mc * g.lda + kq;
-      sasrc[t] = g.sa + mc * g.ldsa;
+      sasrc[t] = g.sa + mc * g.sa_row;
     }
   }
   const float* swsrc = g.sw + (n0 >> 7) * g.ldsw;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
         } else if (tvalid[t]) {
           b.xf[u][t] = make_v8i(gload16(xsrc[t] + ko), gload16(xsrc[t] + ko + 64));
           // CH: no per-block factor; a K block past the range must add nothing
-          b.gsc[u][t] = CH ? (k <= kblast ? 1.f : 0.f) : sasrc[t][kc] * swv;
+          b.gsc[u][t] = CH ? (k <= kblast ? 1.f : 0.f) : sasrc[t][kc * g.sa_kb] * swv;
         } else {
           b.xf[u][t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           b.gsc[u][t] = 0.f;

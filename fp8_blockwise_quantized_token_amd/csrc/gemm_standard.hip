@@ -231,14 +231,18 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     const int row = 8 * (wave + i * S::WAVES) + lrow;
     b_off[i] = (uint32_t)row * (uint32_t)g.ldw + ((lch ^ swz_g(row)) << 4);
   }
-  const float* sa_base = g.sa + m0 * g.ldsa;
-  const uint32_t sa_off = (uint32_t)min((wave * 64 + lane) % BM, rows_valid - 1) * (uint32_t)g.ldsa;
+  const float* sa_base = g.sa + m0 * g.sa_row;
+  const uint32_t sa_off = (uint32_t)min((wave * 64 + lane) % BM, rows_valid - 1) * (uint32_t)g.sa_row;
   const float* sw_base = g.sw + (n0 >> 7) * g.ldsw;
   const uint32_t sw_off = (uint32_t)min(lane, BN / 128 - 1) * (uint32_t)g.ldsw;
   const int sw_slot = BM + ((wave_n * WN) >> 7);  // this wave's weight scale in the stage buffer
   const bool sa_wave = wave < S::SA_INSTR;
   const float* sc_base = sa_wave ? sa_base : sw_base;
   const uint32_t sc_off = sa_wave ? sa_off : sw_off;
+  // bytes from one K block's scales to the next: sa_kb floats for the
+  // activation scales (1 row-major; the token pitch when token-contiguous, so
+  // that a wave's 64 rows are one contiguous 256-byte run), 1 for the weight's
+  const uint32_t sc_kb = sa_wave ? (uint32_t)g.sa_kb * 4u : 4u;
   const int sc_dst = sa_wave ? wave * 64 : BM;
 
   // Buffer resources over the tile bases (raw, byte-addressed; offsets are
@@ -270,7 +274,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     // scales, the others the weight scales (the same values, harmless)
     constexpr int IS = S::A_INSTR + S::B_INSTR;
     if constexpr (!CH && IS >= LO && IS < HI)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(ls + sc_dst), 4, (int)(sc_off * 4u), kb * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void*)(ls + sc_dst), 4, (int)(sc_off * 4u),
+                                               (int)((uint32_t)kb * sc_kb), 0, 0);
   };
   auto issue = [&](uint8_t* la, uint8_t* lb, float* ls, int kb) __attribute__((always_inline)) {
     issue_part(ic<0>{}, ic<PER>{}, la, lb, ls, kb);

@@ -39,6 +39,10 @@ struct GemmArgs {
   const uint8_t* a;
   const float* sa;
   int64_t lda, ldsa;
+  // Activation scale (m, kb) is sa[m * sa_row + kb * sa_kb] (floats): row-major
+  // [M][K/128] has (ldsa, 1), token-contiguous [K/128][ldsa] has (1, ldsa).
+  // Unused by the per-token scale mode.
+  int64_t sa_row, sa_kb;
   const uint8_t* w;
   const float* sw;
   int64_t ldw, ldsw;

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 5
+#define FP8BLK_ABI_VERSION 6
 #define FP8BLK_GROUP 128      /* K-group width and weight block edge */
 #define FP8BLK_E4M3_MAX 448.0f
 /* Smallest accepted eps (2^-80, about 8.3e-25).  With eps at least this,
@@ -89,6 +89,14 @@ extern "C" {
                                 applied exactly by the matrix core (STANDARD
                                 only; results unspecified for other scales:
                                 only the exponent bits of each scale are used) */
+#define FP8BLK_SCALES_SA_MN_MAJOR 2 /* bit OR-ed into either mode: fp8_block_gemm's
+                                activation scales are token-contiguous,
+                                sa[K/128][ldsa] with ldsa >= M, as fp8_group_quant
+                                writes them with FP8BLK_FLAG_SCALE_MN_MAJOR (a
+                                Standard tile then loads each K block's scales
+                                as one contiguous run); requires
+                                (K/128) * ldsa * 4 < 2^31.  fp8_linear ignores
+                                it (it lays out its own scales). */
 
 /* Scale output of fp8_group_quant for other consumers (German page,
  * "Praktische Einschränkungen": UE8M0 scales for GEMMs that take them) */
@@ -136,7 +144,8 @@ typedef struct fp8blk_gemm_config {
     int32_t split_k;
     int32_t kwaves;
     int32_t stages;
-    int32_t scale_mode;  /* FP8BLK_SCALES_FP32 or FP8BLK_SCALES_POW2 */
+    int32_t scale_mode;  /* FP8BLK_SCALES_FP32 or FP8BLK_SCALES_POW2, optionally
+                            | FP8BLK_SCALES_SA_MN_MAJOR */
     int32_t split_tail;  /* 0 or 1, see above */
 } fp8blk_gemm_config;
 
@@ -223,6 +232,8 @@ int64_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
  * quantized GEMM follows the unified GEMM with scaling added; "Scope":
  * 1x128 / 128x128 scales).
  *   a  uint8 e4m3fn [M][lda], lda >= K      sa fp32 [M][ldsa], ldsa >= K/128
+ *                                           (FP8BLK_SCALES_SA_MN_MAJOR in the
+ *                                           configuration: [K/128][ldsa], ldsa >= M)
  *   w  uint8 e4m3fn [N][ldw], ldw >= K      sw fp32 [N/128][ldsw], ldsw >= K/128
  *   y  bf16 [M][ldy], ldy >= N
  *   cfg NULL selects through fp8_block_gemm_select (flags 0: fp32 scale

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fb.fp8_abi_version() == fb.ABI_VERSION == 5
+    assert fb.fp8_abi_version() == fb.ABI_VERSION == 6
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert fb.fp8_status_string(st) != "unknown status"
     assert fb.fp8_status_string(-99) == "unknown status"
@@ -142,9 +142,22 @@ def test_gemm_argument_errors():
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_tail=5)) == CFG
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, split_tail=-1)) == CFG
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, split_tail=1)) == CFG
-    # scale modes: fp32 or power-of-two (Standard only)
-    assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=2)) == CFG
+    # scale modes: fp32 or power-of-two (Standard only), each optionally with
+    # token-contiguous activation scales
+    for bad in (4, 3 | 4, 8, -1):
+        assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, scale_mode=bad)) == CFG, bad
     assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, scale_mode=fb.SCALES_POW2)) == CFG
+    assert _gemm(cfg=fb.make_config(fb.SWAPAB, 16, 16, 1, 2, scale_mode=fb.SCALES_POW2 | 2)) == CFG
+    # token-contiguous activation scales: [K/128][ldsa] needs ldsa >= M, and a
+    # K block's offset (K/128) ldsa 4 below 2^31 bytes
+    for mode in (fb.SCALES_SA_MN_MAJOR, fb.SCALES_POW2 | fb.SCALES_SA_MN_MAJOR):
+        mn = fb.make_config(fb.STANDARD, 128, 128, scale_mode=mode)
+        assert _gemm(cfg=mn, ldsa=2) == STRIDE          # 2 < M = 8
+        assert _gemm(cfg=mn, ldsa=8, M=0) == OK
+        assert _gemm(cfg=mn, ldsa=8, sa=None) == NULL   # accepted up to the pointer check
+        assert _gemm(cfg=mn, ldsa=1 << 21, M=8, K=128 * 256, lda=128 * 256, ldw=128 * 256, ldsw=256) == STRIDE
+    swmn = fb.make_config(fb.SWAPAB, 16, 16, 1, 2, scale_mode=fb.SCALES_SA_MN_MAJOR)
+    assert _gemm(cfg=swmn, ldsa=2) == STRIDE and _gemm(cfg=swmn, ldsa=8, sa=None) == NULL
     # LDS pipeline depth: compiled per tile; Swap-AB takes none
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 256, 256, stages=3)) == CFG
     assert _gemm(cfg=fb.make_config(fb.STANDARD, 128, 128, stages=4)) == CFG

@@ -463,3 +463,43 @@ def test_split_tail_takes_each_tile_from_the_unsplit_or_the_split_run(tm, tn, kw
         assert ok, (tm, tn, sk, np.flatnonzero(~eq_u)[:8], np.flatnonzero(~eq_s)[:8])
         assert not eq_u.all() and not eq_s.all(), (tm, tn, sk)
         assert_close(host(yt_dev)[rows].astype(np.float64), ref, f"split tail {tm}x{tn} {mode} sk{sk}")
+
+
+def _run_mn(qa, sa, qw, sw, cfg):
+    """The same GEMM with the activation scales token-contiguous: sa^T stored
+    [K/128][M + 8] (a padded pitch), configuration bit FP8BLK_SCALES_SA_MN_MAJOR."""
+    M, G = sa.shape
+    st = np.full((G, M + 8), np.nan, np.float32)
+    st[:, :M] = sa.T
+    c = fb.make_config(cfg.variant, cfg.tile_m, cfg.tile_n, cfg.split_k, cfg.kwaves, cfg.stages,
+                       cfg.scale_mode | fb.SCALES_SA_MN_MAJOR, cfg.split_tail)
+    say("gemm mn-major scales", qa.shape, qw.shape, c.as_dict())
+    y = fb.block_gemm(to_dev(qa), to_dev(st)[:, :M], to_dev(qw), to_dev(sw), c)
+    return host(y).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K", SMALL, ids=lambda v: str(v))
+def test_token_contiguous_scales_equal_row_major(M, N, K):
+    """Every configuration reads token-contiguous activation scales to the
+    same result, bit for bit, as row-major ones (only the scale addresses
+    differ), and that result is within the oracle's tolerance."""
+    qa, sa, qw, sw = _random_operands(M, N, K, 2)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    for cfg in _configs(M, N, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        ym = _run_mn(qa, sa, qw, sw, cfg)
+        assert np.array_equal(y, ym), str(cfg)
+        assert_close(ym, ref, str(cfg))
+
+
+def test_token_contiguous_power_of_two_scales():
+    M, N, K = 300, 768, 896
+    x = synth.activations_bf16(synth.Case("ue8m0_32b", "p2", M, N, K, "student_t3", True, 41))
+    qa, sa = oracle.group_quant(x, ue8m0=True)
+    qw, sw = oracle_weight(N, K, True)
+    ref = oracle.block_gemm(qa, sa, qw, sw)
+    for cfg in _pow2_configs(N, K):
+        y = _run(qa, sa, qw, sw, cfg)
+        ym = _run_mn(qa, sa, qw, sw, cfg)
+        assert np.array_equal(y, ym), str(cfg)
+        assert_close(ym, ref, str(cfg))
