@@ -124,6 +124,11 @@ def traffic_from_profiles(symbol: str):
 
 ROTATE_BYTES = 1 << 30  # bytes each timing cycle touches: four times the Infinity Cache
 TRIALS = 5
+# launches per captured graph in the per-case timing: the same for every case
+# (and at least the most rotation copies any case gets), so each case
+# dispatches its kernels equally often and a profiler's per-kernel average
+# over the run is the mean over cases that the roofline figure uses
+GRAPH_LAUNCHES = 64
 
 
 def rotation_copies(copies, nbytes: int, dev, limit: int = 64):
@@ -210,6 +215,19 @@ def extra_measurements(stream, dev):
         del x, q, s, xc
     torch.cuda.empty_cache()
     return out
+
+
+def trace_from_profiles(symbol: str):
+    """The rocprofv3 average duration (us) of a kernel from the committed
+    kernel-trace summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "kernel_trace.json")
+    try:
+        ent = json.load(open(path)).get("kernels", {}).get(symbol)
+    except (OSError, ValueError):
+        return None
+    if ent is None or ent.get("source_hash") != source_hash(*kernel_sources(symbol)):
+        return None
+    return ent.get("avg_us")
 
 
 def cpu_baseline(cases, xs, budget_s: float, dynamic: bool = False):
@@ -511,18 +529,18 @@ def main() -> int:
     sym_work = {}
     for b in bufs:
         c = b["case"]
-        wcopies = rotation_copies(wq[(c.N, c.K, c.ue8m0)], c.N * c.K, dev)
+        wcopies = rotation_copies(wq[(c.N, c.K, c.ue8m0)], c.N * c.K, dev, limit=GRAPH_LAUNCHES)
         xcopies = rotation_copies([(b["x"],)], 2 * c.M * c.K, dev, limit=8)
         nq = max(len(xcopies), 8)
         tq = graph_time(stream, [lambda r=r: quant(b, x=xcopies[r % len(xcopies)][0]) for r in range(nq)])
-        lin = [lambda r=r: linear(b, w=wcopies[r % len(wcopies)]) for r in range(max(len(wcopies), 8))]
+        lin = [lambda r=r: linear(b, w=wcopies[r % len(wcopies)]) for r in range(GRAPH_LAUNCHES)]
         tl = graph_time(stream, lin)
         if b["fused"]:
             tg = tl
         else:
             quant(b)
             tg = graph_time(stream, [lambda r=r: gemm(b, w=wcopies[r % len(wcopies)])
-                                     for r in range(max(len(wcopies), 8))])
+                                     for r in range(GRAPH_LAUNCHES)])
         del wcopies, xcopies
         fl = c.flops()
         gb = gemm_bytes(c, dynamic) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
@@ -563,6 +581,16 @@ def main() -> int:
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic}
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_t * 1e6, 2)
+    # the same kernel's average under rocprofv3 --kernel-trace (committed
+    # summary of a profiled bench.py run on the current sources), and the
+    # fraction of peak it implies
+    rp = trace_from_profiles(dom)
+    roof["rocprof_avg_launch_us"] = round(rp, 2) if rp else None
+    if rp:
+        w_ = flop_per_launch / (rp * 1e-6) / 1e12 if mfma_bound else byte_per_launch / (rp * 1e-6) / 1e9
+        roof["frac_rocprof"] = round(w_ / (PEAK_FP8_TFLOPS if mfma_bound else PEAK_HBM_GBPS), 4)
+    else:
+        roof["frac_rocprof"] = None
     roof["launches_measured"] = dlaunches
     roof["timing"] = ("HIP events over graph replays of back-to-back launches rotating >= 1 GiB of weight "
                       "copies, median of 5")

@@ -3,16 +3,25 @@
 Two steps, each under its own rocprofv3 counter pass:
 
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o p -- \\
-      python3 -m fp8_blockwise_quantized_token_amd.traffic run
+      python3 fp8_blockwise_quantized_token_amd/traffic.py run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_w> -o p -- \\
-      python3 -m fp8_blockwise_quantized_token_amd.traffic run
-  python3 -m fp8_blockwise_quantized_token_amd.traffic summarize <dir_f> <dir_w> \\
+      python3 fp8_blockwise_quantized_token_amd/traffic.py run
+  python3 fp8_blockwise_quantized_token_amd/traffic.py summarize <dir_f> <dir_w> \\
       --out profiles/hbm_traffic.json
 
 ``run`` launches every case of the workload once through fp8_linear (and
-once through fp8_block_gemm on pre-quantized input, so the Standard GEMM
-kernel is seen alone), the two fused producers at the producer benchmark's
-largest size, plus a plain device-to-device copy of a known size.
+once through fp8_block_gemm on pre-quantized input with token-contiguous
+scales, as fp8_linear lays them out, so the Standard GEMM kernel is seen
+alone), the two fused producers at the producer benchmark's largest size,
+plus a plain device-to-device copy of a known size.
+
+``trace`` records the per-kernel average durations of a rocprofv3
+``--kernel-trace --stats`` run of bench.py (its ``*kernel_stats.csv``),
+keyed by kernel name and source hash like the traffic, so that bench.py can
+print the profiler's figure for its dominant kernel beside its own:
+
+  rocprofv3 --kernel-trace --stats --output-format csv -d <dir_t> -o p -- python3 bench.py ...
+  python3 fp8_blockwise_quantized_token_amd/traffic.py trace <dir_t> --out profiles/kernel_trace.json
 ``summarize`` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per
 kernel, scales each by what the same counter reads for the copy (bytes
 expected / bytes counted), and records the result keyed by the kernel name
@@ -89,8 +98,12 @@ def run(workload: str) -> None:
         print(f"[traffic] {c.cid} {cfg.as_dict()}", flush=True)
         fb.linear(x, qw, sw, ue8m0=c.ue8m0, cfg=cfg)
         if cfg.variant == fb.STANDARD:
-            qa, sa = fb.quantize_activations(x, ue8m0=c.ue8m0)
-            fb.block_gemm(qa, sa, qw, sw, cfg)
+            qa = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
+            sa = torch.empty((c.K // 128, c.M), dtype=torch.float32, device=dev)
+            fb.fp8_group_quant(x, qa, sa, ue8m0=c.ue8m0, scale_mn_major=True)
+            gcfg = fb.make_config(cfg.variant, cfg.tile_m, cfg.tile_n, cfg.split_k, cfg.kwaves, cfg.stages,
+                                  cfg.scale_mode | fb.SCALES_SA_MN_MAJOR, cfg.split_tail)
+            fb.block_gemm(qa, sa, qw, sw, gcfg)
         torch.cuda.synchronize()
     # the fused producers at the producer benchmark's largest size
     bench = _bench()
@@ -160,6 +173,27 @@ def summarize(dir_f: str, dir_w: str, out_path: str) -> None:
               f"({v['dispatches']} dispatches)")
 
 
+def trace(dir_t: str, out_path: str, command: str = "") -> None:
+    files = glob.glob(os.path.join(dir_t, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {dir_t}")
+    bench = _bench()
+    kernels = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            name = short_name(r["Name"])
+            if not name.startswith("k_"):
+                continue
+            kernels[name] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                             "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                             "percent": float(r["Percentage"]),
+                             "source_hash": bench.source_hash(*bench.kernel_sources(name))}
+    with open(out_path, "w") as f:
+        json.dump({"unit": "microseconds per dispatch", "command": command, "kernels": kernels}, f, indent=1)
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["percent"])[:12]:
+        print(f"{k:60s} {v['calls']:6d} {v['avg_us']:10.2f} us {v['percent']:6.2f} %")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -169,9 +203,15 @@ def main() -> int:
     s.add_argument("dir_fetch")
     s.add_argument("dir_write")
     s.add_argument("--out", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    t = sub.add_parser("trace")
+    t.add_argument("dir_trace")
+    t.add_argument("--out", default=os.path.join(ROOT, "profiles", "kernel_trace.json"))
+    t.add_argument("--command", default="", help="the profiled command, recorded with the figures")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.workload)
+    elif a.cmd == "trace":
+        trace(a.dir_trace, a.out, a.command)
     else:
         summarize(a.dir_fetch, a.dir_write, a.out)
     return 0
