@@ -310,10 +310,14 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // time; the order (the next row's LDS reads, then 1 MFMA : 4 FMA) is
   // requested from the scheduler per step.  The first rows also issue the
   // direct-to-LDS loads that refill the stage the previous block consumed.
-  // The pipeline runs across K blocks: once the last row's products are
-  // issued, the wave passes the stage barrier, reads the next block's first
-  // A fragment, B fragments and scales, and folds the last row's products
-  // while those reads are in flight.
+  // The pipeline runs across K blocks.  When the stage's loads are all
+  // issued before the last row (EARLY: more tile rows than DMA rows), the
+  // wave passes the stage barrier before that row, whose A fragment is
+  // already in registers, and reads the next block's first A fragment and
+  // activation scale during the row's products; once they are issued, it
+  // reads the next block's B fragments and weight scale and folds the last
+  // row's products while those reads are in flight.  Otherwise the barrier
+  // and all of the next block's first reads follow the last row's products.
   static_assert(S::TM % 2 == 0, "row pipeline assumes an even number of tile rows");
   const int arow = wave_m * WM + frow;
   const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
@@ -329,9 +333,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // LDS reads complete in issue order, so the reads are issued in the order
   // of use (pinned by scheduling barriers): the first MFMA waits only for
   // the first A and B fragments, not for the whole burst.
-  auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
-    af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
-    __builtin_amdgcn_sched_barrier(0);
+  auto read_b = [&](const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < S::TN; ++j) {
       const int r = wave_n * WN + j * 16 + frow;
@@ -339,11 +341,26 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       __builtin_amdgcn_sched_barrier(0);
     }
     swv = ls[sw_slot];
+  };
+  auto read_first = [&](const uint8_t* la, const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
+    af[0] = make_v8i(*(const u32x4*)(la + a_lo), *(const u32x4*)(la + a_hi));
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(lb, ls);
     if constexpr (P2)
       ear = ls[srow];
     else if constexpr (!CH)
       scl = ls[srow];
   };
+  // Before the last tile row of a block: this wave's loads into the next
+  // stage have landed (the NS-2 younger stages may still be in flight);
+  // after the barrier every wave's have, and the last reads of the stage
+  // being consumed (the last row's A fragment and scale, read during the row
+  // before) are complete, so nobody reads it any more.
+  auto stage_barrier = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<(NS - 2) * PER>();
+    __syncthreads();
+  };
+  constexpr bool EARLY = S::TM > DMA_ROWS;
 
   // The loads due in tile row i (none past the first DMA_ROWS rows).
   auto dma_row = [&](int i, uint8_t* ra, uint8_t* rb, float* rs, int kb_refill) __attribute__((always_inline)) {
@@ -369,6 +386,10 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
           af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                              *(const u32x4*)(la + a_hi + (i + 1) * 2048));
           if constexpr (P2) ear = ls[srow + (i + 1) * 16];
+        } else if constexpr (EARLY) {  // the next block's first A fragment (and its scale)
+          stage_barrier();
+          af[prv] = make_v8i(*(const u32x4*)(na + a_lo), *(const u32x4*)(na + a_hi));
+          if constexpr (P2) ear = ns[srow];
         }
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
@@ -379,13 +400,16 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
                                                                          0, 0, 0);
         }
-        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);  // next row's reads first
+        if (EARLY || i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);  // next row's reads first
         __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmcnt<(NS - 2) * PER>();
-      __syncthreads();
-      read_first(na, nb, ns);
+      if constexpr (EARLY) {
+        read_b(nb, ns);  // after the last row's products have read bf
+      } else {
+        stage_barrier();
+        read_first(na, nb, ns);
+      }
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
@@ -398,6 +422,10 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
         af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
                            *(const u32x4*)(la + a_hi + (i + 1) * 2048));
         scn = ls[srow + (i + 1) * 16];
+      } else if constexpr (EARLY) {  // the next block's first A fragment and activation scale
+        stage_barrier();
+        af[prv] = make_v8i(*(const u32x4*)(na + a_lo), *(const u32x4*)(na + a_hi));
+        scn = ns[srow];
       }
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
@@ -409,7 +437,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
         }
       }
       if (i > 0) {
-        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next row's LDS reads first
+        if (EARLY || i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next row's LDS reads first
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -420,12 +448,12 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       gq[cur] = scl * swv;  // row i's factor, folded during row i+1
       scl = scn;
     }
-    // this wave's loads into the next stage have landed (the NS-2 younger
-    // stages may still be in flight); after the barrier every wave's have,
-    // and nobody reads the stage just consumed any more
-    wait_vmcnt<(NS - 2) * PER>();
-    __syncthreads();
-    read_first(na, nb, ns);
+    if constexpr (EARLY) {
+      read_b(nb, ns);  // after the last row's products have read bf
+    } else {
+      stage_barrier();
+      read_first(na, nb, ns);
+    }
     __builtin_amdgcn_sched_barrier(0);
     constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
 #pragma unroll
