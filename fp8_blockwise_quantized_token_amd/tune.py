@@ -17,6 +17,14 @@ call the table serves on the hot path; ``--op gemm`` times
 
   python -m fp8_blockwise_quantized_token_amd.tune --shapes all --out tune.json
   python -m fp8_blockwise_quantized_token_amd.tune --write-table tune.json
+
+``--merge-table`` re-tunes part of the table instead: for every result whose
+(N, K, M) ends a bucket of the current table, the bucket takes the fastest
+configuration when it beats the one dispatched now by more than
+``--min-gain`` (timing noise is about 1-2 %); other buckets are kept.
+
+  python -m fp8_blockwise_quantized_token_amd.tune --shapes 8b --ms 32,64 --out part.json
+  python -m fp8_blockwise_quantized_token_amd.tune --merge-table part.json
 """
 from __future__ import annotations
 
@@ -207,21 +215,55 @@ def write_table(path: str, out_inc: str) -> None:
         lo = 0
         for e in ents:
             b = e["best"]
-            var = "FP8BLK_SWAPAB" if b["variant"] == "swapab" else "FP8BLK_STANDARD"
             hi = e["M"]
             if e is ents[-1]:
                 hi = 2147483647 if b["variant"] == "standard" else e["M"]
-            ns = b.get("stages", 0)
-            cfg = (f"CFGT({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})"
-                   if b.get("split_tail", 0) else
-                   f"CFG({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']})" if ns == 0 else
-                   f"CFGS({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})")
+            cfg = cfg_text(b)
             lines.append(f"    {{{N}, {K}, {lo + 1}, {hi}, {cfg}}},  // {e['best_us']:.2f} us at M={e['M']}")
             lo = e["M"]
     lines.append("};")
     with open(out_inc, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out_inc}: {sum(len(v) for v in by_shape.values())} entries")
+
+
+def cfg_text(b: dict) -> str:
+    var = "FP8BLK_SWAPAB" if b["variant"] == "swapab" else "FP8BLK_STANDARD"
+    ns = b.get("stages", 0)
+    if b.get("split_tail", 0):
+        return f"CFGT({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})"
+    if ns == 0:
+        return f"CFG({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']})"
+    return f"CFGS({var}, {b['tile_m']}, {b['tile_n']}, {b['split_k']}, {b['kwaves']}, {ns})"
+
+
+def merge_table(path: str, inc: str, min_gain: float) -> None:
+    """Replace the buckets of `inc` that end at a re-tuned M with the faster
+    configuration; print what changed."""
+    import re
+    data = json.load(open(path))
+    lines = open(inc).read().split("\n")
+    pat = re.compile(r"^    \{(\d+), (\d+), (\d+), (\d+), (.*)\},  // .*$")
+    where = {}
+    for i, ln in enumerate(lines):
+        m = pat.match(ln)
+        if m:
+            where[(int(m.group(1)), int(m.group(2)), int(m.group(4)))] = (i, int(m.group(3)))
+    changed = 0
+    for e in data["entries"]:
+        key = (e["N"], e["K"], e["M"])
+        if key not in where or e["dispatch_us"] is None:
+            continue
+        if e["best"] == e["dispatch"] or e["best_us"] > e["dispatch_us"] * (1.0 - min_gain):
+            continue
+        i, lo = where[key]
+        lines[i] = (f"    {{{e['N']}, {e['K']}, {lo}, {e['M']}, {cfg_text(e['best'])}}},  "
+                    f"// {e['best_us']:.2f} us at M={e['M']}")
+        changed += 1
+        print(f"N={e['N']} K={e['K']} M={e['M']}: {e['dispatch_us']:.2f} -> {e['best_us']:.2f} us  {e['best']}")
+    with open(inc, "w") as f:
+        f.write("\n".join(lines))
+    print(f"{inc}: {changed} buckets changed")
 
 
 def main() -> int:
@@ -232,7 +274,13 @@ def main() -> int:
     ap.add_argument("--out", default="tune.json")
     ap.add_argument("--op", choices=("linear", "gemm"), default="linear")
     ap.add_argument("--write-table", metavar="RESULTS", help="write csrc/dispatch_table.inc from a result file")
+    ap.add_argument("--merge-table", metavar="RESULTS", help="update the buckets of csrc/dispatch_table.inc "
+                    "that end at a re-tuned M")
+    ap.add_argument("--min-gain", type=float, default=0.03, help="relative gain a merged bucket must show")
     args = ap.parse_args()
+    if args.merge_table:
+        merge_table(args.merge_table, os.path.join(HERE, "csrc", "dispatch_table.inc"), args.min_gain)
+        return 0
     if args.write_table:
         write_table(args.write_table, os.path.join(HERE, "csrc", "dispatch_table.inc"))
         return 0
