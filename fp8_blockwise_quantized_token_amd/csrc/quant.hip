@@ -49,11 +49,26 @@ constexpr uint32_t kGroupsPerIter = (kQuantThreads / 16) * kQuantUnroll;
 // SF (scale output format): 0 fp32 [M][lds]; 1 fp32 MN-major [K/128][lds];
 // 2 and 3: the same layouts with one E8M0 byte per scale (the biased
 // exponent of a power-of-two scale, value 2^(b - 127)).
+//
+// Walk.  Row-major layouts take the groups row by row: group g of a launch
+// is (g / div, g % div) with div = groups per row.  MN-major layouts take
+// tiles of kTileR rows x kTileC group columns, one tile per workgroup
+// iteration: g = 64 t + k is row kTileR (t / div) + k / kTileC and column
+// kTileC (t % div) + k % kTileC, div = tiles per row band (groups outside
+// the rows x cols of the launch are skipped).  A column's kTileR = 32 scales
+// of a tile are then one whole 128-byte line stored from one workgroup,
+// instead of pieces of a line stored from workgroups on different XCDs (that
+// cost 15-20 % at prefill sizes), while each row still reads kTileC
+// consecutive groups.  Either quotient is (n * magic) >> 40 with magic =
+// ceil(2^40 / div), exact for n < 2^24 and div <= 2^16.
+constexpr uint32_t kTileR = 32;
+constexpr uint32_t kTileC = kGroupsPerIter / kTileR;
+
 template <bool UE8M0, bool CONTIG, int SF>
 __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, void* __restrict__ s,
-    uint32_t total_groups, uint32_t gpr, uint64_t magic, int64_t ldx, int64_t ldq,
-    int64_t lds, float eps) {
+    uint32_t total_groups, uint32_t div, uint64_t magic, int64_t ldx, int64_t ldq,
+    int64_t lds, float eps, uint32_t rows, uint32_t cols) {
   constexpr bool MN = (SF & 1) != 0;
   constexpr bool E8M0 = (SF & 2) != 0;
   const uint32_t sub = threadIdx.x & 15u;
@@ -73,8 +88,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_group_quant(
         qo[u] = xo;
         so[u] = g;
       } else {
-        const uint32_t row = (uint32_t)(((uint64_t)g * magic) >> 40);
-        const uint32_t col = g - row * gpr;
+        uint32_t row, col;
+        if (MN) {
+          const uint32_t t = g / kGroupsPerIter, k = g % kGroupsPerIter;
+          const uint32_t tr = (uint32_t)(((uint64_t)t * magic) >> 40);
+          row = tr * kTileR + k / kTileC;
+          col = (t - tr * div) * kTileC + k % kTileC;
+          valid[u] = valid[u] && row < rows && col < cols;
+        } else {
+          row = (uint32_t)(((uint64_t)g * magic) >> 40);
+          col = g - row * div;
+        }
         xo = (int64_t)row * ldx + (int64_t)col * kGroup + sub * 8;
         qo[u] = (int64_t)row * ldq + (int64_t)col * kGroup + sub * 8;
         so[u] = MN ? (int64_t)col * lds + row : (int64_t)row * lds + col;
@@ -231,10 +255,10 @@ int device_cu_count() {
 
 template <bool UE8M0, bool CONTIG, int SF>
 void launch_gq(dim3 grid, dim3 block, hipStream_t stream, const uint16_t* xr, uint8_t* qr, void* sr,
-               uint32_t total, uint32_t gpr, uint64_t magic, int64_t ldx, int64_t ldq, int64_t lds,
-               float eps) {
-  hipLaunchKernelGGL((k_group_quant<UE8M0, CONTIG, SF>), grid, block, 0, stream, xr, qr, sr, total, gpr,
-                     magic, ldx, ldq, lds, eps);
+               uint32_t total, uint32_t div, uint64_t magic, int64_t ldx, int64_t ldq, int64_t lds,
+               float eps, uint32_t rows, uint32_t cols) {
+  hipLaunchKernelGGL((k_group_quant<UE8M0, CONTIG, SF>), grid, block, 0, stream, xr, qr, sr, total, div,
+                     magic, ldx, ldq, lds, eps, rows, cols);
 }
 
 hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
@@ -245,23 +269,29 @@ hipError_t launch_group_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
   const int64_t selt = (scale_format & 2) ? 1 : 4;  // bytes per stored scale
   const bool contig = scale_format == 0 && (ldx == K) && (ldq == K) && (lds == gpr);
   const int max_blocks = device_cu_count() * 8;
-  // Contiguous: one flat launch per 2^31 groups.  Strided: row chunks with
-  // fewer than 2^24 groups, so that row = (g * ceil(2^40/gpr)) >> 40 is exact.
+  // Contiguous: one flat launch per 2^31 groups.  Otherwise row chunks of
+  // fewer than 2^24 groups, so that the kernel's quotients are exact (the
+  // tiled MN-major walk divides tile numbers, below 2^18 then).
   const int64_t chunk_groups = contig ? (int64_t(1) << 31) : (int64_t(1) << 24);
   int64_t rows_per_chunk = chunk_groups / gpr;
+  if (mn) rows_per_chunk = rows_per_chunk / kTileR * kTileR;  // whole row bands per chunk
   if (rows_per_chunk < 1) rows_per_chunk = 1;
-  const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)gpr - 1) / (uint64_t)gpr;
+  const int64_t tiles_c = (gpr + kTileC - 1) / kTileC;
+  const uint64_t div = (!contig && mn) ? (uint64_t)tiles_c : (uint64_t)gpr;
+  const uint64_t magic = ((uint64_t(1) << 40) + div - 1) / div;
   for (int64_t r0 = 0; r0 < M; r0 += rows_per_chunk) {
     const int64_t rows = (M - r0) < rows_per_chunk ? (M - r0) : rows_per_chunk;
-    const uint32_t total = (uint32_t)(rows * gpr);
+    const uint32_t total = (uint32_t)((!contig && mn) ? ((rows + kTileR - 1) / kTileR) * tiles_c * kGroupsPerIter
+                                                      : rows * gpr);
     int64_t blocks = (total + kGroupsPerIter - 1) / kGroupsPerIter;
     if (blocks > max_blocks) blocks = max_blocks;
     const uint16_t* xr = x + r0 * ldx;
     uint8_t* qr = q + r0 * ldq;
     void* sr = (char*)s + (mn ? r0 : r0 * lds) * selt;
     dim3 grid((unsigned)blocks), block(kQuantThreads);
-    const uint32_t g32 = (uint32_t)gpr;
-#define FP8BLK_GQ(U, C, F) launch_gq<U, C, F>(grid, block, stream, xr, qr, sr, total, g32, magic, ldx, ldq, lds, eps)
+    const uint32_t d32 = (uint32_t)div, r32 = (uint32_t)rows, c32 = (uint32_t)gpr;
+#define FP8BLK_GQ(U, C, F) \
+  launch_gq<U, C, F>(grid, block, stream, xr, qr, sr, total, d32, magic, ldx, ldq, lds, eps, r32, c32)
     if (contig) {
       if (ue8m0) FP8BLK_GQ(true, true, 0); else FP8BLK_GQ(false, true, 0);
     } else if (ue8m0) {
