@@ -464,6 +464,123 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ---- epilogue of one tile row i (rows wave_m WM + 16 i + frow): lane
+  // holds row frow and columns orow..orow+3 of each tile (the products are
+  // computed as W A^T, so a lane's four values are consecutive in n): one
+  // 8-byte bf16 store, or one 16-byte fp32 store of split-K partials, per
+  // tile ----
+  v4f swc[S::TN];  // CH: per-channel weight scales of this lane's columns
+  auto load_swc = [&]() __attribute__((always_inline)) {
+    if constexpr (CH) {
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) swc[j][q] = g.sw[n0 + wave_n * WN + j * 16 + orow + q];
+    }
+  };
+  // Rows past M hold exactly the values of row M-1 (their A rows and scales
+  // re-read row M-1), so they are stored there again rather than skipped: the
+  // same bytes, and no branch in the pipeline.
+  auto store_row = [&](auto partial_c, int i) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_c)::value;  // fp32 split-K partials, else bf16
+    const int64_t m = min(m0 + wave_m * WM + i * 16 + frow, mlast);
+    const float sam = CH ? g.sa[m] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) {
+      const int64_t n = n0 + wave_n * WN + j * 16 + orow;
+      v4f v = acc[i][j];
+      if constexpr (CH) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
+      }
+      if constexpr (PARTIAL) {
+        *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
+      } else {
+        const uint32_t lo = bf16x2_bits(v[0], v[1]);
+        const uint32_t hi = bf16x2_bits(v[2], v[3]);
+        *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
+      }
+    }
+  };
+
+  // The last K block: the same row pipeline without a refill, a stage
+  // barrier or the next block's reads, and each tile row leaves as soon as
+  // its accumulators are final (during the next row's products), so the
+  // workgroup's output stores overlap its last block instead of following
+  // it in one burst.
+  auto kblock_last = [&](auto partial_c, const uint8_t* la, const float* ls) __attribute__((always_inline)) {
+    load_swc();
+    if constexpr (P2 || CH) {
+      const uint32_t eb = P2 ? __float_as_uint(swv) >> 23 : 0u;
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i) {
+        const int cur = i & 1, prv = cur ^ 1;
+        const uint32_t eac = __float_as_uint(ear) >> 23;
+        if (i + 1 < S::TM) {
+          af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
+                             *(const u32x4*)(la + a_hi + (i + 1) * 2048));
+          if constexpr (P2) ear = ls[srow + (i + 1) * 16];
+        }
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) {
+          if constexpr (P2)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
+                                                                         (int)eb, 0, (int)eac);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
+                                                                         0, 0, 0);
+        }
+        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i > 0) store_row(partial_c, i - 1);  // its products finished during this row's
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      store_row(partial_c, S::TM - 1);
+      return;
+    }
+    float scn = 0.f;
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) {
+      const int cur = i & 1, prv = cur ^ 1;
+      if (i + 1 < S::TM) {
+        af[prv] = make_v8i(*(const u32x4*)(la + a_lo + (i + 1) * 2048),
+                           *(const u32x4*)(la + a_hi + (i + 1) * 2048));
+        scn = ls[srow + (i + 1) * 16];
+      }
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j) {
+        P[cur][j] = mfma16x16x128(bf[j], af[cur]);
+        if (i > 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i - 1][j][q] = __builtin_fmaf(P[prv][j][q], gq[prv], acc[i - 1][j][q]);
+        }
+      }
+      if (i > 0) {
+        if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      gq[cur] = scl * swv;
+      scl = scn;
+      if (i > 0) store_row(partial_c, i - 1);  // folded during this row
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[last][j][q] = __builtin_fmaf(P[lc][j][q], gq[lc], acc[last][j][q]);
+    store_row(partial_c, last);
+  };
+
+
   // Stage s <- block kb0+s for s < NS-1; stage 0 is waited for, the others
   // stay in flight.  The block in stage s is consumed by kblock(s), which
   // meanwhile fills stage s-1 (consumed one block earlier; the barrier that
@@ -482,56 +599,68 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   __syncthreads();
   read_first(lds_a0, lds_b0, lds_s0);
   int kb = kb0;
-  for (; kb + NS - 1 < kb1; kb += NS) {
-    static_for<NS>([&](auto st) __attribute__((always_inline)) {
+  if constexpr (SPLIT) {
+    // Split launches (fp32 partials or bf16 per workgroup): every block
+    // refills, and the output leaves after the last one.
+    for (; kb + NS - 1 < kb1; kb += NS) {
+      static_for<NS>([&](auto st) __attribute__((always_inline)) {
+        constexpr int i = decltype(st)::value;
+        constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
+        kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}),
+               min(kb + i + NS - 1, kblast), stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+      });
+    }
+    static_for<NS - 1>([&](auto st) __attribute__((always_inline)) {  // the remaining kb1 - kb < NS blocks
       constexpr int i = decltype(st)::value;
       constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
-      kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}),
-             min(kb + i + NS - 1, kblast), stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+      if (kb + i < kb1)
+        kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}), kblast,
+               stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
     });
-  }
-  static_for<NS - 1>([&](auto st) __attribute__((always_inline)) {  // the remaining kb1 - kb < NS blocks
-    constexpr int i = decltype(st)::value;
-    constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
-    if (kb + i < kb1)
-      kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}), kblast,
-             stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
-  });
-  wait_vmcnt<0>();
-
-  // ---- epilogue: lane holds row frow and columns orow..orow+3 of each tile
-  // (the products are computed as W A^T, so a lane's four values are
-  // consecutive in n): one 8-byte bf16 store, or one 16-byte fp32 store of
-  // split-K partials, per tile ----
-  v4f swc[S::TN];  // CH: per-channel weight scales of this lane's columns
-  if constexpr (CH) {
+    wait_vmcnt<0>();
+    load_swc();
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) swc[j][q] = g.sw[n0 + wave_n * WN + j * 16 + orow + q];
-  }
-#pragma unroll
-  for (int i = 0; i < S::TM; ++i) {
-    const int64_t m = m0 + wave_m * WM + i * 16 + frow;
-    if (m >= g.M) continue;
-    const float sam = CH ? g.sa[m] : 1.0f;
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const int64_t n = n0 + wave_n * WN + j * 16 + orow;
-      v4f v = acc[i][j];
-      if constexpr (CH) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
-      }
-      if (SPLIT && !whole) {
-        *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
-      } else {
-        const uint32_t lo = bf16x2_bits(v[0], v[1]);
-        const uint32_t hi = bf16x2_bits(v[2], v[3]);
-        *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
-      }
+    for (int i = 0; i < S::TM; ++i) {
+      if (!whole)
+        store_row(std::true_type{}, i);
+      else
+        store_row(std::false_type{}, i);
     }
+  } else {
+    for (; kb + NS < kb1; kb += NS) {  // whole trips while more than NS blocks remain
+      static_for<NS>([&](auto st) __attribute__((always_inline)) {
+        constexpr int i = decltype(st)::value;
+        constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
+        kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}),
+               min(kb + i + NS - 1, kblast), stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+      });
+    }
+    // The remaining R = 1 .. NS blocks (stages 0 .. R-1), the last one
+    // storing the output as it goes: one straight-line path per R, so that
+    // nothing the refills need stays live into the last block.  (Only a
+    // split launch can have an empty K range.)
+    const int rem = kb1 - kb;
+    static_for<NS>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(rc)::value + 1;
+      if (rem == R) {
+        static_for<R>([&](auto st) __attribute__((always_inline)) {
+          constexpr int i = decltype(st)::value;
+          constexpr int nx = (i + 1) % NS, pv = (i + NS - 1) % NS;
+          if constexpr (i + 1 < R)
+            kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}), kblast,
+                   stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
+          else
+            kblock_last(std::false_type{}, stage_a(st), stage_s(st));
+        });
+      }
+    });
+    // Two stages: nothing but stores is outstanding here (the last block's
+    // data was waited for before it was read, and the last block refills
+    // nothing).  More stages: refills of clamped blocks may still be in
+    // flight into LDS, which must land before the workgroup ends.
+    if constexpr (NS > 2) wait_vmcnt<0>();
   }
+
 }
 
 // Sum of the split_k fp32 partials of the tail tiles (walk order tiles_dp
