@@ -583,8 +583,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 
   // Stage s <- block kb0+s for s < NS-1; stage 0 is waited for, the others
   // stay in flight.  The block in stage s is consumed by kblock(s), which
-  // meanwhile fills stage s-1 (consumed one block earlier; the barrier that
-  // ended that block has released it) with the block NS-1 ahead.  NS K
+  // meanwhile fills stage s-1 (consumed one block earlier; that block's
+  // stage barrier has released it) with the block NS-1 ahead.  NS K
   // blocks per trip so that every LDS buffer is a static object (the
   // compiler then knows the stage being read and the stages being filled
   // never alias and inserts no early wait); no branch inside a trip: block
