@@ -63,31 +63,29 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float y) {
   return __builtin_fmaf(-r, y, q0);
 }
 
-// Reciprocal pair for div_by_scale_f32: yn = RN(1/s), yd = the largest fp32
-// not above 1/s (yn or its predecessor), yl = RN((1 - s yd) / s) >= 0, so
-// that yd + yl is 1/s to about 2^-47.
-struct Recip {
-  float yn, yd, yl;
-};
-__device__ __forceinline__ Recip recip_of_scale(float s) {
-  Recip r;
-  r.yn = 1.0f / s;
-  const float e = __builtin_fmaf(-s, r.yn, 1.0f);  // exact: 1 - s yn
-  r.yd = e < 0.0f ? __uint_as_float(__float_as_uint(r.yn) - 1u) : r.yn;
-  r.yl = __builtin_fmaf(-s, r.yd, 1.0f) * r.yd;    // >= 0
-  return r;
+// 1/s in float64 for a positive normal fp32 s, to within 2^-52 (relative):
+// the hardware reciprocal, then three Newton steps with FMA.  Each step
+// squares the relative error and the last one is limited by its own
+// rounding, so the bound holds for any starting approximation within 2^-8
+// (host test); the steps cost 6 instructions per 128-value group.
+__device__ __forceinline__ double recip_f64(float s) {
+  const double b = (double)s;
+  double d = __builtin_amdgcn_rcp(b);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) d = __builtin_fma(d, __builtin_fma(-b, d, 1.0), d);
+  return d;
 }
 
-// x / s, correctly rounded, for any fp32 x: q0 = RN(x yd + RN(x yl)) is
-// within half an ulp plus a hair of x/s (faithful), so the residual q0 s - x
-// is exact under an FMA and one Markstein correction with RN(1/s) rounds
-// correctly.  yl >= 0 keeps the sign of a zero x through the first FMA; the
-// residual form keeps it through the rest.  4 operations per value.
-__device__ __forceinline__ float div_by_scale_f32(float x, float s, const Recip& r) {
-  const float q0 = __builtin_fmaf(x, r.yd, x * r.yl);
-  const float res = __builtin_fmaf(q0, s, -x);
-  return __builtin_fmaf(-res, r.yn, q0);
-}
+// x / s rounded to fp32 exactly as IEEE division, for any fp32 x, from
+// d = recip_f64(s): z = RN64(x d) is within 2^-51 (relative) of x / s, and a
+// quotient of two fp32 values in the normal range lies at least 2^-49
+// (relative) away from every fp32 rounding midpoint (a midpoint has a
+// 25-bit odd significand, and its product with the scale's significand
+// cannot fit in x's 24 bits), so z rounds to the same fp32 value as x / s.
+// Below 2^-126 the last bit may differ, far below the smallest e4m3 code:
+// both encode to the same signed zero.  x = +-0 gives +-0.  Three
+// operations per value (two conversions and a product).
+__device__ __forceinline__ float div_by_scale_f64(float x, double d) { return (float)((double)x * d); }
 
 // scale = max(amax, eps) / 448, correctly rounded, with the optional
 // power-of-two ceiling done on the exponent field.  The division by 448 is
@@ -144,10 +142,14 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load (non-temporal: data used once, keep it out of the
-// caches' way).
+// caches' way).  The quantizer and the SiLU producer read with it; the RMSNorm
+// rows and the decode GEMM's weight stream measure faster with plain loads.
 __device__ __forceinline__ u32x4 load_nt16(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
+
+// 16-byte load through the caches.
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 
 __device__ __forceinline__ v8i make_v8i(u32x4 lo, u32x4 hi) {
   v8i r;

@@ -10,9 +10,9 @@
 // element; SiLU-and-mul: 4 in, 1 + 4/128 out) and keep the quantizer's
 // lane layout: 16 lanes own one 128-group, 8 contiguous values per lane
 // loaded with one 16-byte load, the group amax reduced with DPP inside the
-// 16-lane row, the scale computed once per group, every value divided with
-// a 4-instruction correctly rounded division for fp32 values, two values
-// per fp8 convert.
+// 16-lane row, the scale and its float64 reciprocal computed once per group,
+// every fp32 value divided by the scale as IEEE division would (a float64
+// product rounded to fp32: three instructions), two values per fp8 convert.
 //
 // RMSNorm (the fp8 RMSNorm example of the Chinese Helion article, section
 // "自己写一个 Helion kernel 并接入 vLLM": variance = mean of squares,
@@ -58,12 +58,12 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float eps, bool ue8
   m = fmaxf(m, fmaxf(fmaxf(fabsf(y[4]), fabsf(y[5])), fmaxf(fabsf(y[6]), fabsf(y[7]))));
   const uint32_t am = row16_max_u32(__float_as_uint(m));
   const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
-  const Recip rc = recip_of_scale(sc);
+  const double d = recip_f64(sc);
   *sc_out = sc;
-  const uint32_t lo = encode4_q(div_by_scale_f32(y[0], sc, rc), div_by_scale_f32(y[1], sc, rc),
-                              div_by_scale_f32(y[2], sc, rc), div_by_scale_f32(y[3], sc, rc));
-  const uint32_t hi = encode4_q(div_by_scale_f32(y[4], sc, rc), div_by_scale_f32(y[5], sc, rc),
-                              div_by_scale_f32(y[6], sc, rc), div_by_scale_f32(y[7], sc, rc));
+  const uint32_t lo = encode4_q(div_by_scale_f64(y[0], d), div_by_scale_f64(y[1], d),
+                                div_by_scale_f64(y[2], d), div_by_scale_f64(y[3], d));
+  const uint32_t hi = encode4_q(div_by_scale_f64(y[4], d), div_by_scale_f64(y[5], d),
+                                div_by_scale_f64(y[6], d), div_by_scale_f64(y[7], d));
   return make_uint2(lo, hi);
 }
 
@@ -84,13 +84,13 @@ __device__ __forceinline__ u32x4 quant16(const float (&y)[16], float eps, bool u
     m[k] = fmaxf(fmaxf(fabsf(y[4 * k]), fabsf(y[4 * k + 1])), fmaxf(fabsf(y[4 * k + 2]), fabsf(y[4 * k + 3])));
   const uint32_t am = row8_max_u32(__float_as_uint(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))));
   const float sc = scale_from_amax(__uint_as_float(am), eps, ue8m0);
-  const Recip rc = recip_of_scale(sc);
+  const double d = recip_f64(sc);
   *sc_out = sc;
   u32x4 c;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    c[k] = encode4_q(div_by_scale_f32(y[4 * k], sc, rc), div_by_scale_f32(y[4 * k + 1], sc, rc),
-                   div_by_scale_f32(y[4 * k + 2], sc, rc), div_by_scale_f32(y[4 * k + 3], sc, rc));
+    c[k] = encode4_q(div_by_scale_f64(y[4 * k], d), div_by_scale_f64(y[4 * k + 1], d),
+                     div_by_scale_f64(y[4 * k + 2], d), div_by_scale_f64(y[4 * k + 3], d));
   return c;
 }
 
@@ -159,9 +159,9 @@ __device__ __forceinline__ void rms_load_row(u32x4 (&v)[VPL], const uint16_t* x,
   for (int i = 0; i < VPL; ++i) {
     const int e = rms_elem<VPL, WPR>(i, wv, lane);
     if (FULL) {
-      v[i] = load_nt16(xr + e);
+      v[i] = load16(xr + e);
     } else {
-      const u32x4 t = load_nt16(xr + (e < H ? e : H - 8));
+      const u32x4 t = load16(xr + (e < H ? e : H - 8));
       v[i] = e < H ? t : u32x4{0u, 0u, 0u, 0u};
     }
   }

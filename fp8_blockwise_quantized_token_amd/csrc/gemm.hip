@@ -38,8 +38,9 @@ namespace {
 // instruction is wasted on padding tokens.  A workgroup owns RN*16 weight
 // rows and all (<= 16*TOKT) tokens; its kwaves waves split the workgroup's K
 // range and their fp32 tiles are summed in LDS in a fixed wave order.  Weight
-// fragments are read straight from HBM (each weight byte is used by exactly
-// one workgroup), two K blocks at a time per wave to keep loads in flight;
+// fragments are read straight from HBM into registers (each weight byte is
+// used by exactly one workgroup; plain loads, which measure faster here than
+// non-temporal ones), two K blocks at a time per wave to keep loads in flight;
 // activations and their scales are small and come from L2.
 
 struct SwapParams {
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(512) void k_gemm_swapab(SwapParams p) {
       const int64_t ko = (int64_t)max(min(kb + u, kblast), 0) * 128;
 #pragma unroll
       for (int r = 0; r < RN; ++r)
-        b.wf[u][r] = make_v8i(load_nt16(wsrc[r] + ko), load_nt16(wsrc[r] + ko + 64));
+        b.wf[u][r] = make_v8i(load16(wsrc[r] + ko), load16(wsrc[r] + ko + 64));
     }
   };
   // fused: quantize one lane's 32 values of group (token, kb) -> operand, scale

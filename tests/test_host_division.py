@@ -2,12 +2,14 @@
 correction step instead of an IEEE divide (residual taken as q0 s - x so
 that signed zeros come out right without a sign copy), and computes the
 scale amax / 448 the same way.  For fp32 inputs (the fused producers) the
-first quotient comes from a two-term reciprocal (yd + yl), which makes it
-faithful, before the correction.  This CPU test checks, for every pair of
-(bf16 value significand, scale significand) the activation path can
-produce, for random fp32 values (the fused producers quantize fp32 values),
-and for every fp32 significand divided by 448, that the 3-operation
-sequence gives exactly the IEEE single-precision quotient.  Scales come from bf16 amax values (one per
+quotient is a float64 product x d rounded to fp32, with d a float64
+reciprocal of the scale from three Newton steps.  This CPU test checks, for
+every pair of (bf16 value significand, scale significand) the activation
+path can produce, for random and near-midpoint fp32 values (the fused
+producers quantize fp32 values), and for every fp32 significand divided by
+448, that these sequences give exactly the IEEE single-precision quotient;
+and, with exact rational arithmetic, that the Newton steps reach 2^-52 from
+any starting reciprocal within 2^-8.  Scales come from bf16 amax values (one per
 bf16 significand) and from eps; power-of-two (UE8M0) scales are exact
 trivially and are checked too.  Scaling x or s by powers of two scales every
 intermediate exactly, so significands at one exponent cover the normal range;
@@ -62,28 +64,6 @@ def _exact_fma_vec(a, b, c):
     for i in np.nonzero(near)[0]:
         t[i] = _libm.fmaf(float(a[i]), float(b[i]), float(c[i]))
     return t
-
-
-def _recip_pair(s):
-    """yn = RN(1/s); yd = yn, or its predecessor when s yn > 1; yl = RN(RN(1 - s yd) yd)."""
-    s = s.astype(np.float32)
-    yn = (np.float32(1) / s).astype(np.float32)
-    e = _exact_fma_vec(-s, yn, np.ones_like(s))
-    yd = np.where(e < 0, (yn.view(np.uint32) - np.uint32(1)).view(np.float32), yn).astype(np.float32)
-    yl = (_exact_fma_vec(-s, yd, np.ones_like(s)) * yd).astype(np.float32)
-    assert np.all(yl >= 0)
-    return yn, yd, yl
-
-
-def _kernel_div_f32_vec(x, s):
-    """The fp32-input division: q0 = RN(x yd + RN(x yl)) (faithful), then one
-    Markstein correction with yn = RN(1/s)."""
-    x = x.astype(np.float32)
-    s = np.broadcast_to(s, x.shape).astype(np.float32)
-    yn, yd, yl = _recip_pair(s)
-    q0 = _exact_fma_vec(x, yd, (x * yl).astype(np.float32))
-    r = _exact_fma_vec(q0, s, -x)
-    return _exact_fma_vec(-r, yn, q0)
 
 
 def _bf16_significands():
@@ -159,27 +139,121 @@ def test_one_step_division_is_not_enough_for_fp32_inputs():
     assert np.any(r64.astype(np.float32).astype(np.float64) != r64)
 
 
-def test_fp32_division_matches_ieee_for_random_fp32_inputs():
-    x, s, y = _random_fp32_groups(1 << 20, 97)
-    got = _kernel_div_f32_vec(x, s)
+def _fma64(a, b, c):
+    """float64 FMA, exactly: the rational a b + c rounded once (CPython's
+    integer true division is correctly rounded)."""
+    from fractions import Fraction
+    return float(Fraction(a) * Fraction(b) + Fraction(c))
+
+
+def _recip_f64(s: float, d0: float) -> float:
+    """The kernel's three Newton steps d <- d + d (1 - s d), each with two FMAs."""
+    d = d0
+    for _ in range(3):
+        d = _fma64(d, _fma64(-s, d, 1.0), d)
+    return d
+
+
+def test_newton_reciprocal_reaches_2_pow_minus_52_from_2_pow_minus_8():
+    from fractions import Fraction
+    g = np.random.Generator(np.random.PCG64(98))
+    sig = np.concatenate([
+        (np.uint32(0x3F800000) | g.integers(0, 1 << 23, 600, dtype=np.uint32)),
+        np.array([0x3F800000, 0x3F800001, 0x3FFFFFFF, 0x3FB504F3, 0x3FAAAAAB], np.uint32)]).view(np.float32)
+    worst = 0.0
+    for i, m in enumerate(sig):
+        for e in (-100, -20, 0, 30):
+            s = float(np.float32(m * np.float32(2.0) ** e))
+            for eps0 in (2.0 ** -8, -(2.0 ** -8), float(g.uniform(-2.0 ** -8, 2.0 ** -8)), 0.0):
+                d0 = float(Fraction(1) / Fraction(s) * (1 + Fraction(eps0)))
+                d = _recip_f64(s, d0)
+                err = abs(float(Fraction(d) * Fraction(s) - 1))
+                worst = max(worst, err)
+    assert worst <= 2.0 ** -52, worst
+
+
+def _div_f64_product(x, d):
+    """The kernel's fp32-input division: RN32(RN64(x d))."""
+    return (x.astype(np.float64) * d).astype(np.float32)
+
+
+def _reciprocals_at_the_error_bound(s):
+    """RN64(1/s) and its neighbours two float64 ulps away on either side
+    (relative error up to 2^-51, beyond the 2^-52 the Newton steps reach)."""
+    d = 1.0 / s.astype(np.float64)
+    up = np.nextafter(np.nextafter(d, np.inf), np.inf)
+    dn = np.nextafter(np.nextafter(d, 0), 0)
+    return (d, up, dn)
+
+
+def test_f64_product_division_matches_ieee_for_random_fp32_inputs():
+    x, s, _ = _random_fp32_groups(1 << 20, 97)
     ref = (x / s).astype(np.float32)
-    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
-    # the hardest significands: x just below a power of two over scales with
-    # significands near 2 (largest error of RN(1/s))
-    xs = (np.uint32(0x3FFFFFFF) - np.arange(4096, dtype=np.uint32)).view(np.float32)
-    for sb in (0x3FFFFFFF, 0x3FFFFF00, 0x3F800001, 0x3FB504F3):
-        s1 = np.uint32(sb).view(np.float32)
-        got = _kernel_div_f32_vec(xs, s1)
-        assert np.array_equal(got.view(np.uint32), (xs / s1).astype(np.float32).view(np.uint32))
+    for d in _reciprocals_at_the_error_bound(s):
+        got = _div_f64_product(x, d)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-def test_fp32_division_signed_zero_and_tiny():
-    # scales whose reciprocal pair has yl > 0, yl = 0 (power of two) and yd < yn
+def test_f64_product_division_near_rounding_midpoints():
+    # x = RN32(m s) for fp32 rounding midpoints m (odd 25-bit significands):
+    # the quotients x / s closest to a midpoint that fp32 operands can give
+    g = np.random.Generator(np.random.PCG64(99))
+    mids = ((g.integers(1 << 23, 1 << 24, 1 << 14, dtype=np.int64) * 2 + 1).astype(np.float64)) * 2.0 ** -24
+    sigs = np.concatenate([
+        (np.uint32(0x3F800000) | g.integers(0, 1 << 23, 62, dtype=np.uint32)),
+        np.array([0x3FFFFFFF, 0x3F800001], np.uint32)]).view(np.float32)
+    for sb in sigs:
+        for e in (-30, 0, 7):
+            s1 = np.float32(sb * np.float32(2.0) ** e)
+            x0 = (mids * np.float64(s1)).astype(np.float32)  # m s is exact in float64
+            xs = np.concatenate([x0, np.nextafter(x0, np.float32(np.inf)), np.nextafter(x0, np.float32(0)), -x0])
+            s = np.full(xs.shape, s1, np.float32)
+            ref = (xs / s).astype(np.float32)
+            for d in _reciprocals_at_the_error_bound(s):
+                got = _div_f64_product(xs, d)
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (float(s1),)
+
+
+def _closest_quotients(n_s=64, seed=5):
+    """Pairs (x, s) whose quotient lies as close to an fp32 rounding midpoint
+    as fp32 operands allow: for an odd scale significand S and a midpoint
+    significand M (odd, 25 bits) with M S = +-r (mod 2^25), r small and odd,
+    x = RN32(M S) differs from the midpoint times s by r units of 2^-47."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    xs, ss = [], []
+    for S in (g.integers(1 << 22, 1 << 23, n_s) * 2 + 1):
+        S = int(S)
+        inv = pow(S, -1, 1 << 25)
+        for r in range(1, 40, 2):
+            for sg in (1, -1):
+                M = (sg * r * inv) % (1 << 25)
+                if M < (1 << 24):
+                    continue
+                s = np.float32(S * 2.0 ** -23)
+                xs.append(np.float32(M * 2.0 ** -24 * float(s)))  # the 49-bit product rounded once
+                ss.append(s)
+    return np.array(xs, np.float32), np.array(ss, np.float32)
+
+
+def test_f64_product_division_at_the_closest_quotients():
+    x, s = _closest_quotients()
+    assert len(x) > 1000
+    ref = (x / s).astype(np.float32)
+    for d in _reciprocals_at_the_error_bound(s):
+        assert np.array_equal(_div_f64_product(x, d).view(np.uint32), ref.view(np.uint32))
+    # these cases are hard: a reciprocal 2^-47 off already changes results
+    d_bad = (1.0 / s.astype(np.float64)) * (1 + 2.0 ** -47)
+    assert np.any(_div_f64_product(x, d_bad) != ref)
+
+
+def test_f64_product_division_signed_zero_and_tiny():
     for s in (np.float32(1.0), np.float32(3.0) / np.float32(448), np.float32(1e30), np.float32(0.3),
               np.float32(0.7), np.float32(1.1)):
         xs = np.array([0.0, -0.0, -2.0 ** -133, 2.0 ** -133, -1e-38, 1e-30, -3e-36], np.float32)
-        got = _kernel_div_f32_vec(xs, s)
-        ref = (xs / s).astype(np.float32)
-        assert np.array_equal(np.signbit(got), np.signbit(xs))
-        big = np.abs(ref) >= 2.0 ** -60
-        assert np.array_equal(got[big], ref[big])
+        s_ = np.full(xs.shape, s, np.float32)
+        ref = (xs / s_).astype(np.float32)
+        for d in _reciprocals_at_the_error_bound(s_):
+            got = _div_f64_product(xs, d)
+            assert np.array_equal(np.signbit(got), np.signbit(xs))
+            big = np.abs(ref) >= 2.0 ** -60
+            assert np.array_equal(got[big], ref[big])
