@@ -178,6 +178,60 @@ def test_rms_norm_quant_strided_formats_and_padding():
             assert np.all((sh[:, M:] if mn else sh[:, G:]) == (0x5A if e8m0 else -1.0))
 
 
+def _closest_quotient_weights(H, seed):
+    """A weight row whose groups divide values that lie as close to an fp32
+    rounding midpoint as fp32 operands allow.  With x = +-1 and eps_norm = 0
+    the row's 1/rms is exactly 1 and y = +-w, so these are the quotients the
+    producer divides: per group, one value A sets the scale s = RN(A / 448)
+    (drawn until its significand S is odd), and the others are RN(M S 2^e)
+    for odd 25-bit midpoint significands M with M S = +-r (mod 2^25), r odd
+    and small, at quotient magnitudes 2^-6 .. 2^7."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = np.empty(H, np.float32)
+    scales = np.empty(H // 128, np.float32)
+    for grp in range(H // 128):
+        while True:
+            a = np.float32(g.uniform(0.5, 4.0) * 2.0 ** int(g.integers(-8, 8)))
+            sc = np.float32(a / np.float32(448))
+            S = int(sc.view(np.uint32) & 0x7FFFFF) | 0x800000
+            if S & 1:
+                break
+        inv = pow(S, -1, 1 << 25)
+        vals = [a]
+        r = 1
+        while len(vals) < 128:
+            for sg in (1, -1):
+                M = (sg * r * inv) % (1 << 25)
+                if M >= (1 << 24) and len(vals) < 128:
+                    e = int(g.integers(-6, 7))
+                    vals.append(np.float32(M * 2.0 ** (e - 24) * float(sc)))  # the 49-bit product rounded once
+            r += 2
+        v = np.array(vals, np.float32) * np.where(g.random(128) < 0.5, -1, 1).astype(np.float32)
+        g.shuffle(v)
+        w[grp * 128:(grp + 1) * 128] = v
+        scales[grp] = sc
+    return w, scales
+
+
+@pytest.mark.parametrize("M,H", [(8, 4096), (1100, 4096), (8, 1536), (1100, 1536)])
+def test_rms_norm_quant_division_at_the_closest_quotients(M, H):
+    """The producers divide fp32 values by the group scale through a float64
+    product; these quotients are the hardest for it (a reciprocal 2^-47 off
+    already changes some of them), and every code must still be the one the
+    oracle's IEEE division gives."""
+    w, sc = _closest_quotient_weights(H, 700 + H)
+    q_ref = (w / np.repeat(sc, 128)).astype(np.float32)
+    d_off = (1.0 / np.repeat(sc, 128).astype(np.float64)) * (1 + 2.0 ** -47)
+    assert np.any((w.astype(np.float64) * d_off).astype(np.float32) != q_ref), "cases are not hard"
+    g = np.random.Generator(np.random.PCG64(M + H))
+    x = np.where(g.random((M, H)) < 0.5, np.uint16(0xBF80), np.uint16(0x3F80)).astype(np.uint16)  # bf16 -1 / +1
+    rq, rs = oracle.rms_norm_per_block_quant(x, w, eps_norm=0.0, eps=EPS)
+    assert np.array_equal(rs, np.broadcast_to(sc, rs.shape)), "1/rms is not exactly 1"
+    say("closest quotients", M, H)
+    q, s = _gpu_rms(x, w, 0.0, False)
+    _assert_exact(q, s, rq, rs, ("closest quotients", M, H))
+
+
 # ------------------------------------------------------------ SiLU and mul
 
 SILU_CASES = [(1, 128), (3, 256), (5, 384), (64, 6144), (7, 12288), (2, 25600), (129, 1024)]
