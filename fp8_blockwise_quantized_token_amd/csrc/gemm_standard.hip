@@ -466,9 +466,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 
   // ---- epilogue of one tile row i (rows wave_m WM + 16 i + frow): lane
   // holds row frow and columns orow..orow+3 of each tile (the products are
-  // computed as W A^T, so a lane's four values are consecutive in n): one
-  // 8-byte bf16 store, or one 16-byte fp32 store of split-K partials, per
-  // tile ----
+  // computed as W A^T, so a lane's four values are consecutive in n); fp32
+  // split-K partials leave in one 16-byte store per tile ----
   v4f swc[S::TN];  // CH: per-channel weight scales of this lane's columns
   auto load_swc = [&]() __attribute__((always_inline)) {
     if constexpr (CH) {
@@ -481,24 +480,53 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // Rows past M hold exactly the values of row M-1 (their A rows and scales
   // re-read row M-1), so they are stored there again rather than skipped: the
   // same bytes, and no branch in the pipeline.
+  //
+  // bf16 output leaves in 16-byte stores of 8 consecutive columns: for each
+  // pair of tiles (j, j+1) the lanes l and l ^ 16 (same row, column groups
+  // 4g and 4g + 4 of both tiles) trade halves, so that the even-group lane
+  // holds 8 columns of tile j and the odd-group lane 8 columns of tile j+1,
+  // and one store instruction writes 64 contiguous bytes of each of its 16
+  // rows (half as many store instructions as 8-byte pieces; 4-5 % faster
+  // on the prefill layers).
   auto store_row = [&](auto partial_c, int i) __attribute__((always_inline)) {
     constexpr bool PARTIAL = decltype(partial_c)::value;  // fp32 split-K partials, else bf16
     const int64_t m = min(m0 + wave_m * WM + i * 16 + frow, mlast);
     const float sam = CH ? g.sa[m] : 1.0f;
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const int64_t n = n0 + wave_n * WN + j * 16 + orow;
+    auto scaled = [&](int j) __attribute__((always_inline)) {
       v4f v = acc[i][j];
       if constexpr (CH) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
       }
-      if constexpr (PARTIAL) {
-        *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
-      } else {
-        const uint32_t lo = bf16x2_bits(v[0], v[1]);
-        const uint32_t hi = bf16x2_bits(v[2], v[3]);
-        *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
+      return v;
+    };
+    if constexpr (!PARTIAL && S::TN % 2 == 0) {
+      const bool odd = (lane >> 4) & 1;
+      const int c8 = ((lane >> 5) & 1) * 8;  // this lane pair's 8 columns within a tile
+#pragma unroll
+      for (int j = 0; j < S::TN; j += 2) {
+        const v4f v0 = scaled(j), v1 = scaled(j + 1);
+        const uint32_t a0 = bf16x2_bits(v0[0], v0[1]), a1 = bf16x2_bits(v0[2], v0[3]);
+        const uint32_t b0 = bf16x2_bits(v1[0], v1[1]), b1 = bf16x2_bits(v1[2], v1[3]);
+        // the even lane sends its tile-(j+1) columns, the odd lane its tile-j ones
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16);
+        const u32x4 d = odd ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
+        const int64_t n = n0 + wave_n * WN + (j + (odd ? 1 : 0)) * 16 + c8;
+        *(u32x4*)(g.y + m * g.ldy + n) = d;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j) {
+        const int64_t n = n0 + wave_n * WN + j * 16 + orow;
+        const v4f v = scaled(j);
+        if constexpr (PARTIAL) {
+          *(v4f*)(g.ws + ((int64_t)split * g.M + m) * g.N + n) = v;
+        } else {
+          const uint32_t lo = bf16x2_bits(v[0], v[1]);
+          const uint32_t hi = bf16x2_bits(v[2], v[3]);
+          *(uint2*)(g.y + m * g.ldy + n) = make_uint2(lo, hi);
+        }
       }
     }
   };
