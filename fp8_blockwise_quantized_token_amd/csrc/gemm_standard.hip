@@ -531,12 +531,55 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
     }
   };
 
+  // The last block's bf16 rows through LDS (two stages, 64-column wave
+  // tiles): the other stage is free by then (its block passed its stage
+  // barrier and nothing refills it), so each wave writes its 16 x 64
+  // output values of tile row i into a private 16-row patch of it (rows
+  // padded to 144 bytes against bank conflicts) and reads them back as
+  // 16 bytes per lane, 8 lanes per row: each store instruction then writes
+  // 8 whole 128-byte rows.  LDS instructions of one wave complete in order;
+  // the wave barriers keep the compiler from moving the reads above the
+  // writes of other lanes, or the next row's writes above these reads.
+  constexpr int kOutPitch = 144;
+  constexpr int kOutBytes = S::WAVES * 16 * kOutPitch;
+  constexpr bool OUT_IN_B = kOutBytes <= BN * 128;  // the free stage's B buffer holds the patches
+  constexpr bool LDS_OUT = !SPLIT && NS == 2 && WN == 64 && (OUT_IN_B || kOutBytes <= BM * 128);
+  auto store_row_lds = [&](int i, uint8_t* scratch) __attribute__((always_inline)) {
+    uint8_t* patch = scratch + wave * (16 * kOutPitch);
+    const float sam = CH ? g.sa[min(m0 + wave_m * WM + i * 16 + frow, mlast)] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) {
+      v4f v = acc[i][j];
+      if constexpr (CH) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = v[q] * sam * swc[j][q];
+      }
+      *(uint2*)(patch + frow * kOutPitch + (j * 16 + orow) * 2) =
+          make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = (lane >> 3) + 8 * k;
+      const u32x4 d = *(const u32x4*)(patch + r * kOutPitch + (lane & 7) * 16);
+      const int64_t m = min(m0 + wave_m * WM + i * 16 + r, mlast);
+      *(u32x4*)(g.y + m * g.ldy + n0 + wave_n * WN + (lane & 7) * 8) = d;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
   // The last K block: the same row pipeline without a refill, a stage
   // barrier or the next block's reads, and each tile row leaves as soon as
   // its accumulators are final (during the next row's products), so the
   // workgroup's output stores overlap its last block instead of following
   // it in one burst.
-  auto kblock_last = [&](auto partial_c, const uint8_t* la, const float* ls) __attribute__((always_inline)) {
+  auto kblock_last = [&](auto partial_c, const uint8_t* la, const float* ls, uint8_t* scratch) __attribute__((always_inline)) {
+    auto out_row = [&](int i) __attribute__((always_inline)) {
+      if constexpr (LDS_OUT && !decltype(partial_c)::value)
+        store_row_lds(i, scratch);
+      else
+        store_row(partial_c, i);
+    };
     load_swc();
     if constexpr (P2 || CH) {
       const uint32_t eb = P2 ? __float_as_uint(swv) >> 23 : 0u;
@@ -561,10 +604,10 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
         if (i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (i > 0) store_row(partial_c, i - 1);  // its products finished during this row's
+        if (i > 0) out_row(i - 1);  // its products finished during this row's
         __builtin_amdgcn_sched_barrier(0);
       }
-      store_row(partial_c, S::TM - 1);
+      out_row(S::TM - 1);
       return;
     }
     float scn = 0.f;
@@ -596,7 +639,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       __builtin_amdgcn_sched_barrier(0);
       gq[cur] = scl * swv;
       scl = scn;
-      if (i > 0) store_row(partial_c, i - 1);  // folded during this row
+      if (i > 0) out_row(i - 1);  // folded during this row
       __builtin_amdgcn_sched_barrier(0);
     }
     constexpr int last = S::TM - 1, lc = (S::TM - 1) & 1;
@@ -605,7 +648,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         acc[last][j][q] = __builtin_fmaf(P[lc][j][q], gq[lc], acc[last][j][q]);
-    store_row(partial_c, last);
+    out_row(last);
   };
 
 
@@ -678,7 +721,8 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
             kblock(stage_a(st), stage_s(st), stage_a(ic<pv>{}), stage_b(ic<pv>{}), stage_s(ic<pv>{}), kblast,
                    stage_a(ic<nx>{}), stage_b(ic<nx>{}), stage_s(ic<nx>{}));
           else
-            kblock_last(std::false_type{}, stage_a(st), stage_s(st));
+            kblock_last(std::false_type{}, stage_a(st), stage_s(st),
+                        OUT_IN_B ? stage_b(ic<(i + 1) % NS>{}) : stage_a(ic<(i + 1) % NS>{}));
         });
       }
     });
