@@ -206,13 +206,15 @@ def extra_measurements(stream, dev):
         q = torch.empty((c.M, c.K), dtype=torch.uint8, device=dev)
         s = torch.empty((c.M, c.K // 128), dtype=torch.float32, device=dev)
         xc = rotation_copies([(x,)], 2 * c.M * c.K, dev)
-        t = graph_time(stream, [lambda r=r: fb.fp8_group_quant(xc[r % len(xc)][0], q, s, stream=stream)
+        oc = [(q, s)] + [(torch.empty_like(q), torch.empty_like(s)) for _ in range(len(xc) - 1)]
+        t = graph_time(stream, [lambda r=r: fb.fp8_group_quant(xc[r % len(xc)][0], oc[r % len(oc)][0],
+                                                                oc[r % len(oc)][1], stream=stream)
                                 for r in range(max(len(xc), 4))])
         gbps = quant_bytes(c) / t / 1e9
         out["quant_m16384"].append({"M": c.M, "K": c.K, "us": round(t * 1e6, 2), "gbps": round(gbps, 1),
                                     "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)})
         print(f"[bench] quant {c.M}x{c.K}: {t * 1e6:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
-        del x, q, s, xc
+        del x, q, s, xc, oc
     torch.cuda.empty_cache()
     return out
 
@@ -325,12 +327,16 @@ def bench_producers(args) -> int:
             for _ in range(args.warmup):
                 fn()
         stream.synchronize()
-        # rotate over copies of x so that every cycle reads >= 1 GiB
-        x0 = fn.__defaults__[0]
+        # rotate over copies of x so that every cycle reads >= 1 GiB, and
+        # over as many output buffers: a buffer rewritten by every launch
+        # stays in the Infinity Cache, and its writes never reach HBM
+        x0, q0, s0 = fn.__defaults__[:3]
         xs_rot = rotation_copies([(x0,)], x0.numel() * 2, dev)
-        t = graph_time(stream, [lambda r=r: fn(x=xs_rot[r % len(xs_rot)][0])
+        out_rot = [(q0, s0)] + [(torch.empty_like(q0), torch.empty_like(s0)) for _ in range(len(xs_rot) - 1)]
+        t = graph_time(stream, [lambda r=r: fn(x=xs_rot[r % len(xs_rot)][0], q=out_rot[r % len(out_rot)][0],
+                                               s=out_rot[r % len(out_rot)][1])
                                 for r in range(max(len(xs_rot), args.kernel_reps))])
-        del xs_rot
+        del xs_rot, out_rot
         b = producer_bytes(op, M)
         tot_b += b
         tot_t += t
@@ -344,7 +350,7 @@ def bench_producers(args) -> int:
            "dtype": "bf16-in/fp32-compute/e4m3-out", "data": "synthetic (seeded)",
            "config": {"workload": "producers_qwen3_8b", "H": PRODUCER_H, "I": PRODUCER_I,
                       "m_values": list(PRODUCER_M), "graph_replay": True,
-                      "timing": "graph replays rotating >= 1 GiB of input copies, median of 5"},
+                      "timing": "graph replays rotating >= 1 GiB of input copies and as many output buffers, median of 5"},
            "roofline": [{"bound": "hbm", "op": r["op"], "kernel": PRODUCER_SYMBOLS[r["op"]],
                          "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": r["hbm_frac"], "avg_launch_us": r["us"],
@@ -455,12 +461,13 @@ def main() -> int:
                          and (cfg.tile_m <= 32 or (cfg.tile_m == 64 and cfg.tile_n == 16))))
     torch.cuda.synchronize()
 
-    def quant(b, x=None):
+    def quant(b, x=None, out=None):
         x = b["x"] if x is None else x
+        qa, sa = (b["qa"], b["sa"]) if out is None else out
         if dynamic:
-            fb.fp8_token_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream)
+            fb.fp8_token_quant(x, qa, sa, ue8m0=b["case"].ue8m0, stream=stream)
         else:
-            fb.fp8_group_quant(x, b["qa"], b["sa"], ue8m0=b["case"].ue8m0, stream=stream, scale_mn_major=True)
+            fb.fp8_group_quant(x, qa, sa, ue8m0=b["case"].ue8m0, stream=stream, scale_mn_major=True)
 
     def gemm(b, w=None):
         qw, sw = (b["qw"], b["sw"]) if w is None else w
@@ -518,9 +525,11 @@ def main() -> int:
     # ---- per-case and per-kernel durations ----
     # Every case is timed from a captured graph of launches replayed TRIALS
     # times (median), HIP events on the launch stream.  The launches rotate
-    # over enough copies of the weight (and, for the quantizer, of X) that
-    # each cycle touches at least ROTATE_BYTES, so no launch finds its
-    # operand in the 256 MB Infinity Cache.  quant: fp8_group_quant alone;
+    # over enough copies of the weight (and, for the quantizer, of X and of
+    # its outputs) that each cycle touches at least ROTATE_BYTES, so no launch
+    # finds its operand in the 256 MB Infinity Cache, nor writes into a
+    # buffer the previous launch left there (a GEMM's output is not rotated:
+    # measured 0.5 % on the prefill layers).  quant: fp8_group_quant alone;
     # gemm: the GEMM kernel of the step's call (fused Swap-AB: fp8_linear
     # itself; otherwise fp8_block_gemm on the quantized input; a split-K call
     # includes its reduce kernel); linear: the step's fp8_linear call.
@@ -531,8 +540,10 @@ def main() -> int:
         c = b["case"]
         wcopies = rotation_copies(wq[(c.N, c.K, c.ue8m0)], c.N * c.K, dev, limit=GRAPH_LAUNCHES)
         xcopies = rotation_copies([(b["x"],)], 2 * c.M * c.K, dev, limit=8)
+        qcopies = [(torch.empty_like(b["qa"]), torch.empty_like(b["sa"])) for _ in xcopies]
         nq = max(len(xcopies), 8)
-        tq = graph_time(stream, [lambda r=r: quant(b, x=xcopies[r % len(xcopies)][0]) for r in range(nq)])
+        tq = graph_time(stream, [lambda r=r: quant(b, x=xcopies[r % len(xcopies)][0],
+                                                   out=qcopies[r % len(qcopies)]) for r in range(nq)])
         lin = [lambda r=r: linear(b, w=wcopies[r % len(wcopies)]) for r in range(GRAPH_LAUNCHES)]
         tl = graph_time(stream, lin)
         if b["fused"]:
@@ -541,7 +552,7 @@ def main() -> int:
             quant(b)
             tg = graph_time(stream, [lambda r=r: gemm(b, w=wcopies[r % len(wcopies)])
                                      for r in range(GRAPH_LAUNCHES)])
-        del wcopies, xcopies
+        del wcopies, xcopies, qcopies
         fl = c.flops()
         gb = gemm_bytes(c, dynamic) + (2 * c.M * c.K - c.M * c.K - 4 * c.M * c.K // 128 if b["fused"] else 0)
         lb = gemm_bytes(c, dynamic) + quant_bytes(c, dynamic) if not b["fused"] else gb
