@@ -314,10 +314,12 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // issued before the last row (EARLY: more tile rows than DMA rows), the
   // wave passes the stage barrier before that row, whose A fragment is
   // already in registers, and reads the next block's first A fragment and
-  // activation scale during the row's products; once they are issued, it
-  // reads the next block's B fragments and weight scale and folds the last
-  // row's products while those reads are in flight.  Otherwise the barrier
-  // and all of the next block's first reads follow the last row's products.
+  // activation scale during the row's products, and the next block's B
+  // fragment j right after its product j of the row (the fragment register
+  // is free once the product has been issued); the weight scale follows, and
+  // the last row's products are folded while those reads are in flight.
+  // Otherwise the barrier and all of the next block's first reads follow
+  // the last row's products.
   static_assert(S::TM % 2 == 0, "row pipeline assumes an even number of tile rows");
   const int arow = wave_m * WM + frow;
   const int a_lo = swz_off(arow, fch), a_hi = swz_off(arow, fch + 1);  // + 2048 per tile row
@@ -333,11 +335,14 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   // LDS reads complete in issue order, so the reads are issued in the order
   // of use (pinned by scheduling barriers): the first MFMA waits only for
   // the first A and B fragments, not for the whole burst.
+  auto read_bj = [&](int j, const uint8_t* lb) __attribute__((always_inline)) {
+    const int r = wave_n * WN + j * 16 + frow;
+    bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
+  };
   auto read_b = [&](const uint8_t* lb, const float* ls) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < S::TN; ++j) {
-      const int r = wave_n * WN + j * 16 + frow;
-      bf[j] = make_v8i(*(const u32x4*)(lb + swz_off(r, fch)), *(const u32x4*)(lb + swz_off(r, fch + 1)));
+      read_bj(j, lb);
       __builtin_amdgcn_sched_barrier(0);
     }
     swv = ls[sw_slot];
@@ -391,6 +396,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
           af[prv] = make_v8i(*(const u32x4*)(na + a_lo), *(const u32x4*)(na + a_hi));
           if constexpr (P2) ear = ns[srow];
         }
+        const bool refill_b = EARLY && i + 1 == S::TM;  // the last row reads the next block's B fragments
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
           if constexpr (P2)
@@ -399,13 +405,22 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
           else  // unscaled accumulate (zero scale operands select the plain instruction)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[cur], acc[i][j], 0, 0, 0,
                                                                          0, 0, 0);
+          if (refill_b) read_bj(j, nb);
         }
         if (EARLY || i + 1 < S::TM) __builtin_amdgcn_sched_group_barrier(0x100, P2 ? 3 : 2, 0);  // next row's reads first
-        __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
+        if (refill_b) {
+#pragma unroll
+          for (int j = 0; j < S::TN; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product j, then the reads that refill bf[j]
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, S::TN, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (EARLY) {
-        read_b(nb, ns);  // after the last row's products have read bf
+        swv = ns[sw_slot];
       } else {
         stage_barrier();
         read_first(na, nb, ns);
@@ -427,9 +442,16 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
         af[prv] = make_v8i(*(const u32x4*)(na + a_lo), *(const u32x4*)(na + a_hi));
         scn = ns[srow];
       }
+      // The last row of an EARLY block reads each B fragment of the next
+      // block as soon as its own product with that fragment has been
+      // issued, so that the next block's first products find their operands
+      // in registers instead of waiting for eight fragment reads issued
+      // after the last product (2-2.4 % on the prefill layers).
+      const bool refill_b = EARLY && i + 1 == S::TM;
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
         P[cur][j] = mfma16x16x128(bf[j], af[cur]);
+        if (refill_b) read_bj(j, nb);
         if (i > 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -441,6 +463,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
 #pragma unroll
         for (int j = 0; j < S::TN; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          if (refill_b) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads that refill bf[j]
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
         }
       }
@@ -449,7 +472,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
       scl = scn;
     }
     if constexpr (EARLY) {
-      read_b(nb, ns);  // after the last row's products have read bf
+      swv = ns[sw_slot];  // after the last row's factor has used this block's
     } else {
       stage_barrier();
       read_first(na, nb, ns);
