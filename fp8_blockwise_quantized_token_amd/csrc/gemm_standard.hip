@@ -97,6 +97,7 @@ struct Shape {
   static constexpr int SA_INSTR = BM / 64;        // 256-byte activation-scale loads, one per wave
   static constexpr int SW_WAVE = SA_INSTR;        // the wave that loads the weight scales
   static constexpr int S_FLOATS = BM + 64;        // per-stage scale buffer: sa[BM], sw[BN/128] (+pad)
+  static constexpr int SW_N = BN >= 128 ? BN / 128 : 1;  // weight-scale blocks a tile spans
   static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "row groups must divide over waves");
   static_assert(128 % WN == 0, "a wave's N range must sit inside one 128-row weight block");
   static_assert(SW_WAVE < WAVES, "one scale load per wave at most");
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(BM / WM * (BN / WN) * 64) void k_gemm_lds(StdParams
   const float* sa_base = g.sa + m0 * g.sa_row;
   const uint32_t sa_off = (uint32_t)min((wave * 64 + lane) % BM, rows_valid - 1) * (uint32_t)g.sa_row;
   const float* sw_base = g.sw + (n0 >> 7) * g.ldsw;
-  const uint32_t sw_off = (uint32_t)min(lane, BN / 128 - 1) * (uint32_t)g.ldsw;
+  const uint32_t sw_off = (uint32_t)min(lane, S::SW_N - 1) * (uint32_t)g.ldsw;
   const int sw_slot = BM + ((wave_n * WN) >> 7);  // this wave's weight scale in the stage buffer
   const bool sa_wave = wave < S::SA_INSTR;
   const float* sc_base = sa_wave ? sa_base : sw_base;
@@ -852,12 +853,16 @@ hipError_t run(const GemmArgs& g, int split_k, bool split_tail, int sm, hipStrea
 }  // namespace
 
 // (tile_m, tile_n, LDS stages, kwaves) combinations that are compiled;
-// stages 0 means the default, 2.  kwaves 2 doubles the waves of the 64x128
-// and 128x128 tiles (each wave 32 columns wide instead of 64): two waves per
-// SIMD hide each other's latencies when the grid holds only one workgroup
-// per CU (M of a few hundred to a few thousand).
+// stages 0 means the default, 2.  kwaves 2 doubles the waves of the 64x64,
+// 64x128 and 128x128 tiles (each wave 32 columns wide instead of 64): two
+// waves per SIMD hide each other's latencies when the grid holds only one
+// workgroup per CU (M of a few hundred to a few thousand).  The 64x64 tile
+// (a 64-wide weight range inside one 128-row scale block) gives decode-sized
+// layers with many weight rows enough workgroups without splitting K, so
+// that no partial sums and no second kernel are needed.
 bool standard_tile_supported(int tile_m, int tile_n, int stages, int kwaves) {
   const int ns = stages == 0 ? 2 : stages;
+  if (tile_m == 64 && tile_n == 64) return (kwaves == 1 || kwaves == 2) && ns >= 2 && ns <= 4;
   if (kwaves == 2) {
     if (tile_m == 64 && tile_n == 128) return ns >= 2 && ns <= 4;
     if (tile_m == 128 && tile_n == 128) return ns == 2 || ns == 3;
@@ -877,7 +882,16 @@ hipError_t launch_gemm_standard(const GemmArgs& g, int tile_m, int tile_n, int s
   const int sm = scale_mode;  // 0 block fp32, 1 block power-of-two, 2 per-token / per-channel
   const int ns = stages == 0 ? 2 : stages;
   hipError_t e = hipErrorInvalidValue;
-  if (kwaves == 2) {
+  if (tile_m == 64 && tile_n == 64) {
+    if (kwaves == 2)
+      e = ns == 4 ? run<64, 64, 32, 32, 4>(g, split_k, split_tail, sm, stream)
+        : ns == 3 ? run<64, 64, 32, 32, 3>(g, split_k, split_tail, sm, stream)
+                  : run<64, 64, 32, 32, 2>(g, split_k, split_tail, sm, stream);
+    else if (kwaves == 1)
+      e = ns == 4 ? run<64, 64, 32, 64, 4>(g, split_k, split_tail, sm, stream)
+        : ns == 3 ? run<64, 64, 32, 64, 3>(g, split_k, split_tail, sm, stream)
+                  : run<64, 64, 32, 64, 2>(g, split_k, split_tail, sm, stream);
+  } else if (kwaves == 2) {
     if (tile_m == 64 && tile_n == 128)
       e = ns == 4 ? run<64, 128, 32, 32, 4>(g, split_k, split_tail, sm, stream)
         : ns == 3 ? run<64, 128, 32, 32, 3>(g, split_k, split_tail, sm, stream)

@@ -65,8 +65,9 @@ def candidates(M: int, N: int, K: int):
                 for sk in (1, 2, 4, 8, 16):
                     if sk * kw <= kb:
                         out.append(fb.make_config(fb.SWAPAB, tm, tn, sk, kw))
-    stages = {(64, 128): (2, 3, 4), (128, 128): (2, 3), (256, 128): (2, 3), (128, 256): (2,), (256, 256): (2,)}
-    for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
+    stages = {(64, 64): (2, 3, 4), (64, 128): (2, 3, 4), (128, 128): (2, 3), (256, 128): (2, 3), (128, 256): (2,),
+              (256, 256): (2,)}
+    for tm, tn in ((64, 64), (64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
         if N % tn or (tm >= 128 and M <= 32):
             continue
         tiles = -(-M // tm) * (N // tn)
@@ -78,7 +79,7 @@ def candidates(M: int, N: int, K: int):
                     continue  # deep pipelines are for few, short K loops
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, 0 if ns == 2 else ns))
                 # twice the waves for grids of about one workgroup per CU
-                if (tm, tn) in ((64, 128), (128, 128)) and tiles * sk <= 1024:
+                if (tm, tn) in ((64, 64), (64, 128), (128, 128)) and tiles * sk <= 1024:
                     out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 2, 0 if ns == 2 else ns))
         # split tail: whole rounds unsplit, the partial last round split
         # (rounds of 256 workgroups for the one-per-CU tiles, else 512)

@@ -115,14 +115,15 @@ extern "C" {
  * are divided among split_k groups of workgroups, each writing an fp32
  * partial product to the workspace, then a second kernel sums the partials
  * in a fixed order and writes bf16 (deterministic, no atomics).
- *   STANDARD: tile_m in {64, 128, 256}, tile_n in {128, 256}; stages = LDS
- *             pipeline depth (K blocks staged ahead): 0 (default, = 2) or
- *             2..4 where compiled (64x128: 2-4; 128x128, 256x128: 2-3;
- *             others: 2).  Deeper pipelines hide memory latency in
- *             decode-sized problems.  kwaves 1 (or 0): the tile's default
- *             waves; 2: twice the waves, each half as wide (64x128 with
- *             stages 2-4, 128x128 with stages 2-3), for grids of about one
- *             workgroup per CU.
+ *   STANDARD: tile_m x tile_n in {64x64, 64x128, 128x128, 256x128,
+ *             128x256, 256x256}; stages = LDS pipeline depth (K blocks
+ *             staged ahead): 0 (default, = 2) or 2..4 where compiled (64x64,
+ *             64x128: 2-4; 128x128, 256x128: 2-3; others: 2).  Deeper
+ *             pipelines hide memory latency in decode-sized problems.
+ *             kwaves 1 (or 0): the tile's default waves; 2: twice the
+ *             waves, each half as wide (64x64 and 64x128 with stages 2-4,
+ *             128x128 with stages 2-3), for grids of about one workgroup
+ *             per CU.
  *   SWAPAB:   tile_m (tokens per workgroup) in {16, 32, 64} and >= M,
  *             tile_n (weight rows per workgroup) in {16, 32, 64},
  *             kwaves (waves sharing one tile, each on its own K range,

@@ -72,8 +72,8 @@ def test_channel_quant_bit_exact(N, K):
 def _configs(M, N, K):
     kb = K // 128
     out = []
-    for tm, tn, ns in ((64, 128, 0), (64, 128, 4), (128, 128, 0), (128, 128, 3), (256, 128, 0),
-                       (128, 256, 0), (256, 256, 0)):
+    for tm, tn, ns in ((64, 64, 0), (64, 64, 3), (64, 128, 0), (64, 128, 4), (128, 128, 0), (128, 128, 3),
+                       (256, 128, 0), (128, 256, 0), (256, 256, 0)):
         if N % tn:
             continue
         for sk in (1, 3):

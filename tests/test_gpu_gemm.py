@@ -23,21 +23,22 @@ def _configs(M, N, K):
     """Every compiled configuration valid for this shape."""
     kb = K // 128
     out = []
-    for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
+    for tm, tn in ((64, 64), (64, 128), (128, 128), (256, 128), (128, 256), (256, 256)):
         if N % tn:
             continue
         for sk in (1, 2, 3):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk))
     # deeper LDS pipelines (3 and 4 stages), with and without split-K
-    for tm, tn, ns in ((64, 128, 3), (64, 128, 4), (128, 128, 3), (256, 128, 3)):
+    for tm, tn, ns in ((64, 64, 3), (64, 64, 4), (64, 128, 3), (64, 128, 4), (128, 128, 3), (256, 128, 3)):
         if N % tn:
             continue
         for sk in (1, 3):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 1, ns))
     # twice the waves (each 32 columns wide)
-    for tm, tn, ns in ((64, 128, 0), (64, 128, 3), (64, 128, 4), (128, 128, 0), (128, 128, 3)):
+    for tm, tn, ns in ((64, 64, 0), (64, 64, 3), (64, 128, 0), (64, 128, 3), (64, 128, 4), (128, 128, 0),
+                       (128, 128, 3)):
         for sk in (1, 2):
             if sk <= kb:
                 out.append(fb.make_config(fb.STANDARD, tm, tn, sk, 2, ns))
@@ -245,8 +246,8 @@ def test_hip_graph_replay_of_split_tail():
 def _pow2_configs(N, K):
     kb = K // 128
     out = []
-    for tm, tn, ns in ((64, 128, 0), (64, 128, 4), (128, 128, 0), (128, 128, 3), (256, 128, 0),
-                       (256, 128, 3), (128, 256, 0), (256, 256, 0)):
+    for tm, tn, ns in ((64, 64, 0), (64, 64, 4), (64, 128, 0), (64, 128, 4), (128, 128, 0), (128, 128, 3),
+                       (256, 128, 0), (256, 128, 3), (128, 256, 0), (256, 256, 0)):
         if N % tn:
             continue
         for sk in (1, 2):
@@ -353,8 +354,9 @@ def test_k_loop_depths_splits_and_stages(kb):
     sa2 = np.exp2(np.round(np.log2(sa))).astype(np.float32)
     sw2 = np.exp2(np.round(np.log2(sw))).astype(np.float32)
     ref2 = oracle.block_gemm(qa, sa2, qw, sw2)
-    for (tm, tn, kw, stages) in ((64, 128, 1, 0), (64, 128, 1, 3), (64, 128, 1, 4), (64, 128, 2, 4),
-                                 (128, 128, 1, 3), (128, 128, 2, 3), (256, 256, 1, 0), (256, 128, 1, 3)):
+    for (tm, tn, kw, stages) in ((64, 64, 1, 0), (64, 64, 2, 3), (64, 128, 1, 0), (64, 128, 1, 3),
+                                 (64, 128, 1, 4), (64, 128, 2, 4), (128, 128, 1, 3), (128, 128, 2, 3),
+                                 (256, 256, 1, 0), (256, 128, 1, 3)):
         for sk in (1, 2, 3, 4, 6):
             if sk > kb:
                 continue
@@ -392,9 +394,10 @@ def test_bf16_output_rounding_ties_and_subnormals():
     expect = np.full((M, N), 0x3F80, np.uint16)     # rows past the targets: sa = 1
     for i, (_, bits) in enumerate(targets):
         expect[i, :] = bits
-    cfgs = [fb.make_config(fb.STANDARD, tm, tn) for tm, tn in ((64, 128), (128, 128), (256, 128), (128, 256),
-                                                                (256, 256))]
-    cfgs += [fb.make_config(fb.STANDARD, 64, 128, 1, 2), fb.make_config(fb.STANDARD, 128, 128, 1, 2, 3)]
+    cfgs = [fb.make_config(fb.STANDARD, tm, tn) for tm, tn in ((64, 64), (64, 128), (128, 128), (256, 128),
+                                                                (128, 256), (256, 256))]
+    cfgs += [fb.make_config(fb.STANDARD, 64, 128, 1, 2), fb.make_config(fb.STANDARD, 128, 128, 1, 2, 3),
+             fb.make_config(fb.STANDARD, 64, 64, 1, 2)]
     cfgs += [fb.make_config(fb.SWAPAB, tm, tn, 1, kw) for tm in (16, 32, 64) for tn in (16, 32, 64)
              for kw in (1, 2) if not (tm == 64 and tn == 64)]
     for cfg in cfgs:
@@ -421,7 +424,7 @@ def _walk(tiles_m, tiles_n):
 _TAIL_CASES = [(256, 256, 1, 0, "block"), (128, 256, 1, 0, "block"), (256, 128, 1, 3, "block"),
                (128, 128, 1, 0, "block"), (128, 128, 2, 3, "block"), (64, 128, 1, 4, "block"),
                (256, 256, 1, 0, "pow2"), (128, 128, 2, 0, "pow2"), (256, 256, 1, 0, "dynamic"),
-               (64, 128, 2, 3, "dynamic")]
+               (64, 128, 2, 3, "dynamic"), (64, 64, 1, 3, "block"), (64, 64, 2, 0, "dynamic")]
 
 
 @pytest.mark.parametrize("tm,tn,kw,ns,mode", _TAIL_CASES, ids=lambda v: str(v))

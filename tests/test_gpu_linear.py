@@ -61,7 +61,8 @@ def test_every_config_equals_separate_quant_and_gemm(M, N, K):
     ref = oracle.block_gemm(qa_ref, sa_ref, qw, sw)
     xd, qwd, swd = to_dev_bf16(x), to_dev(qw), to_dev(sw)
     cfgs = _swap_configs(M, K) + [fb.make_config(fb.STANDARD, 64, 128, 1),
-                                  fb.make_config(fb.STANDARD, 128, 128, 2), None]
+                                  fb.make_config(fb.STANDARD, 128, 128, 2),
+                                  fb.make_config(fb.STANDARD, 64, 64, 1, 2, 3), None]
     for cfg in cfgs:
         y1, y2 = _two_paths(xd, qwd, swd, cfg)
         assert np.array_equal(y1, y2), f"{cfg}: fused differs from quant + GEMM"
