@@ -302,7 +302,7 @@ int fp8_linear(const uint16_t *x, int64_t ldx, const uint8_t *w, const float *sw
  *     M, N, K and configuration) exceeds that size returns
  *     FP8BLK_ERR_WORKSPACE with nothing launched.  Every dispatched
  *     configuration of the tabled Qwen3 shapes up to M = 256 fits (decode
- *     M <= 64 needs at most 12.3 MiB); large prefill calls generally do not.
+ *     M <= 64 needs at most 15.3 MiB); large prefill calls generally do not.
  *   - The array is shared by every call on one GPU and keeps the last
  *     call's contents (nothing in it needs to start at zero): calls that may
  *     overlap on one GPU (several streams or host threads) race on it and
